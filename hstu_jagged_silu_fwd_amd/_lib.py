@@ -1,0 +1,207 @@
+"""ctypes binding of libhstu (argument marshalling only).
+
+Every step of the layer runs in the HIP kernels of libhstu.so; this module
+only turns torch tensors into device pointers and the current HIP stream.
+There is no fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhstu.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG), "include", "hstu.h")
+
+HSTU_F32 = 0
+HSTU_BF16 = 1
+NUM_STAGES = 5
+STAGES = ("prep", "proj", "attn", "norm", "out")
+
+_lib = None
+
+
+class HSTUError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = int(code)
+        super().__init__(f"{what}: {status_string(code)} ({code})" if what else f"{status_string(code)} ({code})")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_users", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_user", ctypes.c_int32),
+        ("num_pool_pages", ctypes.c_int64),
+        ("total_new", ctypes.c_int32),
+        ("pos_buckets", ctypes.c_int32),
+        ("pos_mbits", ctypes.c_int32),
+        ("ts_buckets", ctypes.c_int32),
+        ("ts_mbits", ctypes.c_int32),
+        ("attn_scale", ctypes.c_float),
+        ("norm_eps", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhstu.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m hstu_jagged_silu_fwd_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dp = ctypes.POINTER(LayerDesc)
+    lib.hstu_layer_workspace_size.argtypes = [dp, ctypes.POINTER(SZ)]
+    lib.hstu_layer_workspace_size.restype = I32
+    layer_args = [dp, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hstu_layer_fwd.argtypes = layer_args
+    lib.hstu_layer_fwd.restype = I32
+    lib.hstu_layer_fwd_timed.argtypes = layer_args + [P]
+    lib.hstu_layer_fwd_timed.restype = I32
+    lib.kv_pages_append.argtypes = [dp, P, P, P, P, P, P, P, P, P]
+    lib.kv_pages_append.restype = I32
+    lib.hstu_read_device_status.argtypes = [P, ctypes.POINTER(I32), P]
+    lib.hstu_read_device_status.restype = I32
+    lib.hstu_status_string.argtypes = [I32]
+    lib.hstu_status_string.restype = ctypes.c_char_p
+    _ = I64
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> Sequence[str]:
+    """Names of the functions the C header declares."""
+    src = open(path).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:hstu_status|const char\*)\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
+
+
+def status_string(code: int) -> str:
+    try:
+        return load().hstu_status_string(int(code)).decode()
+    except ImportError:
+        return "status"
+
+
+def make_desc(*, num_users: int, num_heads: int, head_dim: int, page_size: int,
+              max_pages_per_user: int, num_pool_pages: int, total_new: int,
+              pos_buckets: int, pos_mbits: int, attn_scale: float, norm_eps: float,
+              dtype: str, ts_buckets: int = 0, ts_mbits: int = 0) -> LayerDesc:
+    return LayerDesc(num_users=num_users, num_heads=num_heads, head_dim=head_dim,
+                     hidden=num_heads * head_dim, page_size=page_size,
+                     max_pages_per_user=max_pages_per_user, num_pool_pages=num_pool_pages,
+                     total_new=total_new, pos_buckets=pos_buckets, pos_mbits=pos_mbits,
+                     ts_buckets=ts_buckets, ts_mbits=ts_mbits, attn_scale=attn_scale,
+                     norm_eps=norm_eps, dtype=HSTU_BF16 if dtype == "bf16" else HSTU_F32)
+
+
+def _ptr(t, what: str, dtype=None, allow_none: bool = False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{what} is required")
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _tdtype(desc: LayerDesc):
+    import torch
+    return torch.bfloat16 if desc.dtype == HSTU_BF16 else torch.float32
+
+
+def workspace_size(desc: LayerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().hstu_layer_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if rc != 0:
+        raise HSTUError(rc, "hstu_layer_workspace_size")
+    return int(n.value)
+
+
+def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_pool,
+              w1, w2, pos_bias, y, workspace, ts_bias=None, timestamps=None,
+              ts_offsets=None, stream=None, stage_events=None) -> None:
+    """Enqueue one layer (see include/hstu.h).  `workspace` is a uint8 device
+    tensor of at least workspace_size(desc) bytes; `stage_events` optionally
+    a sequence of 2*NUM_STAGES raw hipEvent_t handles."""
+    import torch
+    lib = load()
+    dt = _tdtype(desc)
+    args = [
+        ctypes.byref(desc),
+        _ptr(x, "x", dt, allow_none=desc.total_new == 0),
+        _ptr(new_offsets, "new_offsets", torch.int32),
+        _ptr(hist_len, "hist_len", torch.int32),
+        _ptr(page_table, "page_table", torch.int32),
+        _ptr(k_pool, "k_pool", dt),
+        _ptr(v_pool, "v_pool", dt),
+        _ptr(w1, "w1", dt),
+        _ptr(w2, "w2", dt),
+        _ptr(pos_bias, "pos_bias", torch.float32),
+        _ptr(ts_bias, "ts_bias", torch.float32, allow_none=True),
+        _ptr(timestamps, "timestamps", torch.int64, allow_none=True),
+        _ptr(ts_offsets, "ts_offsets", torch.int32, allow_none=True),
+        _ptr(y, "y", dt, allow_none=desc.total_new == 0),
+        _ptr(workspace, "workspace"),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+        _stream(stream),
+    ]
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * (2 * NUM_STAGES))(*[ctypes.c_void_p(e) for e in stage_events])
+        rc = lib.hstu_layer_fwd_timed(*args, arr)
+    else:
+        rc = lib.hstu_layer_fwd(*args)
+    if rc != 0:
+        raise HSTUError(rc, "hstu_layer_fwd")
+
+
+def kv_pages_append(desc: LayerDesc, k_new, v_new, new_offsets, hist_len, page_table,
+                    k_pool, v_pool, device_status, stream=None) -> None:
+    import torch
+    dt = _tdtype(desc)
+    rc = load().kv_pages_append(
+        ctypes.byref(desc),
+        _ptr(k_new, "k_new", dt, allow_none=desc.total_new == 0),
+        _ptr(v_new, "v_new", dt, allow_none=desc.total_new == 0),
+        _ptr(new_offsets, "new_offsets", torch.int32),
+        _ptr(hist_len, "hist_len", torch.int32),
+        _ptr(page_table, "page_table", torch.int32),
+        _ptr(k_pool, "k_pool", dt),
+        _ptr(v_pool, "v_pool", dt),
+        _ptr(device_status, "device_status", torch.int32),
+        _stream(stream))
+    if rc != 0:
+        raise HSTUError(rc, "kv_pages_append")
+
+
+def read_device_status(status, stream=None) -> int:
+    """Synchronise `stream` and return the device status word at `status`
+    (a workspace tensor, an int32 status tensor or a raw pointer)."""
+    code = ctypes.c_int32(0)
+    rc = load().hstu_read_device_status(_ptr(status, "status"), ctypes.byref(code), _stream(stream))
+    if rc not in (0, -5):
+        raise HSTUError(rc, "hstu_read_device_status")
+    return int(code.value)

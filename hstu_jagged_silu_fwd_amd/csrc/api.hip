@@ -1,0 +1,218 @@
+// C ABI of libhstu: descriptor validation, workspace layout and the launch
+// sequence of one layer (prep -> X W1 + SiLU/split/append -> paged SiLU
+// attention -> norm * U -> G W2).
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+
+using namespace hstu;
+
+namespace {
+
+constexpr int kTargetItems = 512;   // attention split target (see prep.hip)
+constexpr int kAttnWgPerCu = 4;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Layout {
+  size_t row_user, qb_base, qb_first, qb_nch, items, q, u, part, total;
+  int nqb_cap, item_cap;
+};
+
+Layout make_layout(const hstu_layer_desc& d) {
+  Layout L{};
+  const size_t T = static_cast<size_t>(d.total_new);
+  const size_t B = static_cast<size_t>(d.num_users);
+  const size_t es = d.dtype == HSTU_BF16 ? 2 : 4;
+  L.nqb_cap = static_cast<int>((T + kQB - 1) / kQB + B);
+  L.item_cap = d.num_heads * L.nqb_cap + kTargetItems;
+  size_t off = 256;  // WsHeader
+  L.row_user = off; off = align256(off + 4 * T);
+  L.qb_base = off;  off = align256(off + 4 * (B + 1));
+  L.qb_first = off; off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
+  L.qb_nch = off;   off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
+  L.items = off;    off = align256(off + 16 * static_cast<size_t>(L.item_cap));
+  L.q = off;        off = align256(off + es * T * d.hidden);
+  L.u = off;        off = align256(off + es * T * d.hidden);
+  L.part = off;     off = align256(off + 4 * static_cast<size_t>(L.item_cap) * kQB * d.head_dim);
+  L.total = off;
+  return L;
+}
+
+WsPtrs ws_ptrs(void* base, const Layout& L) {
+  char* b = static_cast<char*>(base);
+  WsPtrs w;
+  w.hdr = reinterpret_cast<WsHeader*>(b);
+  w.row_user = reinterpret_cast<int32_t*>(b + L.row_user);
+  w.qb_base = reinterpret_cast<int32_t*>(b + L.qb_base);
+  w.qb_first = reinterpret_cast<int32_t*>(b + L.qb_first);
+  w.qb_nch = reinterpret_cast<int32_t*>(b + L.qb_nch);
+  w.items = reinterpret_cast<int4*>(b + L.items);
+  w.q = b + L.q;
+  w.u = b + L.u;
+  w.part = reinterpret_cast<float*>(b + L.part);
+  return w;
+}
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+// Shape checks shared by every entry point.
+hstu_status check_common(const hstu_layer_desc* d) {
+  if (d == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (d->num_users < 0 || d->num_heads < 1 || d->total_new < 0 || d->max_pages_per_user < 1 ||
+      d->num_pool_pages < 1)
+    return HSTU_ERR_INVALID_ARG;
+  if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return HSTU_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(d->num_heads) * d->head_dim != d->hidden) return HSTU_ERR_INVALID_ARG;
+  if (d->hidden % 64 != 0 || d->hidden > 2048) return HSTU_ERR_UNSUPPORTED;
+  if (!pow2_in(d->page_size, 16, 128)) return HSTU_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(d->max_pages_per_user) * d->page_size >= (int64_t{1} << 30))
+    return HSTU_ERR_UNSUPPORTED;
+  if (d->num_pool_pages > (int64_t{1} << 31) - 1) return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
+
+hstu_status check_layer(const hstu_layer_desc* d) {
+  hstu_status s = check_common(d);
+  if (s != HSTU_OK) return s;
+  if (d->pos_buckets < 1 || d->pos_buckets > kMaxBuckets || d->pos_mbits < 0 || d->pos_mbits > 16)
+    return HSTU_ERR_INVALID_ARG;
+  if (d->ts_buckets < 0 || d->ts_buckets > kMaxBuckets) return HSTU_ERR_INVALID_ARG;
+  if (d->ts_buckets > 0 && (d->ts_mbits < 0 || d->ts_mbits > 30)) return HSTU_ERR_INVALID_ARG;
+  if (!std::isfinite(d->attn_scale) || !(d->norm_eps > 0.0f) || !std::isfinite(d->norm_eps))
+    return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
+hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
+                       const int32_t* hist_len, const int32_t* page_table, void* k_pool, void* v_pool,
+                       const void* w1, const void* w2, const float* pos_bias, const float* ts_bias,
+                       const int64_t* timestamps, const int32_t* ts_offsets, void* y, void* workspace,
+                       size_t workspace_bytes, void* hip_stream, void* const* ev) {
+  hstu_status s = check_layer(desc);
+  if (s != HSTU_OK) return s;
+  const hstu_layer_desc& d = *desc;
+  const bool any_rows = d.total_new > 0;
+  if (new_offsets == nullptr || hist_len == nullptr || page_table == nullptr || k_pool == nullptr ||
+      v_pool == nullptr || w1 == nullptr || w2 == nullptr || pos_bias == nullptr || workspace == nullptr)
+    return HSTU_ERR_INVALID_ARG;
+  if (any_rows && (x == nullptr || y == nullptr)) return HSTU_ERR_INVALID_ARG;
+  if (any_rows && x == y) return HSTU_ERR_INVALID_ARG;
+  if (d.ts_buckets > 0 && (ts_bias == nullptr || timestamps == nullptr || ts_offsets == nullptr))
+    return HSTU_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return HSTU_ERR_INVALID_ARG;
+  const Layout L = make_layout(d);
+  if (workspace_bytes < L.total) return HSTU_ERR_WORKSPACE;
+  const WsPtrs ws = ws_ptrs(workspace, L);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int32_t* ts_off = d.ts_buckets > 0 ? ts_offsets : nullptr;
+  const int64_t* ts = d.ts_buckets > 0 ? timestamps : nullptr;
+  const float* tsb = d.ts_buckets > 0 ? ts_bias : nullptr;
+
+  auto rec = [&](int idx) -> bool {
+    return ev == nullptr || ev[idx] == nullptr ||
+           hipEventRecord(static_cast<hipEvent_t>(ev[idx]), st) == hipSuccess;
+  };
+  hipError_t e;
+  if (!rec(2 * HSTU_STAGE_PREP)) return HSTU_ERR_HIP;
+  e = launch_prep(d, new_offsets, hist_len, page_table, ts_off, ws, L.nqb_cap, L.item_cap, kTargetItems, st);
+  if (e != hipSuccess || !rec(2 * HSTU_STAGE_PREP + 1)) return HSTU_ERR_HIP;
+  if (!any_rows) return HSTU_OK;
+
+  if (!rec(2 * HSTU_STAGE_PROJ)) return HSTU_ERR_HIP;
+  e = launch_gemm_qkv(d, x, w1, new_offsets, hist_len, page_table, k_pool, v_pool, ws, st);
+  if (e != hipSuccess || !rec(2 * HSTU_STAGE_PROJ + 1)) return HSTU_ERR_HIP;
+
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return HSTU_ERR_HIP;
+  int grid = cus * kAttnWgPerCu;
+  if (grid > L.item_cap) grid = L.item_cap;
+  if (!rec(2 * HSTU_STAGE_ATTN)) return HSTU_ERR_HIP;
+  e = launch_attn(d, new_offsets, hist_len, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ws, grid, st);
+  if (e != hipSuccess || !rec(2 * HSTU_STAGE_ATTN + 1)) return HSTU_ERR_HIP;
+
+  if (!rec(2 * HSTU_STAGE_NORM)) return HSTU_ERR_HIP;
+  e = launch_norm_gate(d, new_offsets, ws, st);
+  if (e != hipSuccess || !rec(2 * HSTU_STAGE_NORM + 1)) return HSTU_ERR_HIP;
+
+  if (!rec(2 * HSTU_STAGE_OUT)) return HSTU_ERR_HIP;
+  e = launch_gemm_out(d, ws.q, w2, y, &ws.hdr->status, st);
+  if (e != hipSuccess || !rec(2 * HSTU_STAGE_OUT + 1)) return HSTU_ERR_HIP;
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes) {
+  hstu_status s = check_layer(desc);
+  if (s != HSTU_OK) return s;
+  if (bytes == nullptr) return HSTU_ERR_INVALID_ARG;
+  *bytes = make_layout(*desc).total;
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
+                           const int32_t* hist_len, const int32_t* page_table, void* k_pool, void* v_pool,
+                           const void* w1, const void* w2, const float* pos_bias, const float* ts_bias,
+                           const int64_t* timestamps, const int32_t* ts_offsets, void* y, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1, w2, pos_bias, ts_bias,
+                    timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
+                                 const int32_t* hist_len, const int32_t* page_table, void* k_pool,
+                                 void* v_pool, const void* w1, const void* w2, const float* pos_bias,
+                                 const float* ts_bias, const int64_t* timestamps, const int32_t* ts_offsets,
+                                 void* y, void* workspace, size_t workspace_bytes, void* hip_stream,
+                                 void* const* stage_events) {
+  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1, w2, pos_bias, ts_bias,
+                    timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, stage_events);
+}
+
+hstu_status kv_pages_append(const hstu_layer_desc* desc, const void* k_new, const void* v_new,
+                            const int32_t* new_offsets, const int32_t* hist_len, const int32_t* page_table,
+                            void* k_pool, void* v_pool, int32_t* device_status, void* hip_stream) {
+  hstu_status s = check_common(desc);
+  if (s != HSTU_OK) return s;
+  if (new_offsets == nullptr || hist_len == nullptr || page_table == nullptr || k_pool == nullptr ||
+      v_pool == nullptr || device_status == nullptr)
+    return HSTU_ERR_INVALID_ARG;
+  if (desc->total_new > 0 && (k_new == nullptr || v_new == nullptr)) return HSTU_ERR_INVALID_ARG;
+  hipError_t e = launch_append(*desc, k_new, v_new, new_offsets, hist_len, page_table, k_pool, v_pool,
+                               device_status, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? HSTU_OK : HSTU_ERR_HIP;
+}
+
+hstu_status hstu_read_device_status(const void* device_status, int32_t* code, void* hip_stream) {
+  if (device_status == nullptr || code == nullptr) return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return HSTU_ERR_HIP;
+  if (hipMemcpy(code, device_status, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return HSTU_ERR_HIP;
+  return *code == 0 ? HSTU_OK : HSTU_ERR_DEVICE;
+}
+
+const char* hstu_status_string(int32_t status) {
+  switch (status) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_INVALID_ARG: return "invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case HSTU_ERR_WORKSPACE: return "workspace too small";
+    case HSTU_ERR_HIP: return "HIP runtime error";
+    case HSTU_ERR_DEVICE: return "device status reports an error";
+    case HSTU_DEV_BAD_OFFSETS: return "device: new_offsets not a prefix sum ending at total_new";
+    case HSTU_DEV_BAD_HIST: return "device: negative hist_len";
+    case HSTU_DEV_CAPACITY: return "device: sequence longer than its page-table row";
+    case HSTU_DEV_BAD_PAGE: return "device: page id outside the pool";
+    case HSTU_DEV_BAD_TS: return "device: ts_offsets do not match sequence lengths";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Internal definitions shared by the gfx950 kernels of libhstu.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hstu.h"
+
+namespace hstu {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kQB = 64;          // query rows per attention work item
+constexpr int kMaxBuckets = 1024;
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.  A fragment holds 8 elements per lane.  For a 16x16 tile
+// product D = A*B with a 32-deep contraction, lane l supplies A[l&15][k] and
+// B[k][l&15] for the 8 contraction indices k = 8*(l>>4) + e, e = 0..7; the
+// result lands as D[4*(l>>4) + i][l&15], i = 0..3.
+// bf16: one v_mfma_f32_16x16x32_bf16.  fp32: eight v_mfma_f32_16x16x4_f32,
+// instruction e contracting over {8*g + e : g = 0..3} -- the same index set,
+// so both element types share every load and layout.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ f32x4 mma16(const Frag<bf16>& a, const Frag<bf16>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const Frag<float>& a, const Frag<float>& b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ void load_frag(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float>& f, const float* p) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void zero_frag(Frag<bf16>& f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = static_cast<bf16>(0.0f);
+}
+__device__ __forceinline__ void zero_frag(Frag<float>& f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = 0.0f;
+}
+__device__ __forceinline__ void set_elem(Frag<bf16>& f, int e, float x) { f.v[e] = static_cast<bf16>(x); }
+__device__ __forceinline__ void set_elem(Frag<float>& f, int e, float x) { f.v[e] = x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z), with the hardware exp and
+// reciprocal.  Large negative z gives e^-z = inf and a result of -0.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// Log-linear relative-distance bucket (m mantissa bits, nb buckets).
+__device__ __forceinline__ int bucket32(int delta, int m, int nb) {
+  const uint32_t d = delta < 0 ? 0u : static_cast<uint32_t>(delta);
+  int b;
+  if (d < (1u << m)) {
+    b = static_cast<int>(d);
+  } else {
+    const int e = 31 - __clz(d);
+    b = ((e - m + 1) << m) + static_cast<int>(d >> (e - m)) - (1 << m);
+  }
+  return b < nb - 1 ? b : nb - 1;
+}
+__device__ __forceinline__ int bucket64(int64_t delta, int m, int nb) {
+  if (delta < 0) delta = 0;
+  const uint64_t d = static_cast<uint64_t>(delta);
+  int64_t b;
+  if (d < (1ull << m)) {
+    b = static_cast<int64_t>(d);
+  } else {
+    const int e = 63 - __clzll(d);
+    b = (static_cast<int64_t>(e - m + 1) << m) + static_cast<int64_t>(d >> (e - m)) - (1ll << m);
+  }
+  return b < nb - 1 ? static_cast<int>(b) : nb - 1;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// Index of the user owning jagged row r (largest u with offsets[u] <= r);
+// offsets must be a validated non-decreasing prefix sum.
+__device__ __forceinline__ int row_to_user(const int32_t* offsets, int B, int r) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of one hstu_layer_fwd call (offsets computed on the host).
+// ---------------------------------------------------------------------------
+struct WsHeader {            // first 256 bytes of the workspace
+  int32_t status;            // hstu_device_code of this call
+  int32_t n_items;           // attention work items
+  int32_t chunk_keys;        // keys per attention split
+  int32_t counter;           // dynamic work-fetch counter
+};
+
+struct WsPtrs {
+  WsHeader* hdr;
+  int32_t* row_user;         // [T]
+  int32_t* qb_base;          // [B+1]   first q-block entry of each user
+  int32_t* qb_first;         // [nqb_cap] first work item of a q-block entry (head 0)
+  int32_t* qb_nch;           // [nqb_cap] key chunks of a q-block entry
+  int4* items;               // [item_cap] {user, q-block, head, chunk}
+  void* q;                   // [T, D] dtype; reused for G after attention
+  void* u;                   // [T, D] dtype
+  float* part;               // [item_cap, kQB, d] fp32 partial attention outputs
+};
+
+// Host launchers (one per kernel family), all enqueue on `stream`.
+hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
+                       const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
+                       int nqb_cap, int item_cap, int target_items, hipStream_t stream);
+hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1,
+                           const int32_t* new_off, const int32_t* hist, const int32_t* pt,
+                           void* k_pool, void* v_pool, const WsPtrs& ws, hipStream_t stream);
+hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2, void* y,
+                           const int32_t* status, hipStream_t stream);
+hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
+                       const int32_t* pt, const void* k_pool, const void* v_pool,
+                       const float* pos_bias, const float* ts_bias, const int64_t* ts,
+                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream);
+hipError_t launch_norm_gate(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws,
+                            hipStream_t stream);
+hipError_t launch_append(const hstu_layer_desc& d, const void* k_new, const void* v_new,
+                         const int32_t* new_off, const int32_t* hist, const int32_t* pt,
+                         void* k_pool, void* v_pool, int32_t* status, hipStream_t stream);
+
+}  // namespace hstu

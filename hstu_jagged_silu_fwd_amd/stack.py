@@ -1,0 +1,103 @@
+"""A stack of HSTU layers sharing one paged KV pool (device buffers owned by
+torch; every layer step runs in libhstu).
+
+Each layer has its own weights, bias tables and page table into the shared
+pool; layer l's output rows are layer l+1's input rows.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import _lib
+
+
+class HSTUStack:
+    def __init__(self, *, num_users: int, num_heads: int, head_dim: int, page_size: int,
+                 num_pool_pages: int, max_pages_per_user: int, pos_buckets: int,
+                 pos_mbits: int, attn_scale: float, norm_eps: float = 1e-6,
+                 dtype: str = "bf16", ts_buckets: int = 0, ts_mbits: int = 0,
+                 num_layers: int = 1, device: str = "cuda", pool_fill: Optional[float] = None):
+        self.B, self.H, self.d = num_users, num_heads, head_dim
+        self.D = num_heads * head_dim
+        self.ps, self.P, self.maxP = page_size, num_pool_pages, max_pages_per_user
+        self.dtype = dtype
+        self.tdtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.device = torch.device(device)
+        self.common = dict(num_users=num_users, num_heads=num_heads, head_dim=head_dim,
+                           page_size=page_size, max_pages_per_user=max_pages_per_user,
+                           num_pool_pages=num_pool_pages, pos_buckets=pos_buckets,
+                           pos_mbits=pos_mbits, attn_scale=attn_scale, norm_eps=norm_eps,
+                           dtype=dtype, ts_buckets=ts_buckets, ts_mbits=ts_mbits)
+        shape_k = (num_pool_pages, num_heads, page_size, head_dim)
+        shape_v = (num_pool_pages, num_heads, head_dim, page_size)
+        if pool_fill is None:
+            self.k_pool = torch.empty(shape_k, dtype=self.tdtype, device=self.device)
+            self.v_pool = torch.empty(shape_v, dtype=self.tdtype, device=self.device)
+        else:
+            self.k_pool = torch.full(shape_k, pool_fill, dtype=self.tdtype, device=self.device)
+            self.v_pool = torch.full(shape_v, pool_fill, dtype=self.tdtype, device=self.device)
+        self.layers: List[dict] = [dict() for _ in range(num_layers)]
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self._ws = None
+
+    def desc(self, total_new: int) -> _lib.LayerDesc:
+        return _lib.make_desc(total_new=total_new, **self.common)
+
+    def _dev(self, a, dtype):
+        t = torch.as_tensor(a)
+        return t.to(device=self.device, dtype=dtype).contiguous()
+
+    def set_layer(self, l: int, *, w1, w2, pos_bias, page_table, ts_bias=None) -> None:
+        self.layers[l] = dict(
+            w1=self._dev(w1, self.tdtype), w2=self._dev(w2, self.tdtype),
+            pos_bias=self._dev(pos_bias, torch.float32),
+            ts_bias=None if ts_bias is None else self._dev(ts_bias, torch.float32),
+            page_table=self._dev(page_table, torch.int32))
+
+    def workspace(self, total_new: int) -> torch.Tensor:
+        need = _lib.workspace_size(self.desc(total_new))
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def append(self, l: int, k_new, v_new, new_offsets, hist_len, stream=None) -> None:
+        """kv_pages_append of rows into layer l's pages (status in self.status)."""
+        k_new = self._dev(k_new, self.tdtype)
+        v_new = self._dev(v_new, self.tdtype)
+        off = self._dev(new_offsets, torch.int32)
+        T = int(k_new.shape[0])
+        _lib.kv_pages_append(self.desc(T), k_new, v_new, off, self._dev(hist_len, torch.int32),
+                             self.layers[l]["page_table"], self.k_pool, self.v_pool, self.status,
+                             stream=stream)
+
+    def layer(self, l: int, x: torch.Tensor, new_offsets: torch.Tensor, hist_len: torch.Tensor,
+              y: torch.Tensor, workspace: Optional[torch.Tensor] = None, timestamps=None,
+              ts_offsets=None, stream=None, stage_events=None) -> None:
+        T = int(x.shape[0])
+        ws = self.workspace(T) if workspace is None else workspace
+        L = self.layers[l]
+        _lib.layer_fwd(self.desc(T), x, new_offsets, hist_len, L["page_table"], self.k_pool,
+                       self.v_pool, L["w1"], L["w2"], L["pos_bias"], y, ws,
+                       ts_bias=L["ts_bias"], timestamps=timestamps, ts_offsets=ts_offsets,
+                       stream=stream, stage_events=stage_events)
+
+    def forward(self, x, new_offsets, hist_len, timestamps=None, ts_offsets=None,
+                stream=None, return_all: bool = False):
+        """Run every layer; returns the last layer's output (or all outputs)."""
+        x = self._dev(x, self.tdtype)
+        off = self._dev(new_offsets, torch.int32)
+        hl = self._dev(hist_len, torch.int32)
+        ts = None if timestamps is None else self._dev(timestamps, torch.int64)
+        tso = None if ts_offsets is None else self._dev(ts_offsets, torch.int32)
+        outs = []
+        for l in range(len(self.layers)):
+            y = torch.empty_like(x)
+            self.layer(l, x, off, hl, y, timestamps=ts, ts_offsets=tso, stream=stream)
+            outs.append(y)
+            x = y
+        return outs if return_all else outs[-1]
+
+    def read_status(self, workspace: Optional[torch.Tensor] = None) -> int:
+        return _lib.read_device_status(self._ws if workspace is None else workspace)

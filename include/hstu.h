@@ -1,0 +1,191 @@
+/*
+ * hstu.h -- C ABI of libhstu: the HSTU layer forward over jagged per-user
+ * sequences whose cached history K/V lives in a paged GPU KV pool, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the layer computes (per layer, per user u with c cached tokens and n
+ * new rows; head h of H, head dim d, hidden D = H*d):
+ *   Z = SiLU(X W1); U, V, Q, K = the four D-wide column blocks of Z, in that
+ *       order; head h owns columns [h*d, (h+1)*d) of each block.
+ *   New row t sits at absolute position p = c + t.  For each key j <= p:
+ *       s = <Q[t,h], K[j,h]> + pos_bias[b(p-j)] (+ ts_bias[b_ts(ts[p]-ts[j])])
+ *       O[t,h] = attn_scale * sum_j SiLU(s) * V[j,h]          (no softmax)
+ *   G = LayerNorm_row(O) (mean/population variance over the D entries of a
+ *       row, eps = norm_eps, no affine) * U;   Y = G W2.
+ *   Keys/values j < c come from the pool; the new rows' K and V are appended
+ *   into the pool by the same call and read back from it.
+ * Sources: NVIDIA technical blog "Deploying an HSTU generative recommender
+ * with NVIDIA Dynamo-Triton", section "Why serving large sequential
+ * recommenders is hard" (jagged inputs, reuse of cached history K/V, a paged
+ * GPU KV data table with append, an HSTU attention kernel reading the paged
+ * cache); aitrends.kr article 100093, section "HSTU sequential modelling"
+ * (SiLU weighting instead of softmax, relative attention bias, elementwise
+ * gating before the output projection).  The exact block split, 1/N scale,
+ * LayerNorm and bucket rule are this library's readings of that prose.
+ *
+ * Bucket rule b(delta) (mantissa bits m, s = 2^m, nb buckets):
+ *   delta < 0 -> 0;  delta < s -> delta;
+ *   else e = floor(log2 delta), b = s*(e-m+1) + (delta >> (e-m)) - s;
+ *   b = min(b, nb-1).
+ *
+ * KV pool layout (both pools hold `dtype` elements, P = num_pool_pages,
+ * ps = page_size):
+ *   user u's position p lives in page page_table[u*max_pages_per_user + p/ps],
+ *   slot p % ps;
+ *   k_pool[P][H][ps][d]  -- element (page, h, slot, e)
+ *   v_pool[P][H][d][ps]  -- element (page, h, e, slot)   (V stored transposed
+ *                           per page so the attention kernel reads key-
+ *                           contiguous V runs)
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers unless stated, row-major,
+ *     allocated and owned by the caller.  The library never allocates, frees
+ *     or caches device memory and keeps no mutable global state.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream)
+ *     and runs asynchronously; calls return before the GPU finishes.
+ *   - Host-checkable problems (null pointer, inconsistent sizes, unsupported
+ *     shape/dtype, workspace too small) return a negative hstu_status and
+ *     enqueue nothing.
+ *   - Data-dependent problems (offsets not a non-decreasing prefix sum ending
+ *     at total_new, negative history length, a sequence longer than its page
+ *     table row, a page id outside [0, num_pool_pages)) are detected on the
+ *     device: the call's device status word receives a nonzero
+ *     hstu_device_code and every later kernel of that call writes nothing
+ *     (y, pools and workspace outputs keep their previous contents).
+ *   - Calls on the same stream are ordered; concurrent calls need distinct
+ *     workspaces and must not append to the same pool slots.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = -1,   /* null pointer, bad size or inconsistent descriptor */
+  HSTU_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / dtype not supported */
+  HSTU_ERR_WORKSPACE = -3,     /* workspace_bytes smaller than required */
+  HSTU_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
+  HSTU_ERR_DEVICE = -5         /* device status word holds a nonzero code */
+} hstu_status;
+
+typedef enum {
+  HSTU_F32 = 0,   /* fp32 storage and fp32 arithmetic */
+  HSTU_BF16 = 1   /* bf16 storage, fp32 accumulation and score math */
+} hstu_dtype;
+
+/* Codes written to the device status word. */
+typedef enum {
+  HSTU_DEV_OK = 0,
+  HSTU_DEV_BAD_OFFSETS = 1,    /* new_offsets[0] != 0, decreasing, or [B] != total_new */
+  HSTU_DEV_BAD_HIST = 2,       /* hist_len[u] < 0 */
+  HSTU_DEV_CAPACITY = 3,       /* hist_len[u] + n_u > max_pages_per_user * page_size */
+  HSTU_DEV_BAD_PAGE = 4,       /* a needed page id outside [0, num_pool_pages) */
+  HSTU_DEV_BAD_TS = 5          /* ts_offsets[u+1]-ts_offsets[u] != hist_len[u]+n_u */
+} hstu_device_code;
+
+typedef struct {
+  int32_t num_users;           /* B >= 0 */
+  int32_t num_heads;           /* H >= 1 */
+  int32_t head_dim;            /* d: 32, 64 or 128 */
+  int32_t hidden;              /* D = H*d, a multiple of 64 */
+  int32_t page_size;           /* ps: 16, 32, 64 or 128 tokens */
+  int32_t max_pages_per_user;  /* row stride of page_table */
+  int64_t num_pool_pages;      /* P: pages in each pool */
+  int32_t total_new;           /* T = new_offsets[B], rows of x and y */
+  int32_t pos_buckets;         /* nb in [1, 1024] */
+  int32_t pos_mbits;           /* m in [0, 16] */
+  int32_t ts_buckets;          /* 0 = no timestamp term, else in [1, 1024] */
+  int32_t ts_mbits;            /* m for the timestamp-delta rule */
+  float attn_scale;            /* 1/N */
+  float norm_eps;              /* LayerNorm epsilon (> 0) */
+  int32_t dtype;               /* hstu_dtype */
+} hstu_layer_desc;
+
+/* Bytes of device workspace hstu_layer_fwd needs for `desc` (depends only on
+ * B, H, d, D, total_new and dtype).  Host-only; enqueues nothing. */
+hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes);
+
+/* One HSTU layer over a jagged batch of new rows (see the top of this file).
+ *   x            [T, D] dtype     new rows of all users back to back
+ *   new_offsets  [B+1]  int32     prefix sums of new-row counts; user u owns
+ *                                 rows new_offsets[u] .. new_offsets[u+1]-1
+ *   hist_len     [B]    int32     tokens of user u already in the pool (this
+ *                                 layer); not advanced by the library
+ *   page_table   [B, max_pages_per_user] int32, -1 = unused entry; entries
+ *                                 for positions [0, hist_len+n) must be valid
+ *   k_pool, v_pool                pools (layout above); the new rows' K and V
+ *                                 are written at positions hist_len[u] + t
+ *   w1           [D, 4D] dtype    columns: U | V | Q | K blocks
+ *   w2           [D, D]  dtype
+ *   pos_bias     [pos_buckets] float32
+ *   ts_bias      [ts_buckets]  float32, or NULL when ts_buckets == 0
+ *   timestamps   int64, jagged over every position (history then new) of each
+ *                user; user u's run starts at ts_offsets[u]; NULL when
+ *                ts_buckets == 0
+ *   ts_offsets   [B+1] int32 or NULL
+ *   y            [T, D] dtype     output; must not alias x
+ *   workspace    device scratch of hstu_layer_workspace_size bytes (256-byte
+ *                aligned); its first int32 is the call's device status word
+ * total_new == 0 is a valid no-op. */
+hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x,
+                           const int32_t* new_offsets, const int32_t* hist_len,
+                           const int32_t* page_table, void* k_pool, void* v_pool,
+                           const void* w1, const void* w2, const float* pos_bias,
+                           const float* ts_bias, const int64_t* timestamps,
+                           const int32_t* ts_offsets, void* y, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
+/* Same as hstu_layer_fwd, and additionally records caller-created hipEvent_t
+ * handles around each stage so a caller can time the stages on the stream the
+ * kernels run on.  stage_events holds 2*HSTU_NUM_STAGES events (start, stop
+ * per stage, in the order of hstu_stage); NULL behaves like hstu_layer_fwd. */
+typedef enum {
+  HSTU_STAGE_PREP = 0,         /* index prep / validation / work list */
+  HSTU_STAGE_PROJ = 1,         /* X W1 + SiLU + split + K/V append */
+  HSTU_STAGE_ATTN = 2,         /* paged SiLU attention */
+  HSTU_STAGE_NORM = 3,         /* row norm * U */
+  HSTU_STAGE_OUT = 4,          /* G W2 */
+  HSTU_NUM_STAGES = 5
+} hstu_stage;
+hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x,
+                                 const int32_t* new_offsets, const int32_t* hist_len,
+                                 const int32_t* page_table, void* k_pool, void* v_pool,
+                                 const void* w1, const void* w2, const float* pos_bias,
+                                 const float* ts_bias, const int64_t* timestamps,
+                                 const int32_t* ts_offsets, void* y, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream,
+                                 void* const* stage_events);
+
+/* Append new rows' K and V into the pools (the paged KV table's append, NVIDIA
+ * blog above, same section).  k_new, v_new [T, D] dtype, rows laid out as x in
+ * hstu_layer_fwd; row t of user u goes to position hist_len[u] + t.  Only
+ * those slots are written; the copy is bit-exact.  Uses desc fields num_users,
+ * num_heads, head_dim, hidden, page_size, max_pages_per_user, num_pool_pages,
+ * total_new and dtype.  device_status: one device int32 that receives this
+ * call's hstu_device_code (0 on success); on a nonzero code nothing is
+ * written to the pools. */
+hstu_status kv_pages_append(const hstu_layer_desc* desc, const void* k_new,
+                            const void* v_new, const int32_t* new_offsets,
+                            const int32_t* hist_len, const int32_t* page_table,
+                            void* k_pool, void* v_pool, int32_t* device_status,
+                            void* hip_stream);
+
+/* Waits for `hip_stream`, then copies the device status word at
+ * `device_status` (a workspace base or kv_pages_append's status int) to
+ * *code.  Returns HSTU_ERR_DEVICE when *code != 0. */
+hstu_status hstu_read_device_status(const void* device_status, int32_t* code,
+                                    void* hip_stream);
+
+/* Static description of a hstu_status or hstu_device_code value. */
+const char* hstu_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSTU_H_ */

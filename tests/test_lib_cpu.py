@@ -1,0 +1,73 @@
+"""Host-side checks of libhstu that need no GPU: the library loads, exports
+every function the header declares, sizes workspaces, and rejects bad
+descriptors before touching the device."""
+import ctypes
+
+import pytest
+
+import hstu_jagged_silu_fwd_amd as hs
+from hstu_jagged_silu_fwd_amd import _lib
+
+
+def desc(**over):
+    kw = dict(num_users=8, num_heads=4, head_dim=128, page_size=32, max_pages_per_user=136,
+              num_pool_pages=1 << 16, total_new=1000, pos_buckets=128, pos_mbits=3,
+              attn_scale=1 / 4096, norm_eps=1e-6, dtype="bf16")
+    kw.update(over)
+    return hs.make_desc(**kw)
+
+
+def test_exports_every_header_function():
+    lib = hs.load()
+    names = list(hs.header_functions())
+    assert set(names) == {"hstu_layer_workspace_size", "hstu_layer_fwd", "hstu_layer_fwd_timed",
+                          "kv_pages_append", "hstu_read_device_status", "hstu_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_desc_struct_layout():
+    # int32 x6, int64, int32 x5, float x2, int32 -> 64 bytes with the int64 aligned at 24.
+    assert ctypes.sizeof(_lib.LayerDesc) == 64
+    assert _lib.LayerDesc.num_pool_pages.offset == 24
+
+
+def test_workspace_size_grows_with_rows():
+    a = hs.workspace_size(desc(total_new=100))
+    b = hs.workspace_size(desc(total_new=10000))
+    assert 0 < a < b
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=96), -2),
+    (dict(page_size=24), -2),
+    (dict(page_size=8), -2),
+    (dict(num_heads=0), -1),
+    (dict(pos_buckets=0), -1),
+    (dict(pos_buckets=4096), -1),
+    (dict(norm_eps=0.0), -1),
+    (dict(dtype="f32", head_dim=32, num_heads=1), -2),   # hidden 32 not a multiple of 64
+    (dict(total_new=-1), -1),
+])
+def test_bad_descriptors_rejected(over, code):
+    with pytest.raises(hs.HSTUError) as ei:
+        hs.workspace_size(desc(**over))
+    assert ei.value.code == code
+
+
+def test_null_pointers_rejected_before_any_device_work():
+    lib = hs.load()
+    d = desc()
+    rc = lib.hstu_layer_fwd(ctypes.byref(d), *([None] * 14), ctypes.c_size_t(0), None)
+    assert rc == -1
+    rc = lib.kv_pages_append(ctypes.byref(d), *([None] * 8), None)
+    assert rc == -1
+    code = ctypes.c_int32(0)
+    assert lib.hstu_read_device_status(None, ctypes.byref(code), None) == -1
+
+
+def test_status_strings():
+    assert hs.status_string(0) == "ok"
+    assert "workspace" in hs.status_string(-3)
+    assert "page" in hs.status_string(4)

@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark: new-token throughput of a 3-layer bf16 HSTU stack over a 100%-hit
+paged KV cache at batch 8, on one MI355X.
+
+Workload (synthetic, seeded): 8 users per step, cached history U{256..4096}
+tokens and U{16..256} new tokens per user, hidden 512, 4 heads, head dim 128,
+32-token pages scattered over a 2^16-page pool, 128 log-buckets of relative
+position, scale 1/4096.  A step runs the three layers over one batch; the new
+K/V of every layer is appended into the pool by the projection kernel.  To keep
+the KV stream honest against the 256 MB Infinity Cache, steps rotate over
+`--instances` independent batches (different users and pages) whose KV
+working set together exceeds that cache.
+
+Prints one JSON line with the throughput, the attention kernel's roofline
+position (HBM-bound: algorithmic bytes / its mean duration, timed with HIP
+events recorded around it on the stream it runs on) and a CPU baseline (the
+fp64 oracle on a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HSTU layer new-tokens/sec at batch 8 (paged KV hit); % bf16 MFMA peak, HBM GB/s"
+WORKLOAD_CFG = 3
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+EPS = 1e-6
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--instances", type=int, default=6)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-events", action="store_true", help="time without per-stage events")
+    return ap.parse_args()
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+        import hstu_jagged_silu_fwd_amd as hs
+        from hstu_jagged_silu_fwd_amd import _lib
+        from workloads import make_workload
+
+        self.torch, self.hs, self._lib = torch, hs, _lib
+        self.lib = hs.load()
+        self.hip = _lib.hip_runtime()
+        self.R = args.instances
+        B = 8
+        self.wl = wl = make_workload(WORKLOAD_CFG, seed=args.seed, B=B * self.R)
+        self.L, self.D, self.H, self.d = wl.layers, wl.D, wl.H, wl.d
+        dev = torch.device("cuda")
+        bf = torch.bfloat16
+        self.k_pool = torch.empty((wl.num_pool_pages, wl.H, wl.page_size, wl.d), dtype=bf, device=dev)
+        self.v_pool = torch.empty((wl.num_pool_pages, wl.H, wl.d, wl.page_size), dtype=bf, device=dev)
+        common = dict(num_heads=wl.H, head_dim=wl.d, page_size=wl.page_size,
+                      max_pages_per_user=wl.max_pages, num_pool_pages=wl.num_pool_pages,
+                      pos_buckets=wl.pos_buckets, pos_mbits=wl.pos_mbits,
+                      attn_scale=wl.attn_scale, norm_eps=EPS, dtype="bf16")
+        self.common = common
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.layers = []
+        hoff = np.concatenate([[0], np.cumsum(wl.hist_len.astype(np.int64))]).astype(np.int32)
+        for l in range(self.L):
+            li = wl.layer(l)
+            lay = dict(w1=torch.from_numpy(li.w1).to(dev, bf), w2=torch.from_numpy(li.w2).to(dev, bf),
+                       pos_bias=torch.from_numpy(li.pos_bias).to(dev),
+                       pt_all=torch.from_numpy(li.page_table).to(dev))
+            # history of all users of all instances, positions 0..hist-1
+            k = torch.from_numpy(np.concatenate(li.hist_k)).to(dev, bf)
+            v = torch.from_numpy(np.concatenate(li.hist_v)).to(dev, bf)
+            d_app = hs.make_desc(num_users=wl.B, total_new=int(hoff[-1]), **common)
+            hs.kv_pages_append(d_app, k, v, torch.from_numpy(hoff).to(dev),
+                               torch.zeros(wl.B, dtype=torch.int32, device=dev), lay["pt_all"],
+                               self.k_pool, self.v_pool, status)
+            assert hs.read_device_status(status) == 0
+            del k, v
+            self.layers.append(lay)
+        # per-instance buffers and prebuilt argument lists
+        self.inst = []
+        ws_bytes = 0
+        for i in range(self.R):
+            us = list(range(B * i, B * (i + 1)))
+            off = wl.new_offsets
+            rows = slice(int(off[us[0]]), int(off[us[-1] + 1]))
+            T = rows.stop - rows.start
+            newl = wl.new_len[us]
+            hist = wl.hist_len[us]
+            io = dict(T=T, users=us, new_len=newl, hist=hist,
+                      off=torch.from_numpy(np.concatenate([[0], np.cumsum(newl)]).astype(np.int32)).to(dev),
+                      hist_t=torch.from_numpy(hist.astype(np.int32)).to(dev),
+                      x=torch.from_numpy(wl.x0[rows]).to(dev, bf),
+                      ys=[torch.empty((T, self.D), dtype=bf, device=dev) for _ in range(self.L)],
+                      pts=[lay["pt_all"][B * i:B * (i + 1)].contiguous() for lay in self.layers],
+                      desc=hs.make_desc(num_users=B, total_new=T, **common))
+            ws_bytes = max(ws_bytes, hs.workspace_size(io["desc"]))
+            self.inst.append(io)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream().cuda_stream
+        P = ctypes.c_void_p
+        for io in self.inst:
+            args = []
+            for l in range(self.L):
+                lay = self.layers[l]
+                x = io["x"] if l == 0 else io["ys"][l - 1]
+                args.append((ctypes.byref(io["desc"]), P(x.data_ptr()), P(io["off"].data_ptr()),
+                             P(io["hist_t"].data_ptr()), P(io["pts"][l].data_ptr()),
+                             P(self.k_pool.data_ptr()), P(self.v_pool.data_ptr()),
+                             P(lay["w1"].data_ptr()), P(lay["w2"].data_ptr()),
+                             P(lay["pos_bias"].data_ptr()), None, None, None,
+                             P(io["ys"][l].data_ptr()), P(self.ws.data_ptr()),
+                             ctypes.c_size_t(ws_bytes), P(self.stream)))
+            io["args"] = args
+        torch.cuda.synchronize()
+
+    def step(self, s, events=None):
+        io = self.inst[s % self.R]
+        for l in range(self.L):
+            if events is None:
+                rc = self.lib.hstu_layer_fwd(*io["args"][l])
+            else:
+                rc = self.lib.hstu_layer_fwd_timed(*io["args"][l], events[l])
+            if rc != 0:
+                raise RuntimeError(f"hstu_layer_fwd failed: {rc}")
+
+    def make_events(self, steps):
+        hip = self.hip
+        hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        n = 2 * self._lib.NUM_STAGES
+        evs = []
+        for _ in range(steps):
+            per_layer = []
+            for _ in range(self.L):
+                arr = (ctypes.c_void_p * n)()
+                for j in range(n):
+                    e = ctypes.c_void_p()
+                    assert hip.hipEventCreate(ctypes.byref(e)) == 0
+                    arr[j] = e
+                per_layer.append(arr)
+            evs.append(per_layer)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float(0)
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return ms.value
+
+    def attn_work(self, io):
+        """Algorithmic bytes and FLOPs of one attention launch on instance io."""
+        D = self.D
+        kv = 0
+        flops = 0
+        for c, n in zip(io["hist"].tolist(), io["new_len"].tolist()):
+            kv += (c + n) * 4 * D                 # K and V rows (bf16) read once
+            flops += 4 * D * (n * c + n * (n + 1) // 2)
+        T = io["T"]
+        return kv + T * D * 2 + T * D * 4, flops, kv
+
+
+def cpu_baseline(wl, B):
+    """The fp64 oracle (as it stands) on instance 0: 8 users, all layers."""
+    import threadpoolctl
+    from oracle import layer as olayer
+    us = list(range(B))
+    off = wl.new_offsets
+    x = wl.x0[int(off[0]):int(off[B])]
+    t0 = time.perf_counter()
+    for l in range(wl.layers):
+        li = wl.layer(l)
+        r = olayer.layer_forward(x, wl.new_len[us], wl.hist_len[us], [li.hist_k[u] for u in us],
+                                 [li.hist_v[u] for u in us], li.w1, li.w2, li.pos_bias, wl.pos_mbits,
+                                 wl.attn_scale, EPS, wl.H)
+        x = r["y"]
+    dt = time.perf_counter() - t0
+    T = int(off[B])
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return dict(value=T / dt, unit="new tokens/s", cores=int(threads), kind="oracle",
+                sample=f"one batch of the same workload: {B} users, {T} new rows, "
+                       f"{int(wl.hist_len[us].sum())} cached tokens, {wl.layers} layers, fp64 numpy "
+                       f"({dt:.1f} s)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+    import torch
+    b = Bench(args)
+    for s in range(args.warmup):
+        b.step(s)
+    torch.cuda.synchronize()
+    events = None if args.no_events else b.make_events(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        b.step(s, None if events is None else events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    tokens = sum(b.inst[s % b.R]["T"] for s in range(args.steps))
+    value = tokens / wall
+    out = dict(metric=METRIC, value=value, unit="new tokens/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=1e3 * wall / args.steps, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+               config=dict(workload=b.wl.cfg["name"], layers=b.L, batch=8, hidden=b.D, heads=b.H,
+                           head_dim=b.d, page_size=b.wl.page_size, pool_pages=b.wl.num_pool_pages,
+                           hist="U{256..4096}", new="U{16..256}", instances=b.R,
+                           new_tokens_per_step=tokens / args.steps,
+                           per_layer_new_tokens_per_s=value * b.L))
+    if events is not None:
+        stage_ms = np.zeros(b._lib.NUM_STAGES)
+        attn_bytes = attn_flops = 0
+        n_launch = 0
+        for s in range(args.steps):
+            io = b.inst[s % b.R]
+            by, fl, _ = b.attn_work(io)
+            for l in range(b.L):
+                ev = events[s][l]
+                for k in range(b._lib.NUM_STAGES):
+                    stage_ms[k] += b.elapsed_ms(ev[2 * k], ev[2 * k + 1])
+                attn_bytes += by
+                attn_flops += fl
+                n_launch += 1
+        attn_s = stage_ms[2] / 1e3
+        achieved = attn_bytes / attn_s / 1e9
+        out["roofline"] = dict(kernel="paged_silu_attn", bound="hbm", achieved=achieved,
+                               peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                               traffic=None, mean_us=1e6 * attn_s / n_launch,
+                               bytes_per_launch=attn_bytes / n_launch,
+                               mfma_tflops=attn_flops / attn_s / 1e12,
+                               mfma_frac=attn_flops / attn_s / 1e12 / BF16_PEAK_TFLOPS)
+        out["stages_us"] = {name: 1e3 * stage_ms[k] / n_launch for k, name in enumerate(b._lib.STAGES)}
+        out["kernel_sum_ms_per_step"] = float(stage_ms.sum() / args.steps)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(b.wl, 8)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

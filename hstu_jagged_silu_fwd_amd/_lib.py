@@ -56,6 +56,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} not found: build it with `python -m hstu_jagged_silu_fwd_amd.build`")
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Importing torch first makes the loader bind libhstu to that runtime, so
+    # torch's device pointers and streams are valid in our calls and only one
+    # HIP runtime lives in the process.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     dp = ctypes.POINTER(LayerDesc)
@@ -75,6 +80,22 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     _ = I64
     _lib = lib
     return lib
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime the library is bound to (for events in benchmarks)."""
+    load()
+    return ctypes.CDLL("libamdhip64.so.7")
+
+
+def loaded_hip_runtimes() -> Sequence[str]:
+    """Paths of every libamdhip64 mapped into this process."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return sorted(paths)
 
 
 def header_functions(path: str = HEADER_PATH) -> Sequence[str]:

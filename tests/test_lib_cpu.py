@@ -71,3 +71,9 @@ def test_status_strings():
     assert hs.status_string(0) == "ok"
     assert "workspace" in hs.status_string(-3)
     assert "page" in hs.status_string(4)
+
+
+def test_single_hip_runtime_in_process():
+    hs.load()
+    rts = _lib.loaded_hip_runtimes()
+    assert len(rts) == 1, rts

@@ -29,6 +29,9 @@ CFLAGS = [
     "-Wno-unused-result",
     # keep the compiler from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the attention kernel's accumulators and
+    # fragment buffers then fit the register file without spilling
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -10,8 +10,7 @@ using namespace hstu;
 
 namespace {
 
-constexpr int kTargetItems = 512;   // attention split target (see prep.hip)
-constexpr int kAttnWgPerCu = 4;
+constexpr int kAttnWgPerCu = 1;     // resident attention workgroups per CU
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -20,19 +19,32 @@ struct Layout {
   int nqb_cap, item_cap;
 };
 
-Layout make_layout(const hstu_layer_desc& d) {
+// Attention workgroups launched (and the split target): one per CU.
+int attn_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus * kAttnWgPerCu;
+}
+
+Layout make_layout(const hstu_layer_desc& d, int target) {
   Layout L{};
   const size_t T = static_cast<size_t>(d.total_new);
   const size_t B = static_cast<size_t>(d.num_users);
   const size_t es = d.dtype == HSTU_BF16 ? 2 : 4;
   L.nqb_cap = static_cast<int>((T + kQB - 1) / kQB + B);
-  L.item_cap = d.num_heads * L.nqb_cap + kTargetItems;
+  // items <= total/chunk + H * entries, and total/chunk <= target unless the
+  // chunk hits its cap, where it is <= H * entries * ceil(max_len / cap).
+  const int64_t max_len = static_cast<int64_t>(d.max_pages_per_user) * d.page_size;
+  const int64_t per_entry = 1 + (max_len + kMaxChunkKeys - 1) / kMaxChunkKeys;
+  L.item_cap = static_cast<int>(d.num_heads * L.nqb_cap * per_entry + target);
   size_t off = 256;  // WsHeader
   L.row_user = off; off = align256(off + 4 * T);
   L.qb_base = off;  off = align256(off + 4 * (B + 1));
   L.qb_first = off; off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
   L.qb_nch = off;   off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
-  L.items = off;    off = align256(off + 16 * static_cast<size_t>(L.item_cap));
+  L.items = off;    off = align256(off + sizeof(AttnItem) * static_cast<size_t>(L.item_cap));
   L.q = off;        off = align256(off + es * T * d.hidden);
   L.u = off;        off = align256(off + es * T * d.hidden);
   L.part = off;     off = align256(off + 4 * static_cast<size_t>(L.item_cap) * kQB * d.head_dim);
@@ -48,7 +60,7 @@ WsPtrs ws_ptrs(void* base, const Layout& L) {
   w.qb_base = reinterpret_cast<int32_t*>(b + L.qb_base);
   w.qb_first = reinterpret_cast<int32_t*>(b + L.qb_first);
   w.qb_nch = reinterpret_cast<int32_t*>(b + L.qb_nch);
-  w.items = reinterpret_cast<int4*>(b + L.items);
+  w.items = reinterpret_cast<AttnItem*>(b + L.items);
   w.q = b + L.q;
   w.u = b + L.u;
   w.part = reinterpret_cast<float*>(b + L.part);
@@ -60,6 +72,8 @@ bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1))
 // Shape checks shared by every entry point.
 hstu_status check_common(const hstu_layer_desc* d) {
   if (d == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (d->num_users > kMaxUsers) return HSTU_ERR_UNSUPPORTED;
+  if (d->total_new > kMaxRows) return HSTU_ERR_UNSUPPORTED;
   if (d->num_users < 0 || d->num_heads < 1 || d->total_new < 0 || d->max_pages_per_user < 1 ||
       d->num_pool_pages < 1)
     return HSTU_ERR_INVALID_ARG;
@@ -103,7 +117,8 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   if (d.ts_buckets > 0 && (ts_bias == nullptr || timestamps == nullptr || ts_offsets == nullptr))
     return HSTU_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return HSTU_ERR_INVALID_ARG;
-  const Layout L = make_layout(d);
+  const int grid = attn_grid();
+  const Layout L = make_layout(d, grid);
   if (workspace_bytes < L.total) return HSTU_ERR_WORKSPACE;
   const WsPtrs ws = ws_ptrs(workspace, L);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -117,7 +132,7 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   };
   hipError_t e;
   if (!rec(2 * HSTU_STAGE_PREP)) return HSTU_ERR_HIP;
-  e = launch_prep(d, new_offsets, hist_len, page_table, ts_off, ws, L.nqb_cap, L.item_cap, kTargetItems, st);
+  e = launch_prep(d, new_offsets, hist_len, page_table, ts_off, ws, L.nqb_cap, L.item_cap, grid, st);
   if (e != hipSuccess || !rec(2 * HSTU_STAGE_PREP + 1)) return HSTU_ERR_HIP;
   if (!any_rows) return HSTU_OK;
 
@@ -125,14 +140,9 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   e = launch_gemm_qkv(d, x, w1, new_offsets, hist_len, page_table, k_pool, v_pool, ws, st);
   if (e != hipSuccess || !rec(2 * HSTU_STAGE_PROJ + 1)) return HSTU_ERR_HIP;
 
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return HSTU_ERR_HIP;
-  int grid = cus * kAttnWgPerCu;
-  if (grid > L.item_cap) grid = L.item_cap;
   if (!rec(2 * HSTU_STAGE_ATTN)) return HSTU_ERR_HIP;
-  e = launch_attn(d, new_offsets, hist_len, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ws, grid, st);
+  e = launch_attn(d, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ws,
+                  grid < L.item_cap ? grid : L.item_cap, st);
   if (e != hipSuccess || !rec(2 * HSTU_STAGE_ATTN + 1)) return HSTU_ERR_HIP;
 
   if (!rec(2 * HSTU_STAGE_NORM)) return HSTU_ERR_HIP;
@@ -153,7 +163,7 @@ hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes
   hstu_status s = check_layer(desc);
   if (s != HSTU_OK) return s;
   if (bytes == nullptr) return HSTU_ERR_INVALID_ARG;
-  *bytes = make_layout(*desc).total;
+  *bytes = make_layout(*desc, attn_grid()).total;
   return HSTU_OK;
 }
 

@@ -11,10 +11,16 @@ namespace hstu {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kQB = 64;          // query rows per attention work item
+constexpr int kQB = 64;          // query rows per attention work item (q-block)
+constexpr int kMaxUsers = 4096;  // users per call (metadata is cached in LDS)
+constexpr float kNegLn2 = -0.6931471805599453f;
 constexpr int kMaxBuckets = 1024;
+constexpr int kMaxChunkKeys = 8192;   // attention split never exceeds this many keys
+constexpr int kMaxRows = 1 << 18;     // new rows per call
+constexpr int kMaxQBlocks = kMaxRows / kQB + kMaxUsers;
 
 // ---------------------------------------------------------------------------
 // MFMA fragments.  A fragment holds 8 elements per lane.  For a 16x16 tile
@@ -122,13 +128,20 @@ struct WsHeader {            // first 256 bytes of the workspace
   int32_t counter;           // dynamic work-fetch counter
 };
 
+// One attention work item: a = {user, first row of the q-block, head, first
+// key}, b = {end key, first jagged row of the user, new rows, history}.
+struct AttnItem {
+  int4 a;
+  int4 b;
+};
+
 struct WsPtrs {
   WsHeader* hdr;
   int32_t* row_user;         // [T]
   int32_t* qb_base;          // [B+1]   first q-block entry of each user
   int32_t* qb_first;         // [nqb_cap] first work item of a q-block entry (head 0)
   int32_t* qb_nch;           // [nqb_cap] key chunks of a q-block entry
-  int4* items;               // [item_cap] {user, q-block, head, chunk}
+  AttnItem* items;           // [item_cap]
   void* q;                   // [T, D] dtype; reused for G after attention
   void* u;                   // [T, D] dtype
   float* part;               // [item_cap, kQB, d] fp32 partial attention outputs
@@ -143,8 +156,7 @@ hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* 
                            void* k_pool, void* v_pool, const WsPtrs& ws, hipStream_t stream);
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2, void* y,
                            const int32_t* status, hipStream_t stream);
-hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
-                       const int32_t* pt, const void* k_pool, const void* v_pool,
+hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,
                        const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream);
 hipError_t launch_norm_gate(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws,

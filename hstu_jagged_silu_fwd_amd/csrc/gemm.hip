@@ -128,7 +128,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, cons
           if (blk == 0) {
             ep.u[static_cast<size_t>(row) * D + cc] = z;
           } else if (blk == 2) {
-            ep.q[static_cast<size_t>(row) * D + cc] = z;
+            // queries are stored pre-scaled by -log2(e) for the exp2-domain SiLU
+            ep.q[static_cast<size_t>(row) * D + cc] = from_f32<T>(-1.4426950408889634f * silu(acc[i][j][r]));
           } else {
             const int h = cc / ep.hd, e = cc % ep.hd;
             if (blk == 3)

@@ -1,6 +1,7 @@
 // Row norm and gating: O = attn_scale * (sum of the row's chunk partials, in
-// chunk order), then G = LayerNorm_row(O) * U, the elementwise gating that
-// precedes the output projection (aitrends.kr article 100093, "HSTU
+// chunk order; the partials hold -log2(e) * sum SiLU(s) v, undone here), then
+// G = LayerNorm_row(O) * U, the elementwise gating that precedes the output
+// projection (aitrends.kr article 100093, "HSTU
 // sequential modelling").  One wavefront per row; mean and variance come from
 // wavefront reductions over the row's D entries (population variance, no
 // affine).  G overwrites the Q buffer, which is dead after the attention.
@@ -79,8 +80,20 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormArgs<T> a) {
     if (col < D) {
       const int h = col / a.hd, e = col % a.hd;
       const float* src = a.part + (static_cast<size_t>(first + h * nch) * kQB + tl) * a.hd + e;
-      for (int kc = 0; kc < nch; ++kc) {
-        const float4 v = *reinterpret_cast<const float4*>(src + static_cast<size_t>(kc) * kQB * a.hd);
+      const size_t stride = static_cast<size_t>(kQB) * a.hd;
+      int kc = 0;
+      for (; kc + 4 <= nch; kc += 4) {   // four independent loads in flight, summed in chunk order
+        const float4 v0 = *reinterpret_cast<const float4*>(src + (kc + 0) * stride);
+        const float4 v1 = *reinterpret_cast<const float4*>(src + (kc + 1) * stride);
+        const float4 v2 = *reinterpret_cast<const float4*>(src + (kc + 2) * stride);
+        const float4 v3 = *reinterpret_cast<const float4*>(src + (kc + 3) * stride);
+        x[k][0] += v0.x; x[k][1] += v0.y; x[k][2] += v0.z; x[k][3] += v0.w;
+        x[k][0] += v1.x; x[k][1] += v1.y; x[k][2] += v1.z; x[k][3] += v1.w;
+        x[k][0] += v2.x; x[k][1] += v2.y; x[k][2] += v2.z; x[k][3] += v2.w;
+        x[k][0] += v3.x; x[k][1] += v3.y; x[k][2] += v3.z; x[k][3] += v3.w;
+      }
+      for (; kc < nch; ++kc) {
+        const float4 v = *reinterpret_cast<const float4*>(src + kc * stride);
         x[k][0] += v.x; x[k][1] += v.y; x[k][2] += v.z; x[k][3] += v.w;
       }
 #pragma unroll
@@ -133,7 +146,7 @@ hipError_t norm_t(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs
   a.T_rows = d.total_new;
   a.D = d.hidden;
   a.hd = d.head_dim;
-  a.scale = d.attn_scale;
+  a.scale = d.attn_scale * kNegLn2;   // the attention accumulates -log2(e) * SiLU
   a.eps = d.norm_eps;
   const int grid = (d.total_new + 3) / 4;
   norm_gate_kernel<T><<<grid, 256, 0, stream>>>(a);

@@ -1,5 +1,6 @@
 // Index prep for one layer call: validates the jagged/paged metadata, maps
-// rows to users, and builds the attention work list.
+// rows to users, and builds the attention work list.  One workgroup; all
+// per-user and per-q-block metadata is kept in LDS while it is built.
 //
 // Work decomposition: the new rows of user u are cut into q-blocks of kQB
 // rows; q-block qb sees keys [0, hist + min(n, (qb+1)*kQB)) (causal).  The key
@@ -7,15 +8,18 @@
 // (fixed absolute boundaries), one work item per (user, q-block, head, chunk).
 // Because the attention has no softmax, the partial outputs of the chunks of
 // a row simply add; the norm kernel sums them in chunk order.
-// chunk_keys = max(kMinChunk, round_up(total_keys / target_items, 64)) keeps
-// the item count near target_items + H * (#q-blocks).
+// The chunk length bound ck = clamp(round_up(total_keys / budget, 64), 64,
+// kMaxChunkKeys) keeps the item count within the number of resident attention
+// workgroups; each entry's keys are then cut into ceil(keys / ck) chunks of
+// near-equal length (multiples of 64).
 #include "common.h"
 
 namespace hstu {
 namespace {
 
 constexpr int kPrepThreads = 1024;
-constexpr int kMinChunk = 256;
+constexpr int kPrepWaves = kPrepThreads / kWave;
+constexpr int kMinChunk = 64;
 
 struct PrepArgs {
   const int32_t* new_off;
@@ -28,25 +32,43 @@ struct PrepArgs {
   int nqb_cap, item_cap, target_items;
 };
 
-__device__ void set_err(int* s_err, int code) { atomicCAS(s_err, 0, code); }
+struct PrepShared {
+  int err;
+  int64_t wsum[kPrepWaves];
+  int32_t off[kMaxUsers + 1];
+  int32_t hist[kMaxUsers];
+  int32_t qbb[kMaxUsers + 1];      // first q-block entry of each user
+  int32_t qbn[kMaxQBlocks];        // chunks per q-block entry
+  int32_t qbf[kMaxQBlocks];        // first work item of each q-block entry
+};
 
-// In-place exclusive scan of v[0..n) by the whole block; returns the total.
-__device__ int64_t block_scan_inplace(int32_t* v, int n, int64_t* s_tmp) {
-  const int tid = threadIdx.x;
+__device__ void set_err(PrepShared& s, int code) { atomicCAS(&s.err, 0, code); }
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// In-place exclusive scan of v[0..n) (LDS) by the whole block; returns the total.
+__device__ int64_t block_scan(int32_t* v, int n, PrepShared& s) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int seg = (n + kPrepThreads - 1) / kPrepThreads;
   const int lo = min(n, tid * seg), hi = min(n, lo + seg);
   int64_t sum = 0;
   for (int i = lo; i < hi; ++i) sum += v[i];
-  s_tmp[tid] = sum;
+  const int64_t incl = wave_incl_scan(sum, lane);
+  if (lane == kWave - 1) s.wsum[w] = incl;
   __syncthreads();
-  for (int off = 1; off < kPrepThreads; off <<= 1) {
-    const int64_t add = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += add;
-    __syncthreads();
+  int64_t before = 0, total = 0;
+  for (int i = 0; i < kPrepWaves; ++i) {
+    if (i < w) before += s.wsum[i];
+    total += s.wsum[i];
   }
-  int64_t run = s_tmp[tid] - sum;
-  const int64_t total = s_tmp[kPrepThreads - 1];
+  int64_t run = before + incl - sum;
   for (int i = lo; i < hi; ++i) {
     const int32_t x = v[i];
     v[i] = static_cast<int32_t>(run);
@@ -56,60 +78,73 @@ __device__ int64_t block_scan_inplace(int32_t* v, int n, int64_t* s_tmp) {
   return total;
 }
 
-__device__ int64_t block_sum(int64_t x, int64_t* s_tmp) {
-  const int tid = threadIdx.x;
-  s_tmp[tid] = x;
+__device__ int64_t block_sum(int64_t x, PrepShared& s) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  if (lane == 0) s.wsum[w] = x;
   __syncthreads();
-  for (int off = kPrepThreads / 2; off > 0; off >>= 1) {
-    if (tid < off) s_tmp[tid] += s_tmp[tid + off];
-    __syncthreads();
+  int64_t t = 0;
+  for (int i = 0; i < kPrepWaves; ++i) t += s.wsum[i];
+  __syncthreads();
+  return t;
+}
+
+// Entry e -> (user, q-block) by binary search over the user's first entries.
+__device__ __forceinline__ int entry_user(const int32_t* qbb, int B, int e) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qbb[mid] <= e) lo = mid; else hi = mid - 1;
   }
-  const int64_t r = s_tmp[0];
-  __syncthreads();
-  return r;
+  return lo;
 }
 
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
-  __shared__ int s_err;
-  __shared__ int64_t s_tmp[kPrepThreads];
-  const int tid = threadIdx.x;
+  __shared__ PrepShared s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   WsHeader* hdr = a.ws.hdr;
-  if (tid == 0) s_err = 0;
+  const int B = a.B;
+  if (tid == 0) s.err = 0;
+  for (int u = tid; u <= B; u += kPrepThreads) s.off[u] = a.new_off[u];
+  for (int u = tid; u < B; u += kPrepThreads) s.hist[u] = a.hist[u];
   __syncthreads();
 
   // 1. metadata checks
-  if (tid == 0 && a.B == 0 && a.T != 0) set_err(&s_err, HSTU_DEV_BAD_OFFSETS);
-  for (int u = tid; u < a.B; u += kPrepThreads) {
-    const int o0 = a.new_off[u], o1 = a.new_off[u + 1];
-    if ((u == 0 && o0 != 0) || o1 < o0 || (u == a.B - 1 && o1 != a.T)) set_err(&s_err, HSTU_DEV_BAD_OFFSETS);
-    const int c = a.hist[u];
+  if (tid == 0 && B == 0 && a.T != 0) set_err(s, HSTU_DEV_BAD_OFFSETS);
+  for (int u = tid; u < B; u += kPrepThreads) {
+    const int o0 = s.off[u], o1 = s.off[u + 1];
+    if ((u == 0 && o0 != 0) || o1 < o0 || (u == B - 1 && o1 != a.T)) set_err(s, HSTU_DEV_BAD_OFFSETS);
+    const int c = s.hist[u];
     if (c < 0) {
-      set_err(&s_err, HSTU_DEV_BAD_HIST);
+      set_err(s, HSTU_DEV_BAD_HIST);
     } else if (static_cast<int64_t>(c) + (o1 - o0) > static_cast<int64_t>(a.maxP) * a.ps) {
-      set_err(&s_err, HSTU_DEV_CAPACITY);
+      set_err(s, HSTU_DEV_CAPACITY);
     }
     if (a.ts_off != nullptr) {
       if ((u == 0 && a.ts_off[0] != 0) ||
           static_cast<int64_t>(a.ts_off[u + 1]) - a.ts_off[u] != static_cast<int64_t>(c) + (o1 - o0))
-        set_err(&s_err, HSTU_DEV_BAD_TS);
+        set_err(s, HSTU_DEV_BAD_TS);
     }
   }
   __syncthreads();
-  if (s_err == 0) {
-    for (int u = 0; u < a.B; ++u) {
-      const int len = a.hist[u] + (a.new_off[u + 1] - a.new_off[u]);
+  if (s.err == 0) {
+    // page ids of every position in use: one wavefront per user
+    for (int u = w; u < B; u += kPrepWaves) {
+      const int len = s.hist[u] + (s.off[u + 1] - s.off[u]);
       const int npg = (len + a.ps - 1) / a.ps;
       const int32_t* row = a.pt + static_cast<size_t>(u) * a.maxP;
-      for (int j = tid; j < npg; j += kPrepThreads) {
+      for (int j = lane; j < npg; j += kWave) {
         const int32_t pg = row[j];
-        if (pg < 0 || pg >= a.P) set_err(&s_err, HSTU_DEV_BAD_PAGE);
+        if (pg < 0 || pg >= a.P) set_err(s, HSTU_DEV_BAD_PAGE);
       }
     }
   }
   __syncthreads();
-  if (s_err != 0) {
+  if (s.err != 0) {
     if (tid == 0) {
-      hdr->status = s_err;
+      hdr->status = s.err;
       hdr->n_items = 0;
       hdr->chunk_keys = 0;
       hdr->counter = 0;
@@ -118,41 +153,42 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   }
 
   // 2. q-block entries per user
-  for (int u = tid; u < a.B; u += kPrepThreads)
-    a.ws.qb_base[u] = (a.new_off[u + 1] - a.new_off[u] + kQB - 1) / kQB;
+  for (int u = tid; u < B; u += kPrepThreads) s.qbb[u] = (s.off[u + 1] - s.off[u] + kQB - 1) / kQB;
   __syncthreads();
-  const int64_t nqb = block_scan_inplace(a.ws.qb_base, a.B, s_tmp);
-  if (tid == 0) a.ws.qb_base[a.B] = static_cast<int32_t>(nqb);
+  const int nqb = static_cast<int>(block_scan(s.qbb, B, s));
+  if (tid == 0) s.qbb[B] = nqb;
+  __syncthreads();
 
   // 3. chunk size from the total key work
   int64_t local = 0;
-  for (int u = 0; u < a.B; ++u) {
-    const int n = a.new_off[u + 1] - a.new_off[u];
-    const int c = a.hist[u];
-    const int nq = (n + kQB - 1) / kQB;
-    for (int qb = tid; qb < nq; qb += kPrepThreads) local += c + min(n, (qb + 1) * kQB);
+  for (int e = tid; e < nqb; e += kPrepThreads) {
+    const int u = entry_user(s.qbb, B, e);
+    const int qb = e - s.qbb[u];
+    const int n = s.off[u + 1] - s.off[u];
+    local += s.hist[u] + min(n, (qb + 1) * kQB);
   }
-  const int64_t total = block_sum(local, s_tmp) * a.H;
-  int64_t ck = (total + a.target_items - 1) / a.target_items;
+  const int64_t total = block_sum(local, s) * a.H;
+  // Rounding adds at most one item per (entry, head); aim below the target
+  // by that much so one pass of resident workgroups covers every item.
+  const int64_t slack = static_cast<int64_t>(a.H) * nqb;
+  const int64_t budget = max(a.target_items - slack, static_cast<int64_t>(a.target_items / 2));
+  int64_t ck = (total + budget - 1) / budget;
   ck = (ck + 63) / 64 * 64;
   if (ck < kMinChunk) ck = kMinChunk;
-  if (ck > (1 << 30)) ck = 1 << 30;
+  if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
 
   // 4. chunks per entry, then first item of each entry
-  for (int u = 0; u < a.B; ++u) {
-    const int n = a.new_off[u + 1] - a.new_off[u];
-    const int c = a.hist[u];
-    const int nq = (n + kQB - 1) / kQB;
-    const int base = a.ws.qb_base[u];
-    for (int qb = tid; qb < nq; qb += kPrepThreads) {
-      const int64_t keys = c + min(n, (qb + 1) * kQB);
-      const int nch = static_cast<int>((keys + ck - 1) / ck);
-      a.ws.qb_nch[base + qb] = nch;
-      a.ws.qb_first[base + qb] = nch * a.H;
-    }
+  for (int e = tid; e < nqb; e += kPrepThreads) {
+    const int u = entry_user(s.qbb, B, e);
+    const int qb = e - s.qbb[u];
+    const int n = s.off[u + 1] - s.off[u];
+    const int64_t keys = s.hist[u] + min(n, (qb + 1) * kQB);
+    const int nch = static_cast<int>((keys + ck - 1) / ck);
+    s.qbn[e] = nch;
+    s.qbf[e] = nch * a.H;
   }
   __syncthreads();
-  const int64_t n_items = block_scan_inplace(a.ws.qb_first, static_cast<int>(nqb), s_tmp);
+  const int64_t n_items = block_scan(s.qbf, nqb, s);
   if (n_items > a.item_cap) {
     if (tid == 0) {
       hdr->status = HSTU_DEV_CAPACITY;
@@ -163,21 +199,31 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     return;
   }
 
-  // 5. the work list
-  for (int u = 0; u < a.B; ++u) {
-    const int n = a.new_off[u + 1] - a.new_off[u];
-    const int nq = (n + kQB - 1) / kQB;
-    const int base = a.ws.qb_base[u];
-    for (int qb = tid; qb < nq; qb += kPrepThreads) {
-      const int f = a.ws.qb_first[base + qb];
-      const int nch = a.ws.qb_nch[base + qb];
-      for (int h = 0; h < a.H; ++h)
-        for (int kc = 0; kc < nch; ++kc) a.ws.items[f + h * nch + kc] = make_int4(u, qb, h, kc);
-    }
+  // 5. the work list and the per-entry tables used by the norm kernel
+  for (int e = tid; e < nqb; e += kPrepThreads) {
+    const int u = entry_user(s.qbb, B, e);
+    const int qb = e - s.qbb[u];
+    const int f = s.qbf[e], nch = s.qbn[e];
+    a.ws.qb_first[e] = f;
+    a.ws.qb_nch[e] = nch;
+    const int n = s.off[u + 1] - s.off[u];
+    const int c = s.hist[u];
+    const int keys = c + min(n, (qb + 1) * kQB);
+    // the entry's keys are cut into nch near-equal chunks (multiples of 64)
+    const int csz = ((keys + nch - 1) / nch + 63) / 64 * 64;
+    for (int h = 0; h < a.H; ++h)
+      for (int kc = 0; kc < nch; ++kc) {
+        const int k_lo = kc * csz;
+        AttnItem it;
+        it.a = make_int4(u, qb * kQB, h, k_lo);
+        it.b = make_int4(min(keys, k_lo + csz), s.off[u], n, c);
+        a.ws.items[f + h * nch + kc] = it;
+      }
   }
+  for (int u = tid; u <= B; u += kPrepThreads) a.ws.qb_base[u] = s.qbb[u];
 
   // 6. row -> user
-  for (int r = tid; r < a.T; r += kPrepThreads) a.ws.row_user[r] = row_to_user(a.new_off, a.B, r);
+  for (int r = tid; r < a.T; r += kPrepThreads) a.ws.row_user[r] = row_to_user(s.off, B, r);
 
   if (tid == 0) {
     hdr->status = 0;

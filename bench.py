@@ -77,7 +77,7 @@ class Bench:
         hoff = np.concatenate([[0], np.cumsum(wl.hist_len.astype(np.int64))]).astype(np.int32)
         for l in range(self.L):
             li = wl.layer(l)
-            lay = dict(w1=torch.from_numpy(li.w1).to(dev, bf), w2=torch.from_numpy(li.w2).to(dev, bf),
+            lay = dict(w1t=torch.from_numpy(li.w1t).to(dev, bf), w2t=torch.from_numpy(li.w2t).to(dev, bf),
                        pos_bias=torch.from_numpy(li.pos_bias).to(dev),
                        pt_all=torch.from_numpy(li.page_table).to(dev))
             # history of all users of all instances, positions 0..hist-1
@@ -120,7 +120,7 @@ class Bench:
                 args.append((ctypes.byref(io["desc"]), P(x.data_ptr()), P(io["off"].data_ptr()),
                              P(io["hist_t"].data_ptr()), P(io["pts"][l].data_ptr()),
                              P(self.k_pool.data_ptr()), P(self.v_pool.data_ptr()),
-                             P(lay["w1"].data_ptr()), P(lay["w2"].data_ptr()),
+                             P(lay["w1t"].data_ptr()), P(lay["w2t"].data_ptr()),
                              P(lay["pos_bias"].data_ptr()), None, None, None,
                              P(io["ys"][l].data_ptr()), P(self.ws.data_ptr()),
                              ctypes.c_size_t(ws_bytes), P(self.stream)))

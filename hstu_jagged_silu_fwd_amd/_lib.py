@@ -163,7 +163,7 @@ def workspace_size(desc: LayerDesc) -> int:
 
 
 def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_pool,
-              w1, w2, pos_bias, y, workspace, ts_bias=None, timestamps=None,
+              w1t, w2t, pos_bias, y, workspace, ts_bias=None, timestamps=None,
               ts_offsets=None, stream=None, stage_events=None) -> None:
     """Enqueue one layer (see include/hstu.h).  `workspace` is a uint8 device
     tensor of at least workspace_size(desc) bytes; `stage_events` optionally
@@ -179,8 +179,8 @@ def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_p
         _ptr(page_table, "page_table", torch.int32),
         _ptr(k_pool, "k_pool", dt),
         _ptr(v_pool, "v_pool", dt),
-        _ptr(w1, "w1", dt),
-        _ptr(w2, "w2", dt),
+        _ptr(w1t, "w1t", dt),
+        _ptr(w2t, "w2t", dt),
         _ptr(pos_bias, "pos_bias", torch.float32),
         _ptr(ts_bias, "ts_bias", torch.float32, allow_none=True),
         _ptr(timestamps, "timestamps", torch.int64, allow_none=True),

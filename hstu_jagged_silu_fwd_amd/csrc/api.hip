@@ -15,7 +15,7 @@ constexpr int kAttnWgPerCu = 1;     // resident attention workgroups per CU
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-  size_t row_user, qb_base, qb_first, qb_nch, items, q, u, part, total;
+  size_t row_user, row_loc, qb_base, qb_first, qb_nch, items, q, u, part, total;
   int nqb_cap, item_cap;
 };
 
@@ -41,6 +41,7 @@ Layout make_layout(const hstu_layer_desc& d, int target) {
   L.item_cap = static_cast<int>(d.num_heads * L.nqb_cap * per_entry + target);
   size_t off = 256;  // WsHeader
   L.row_user = off; off = align256(off + 4 * T);
+  L.row_loc = off;  off = align256(off + 8 * T);
   L.qb_base = off;  off = align256(off + 4 * (B + 1));
   L.qb_first = off; off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
   L.qb_nch = off;   off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
@@ -57,6 +58,7 @@ WsPtrs ws_ptrs(void* base, const Layout& L) {
   WsPtrs w;
   w.hdr = reinterpret_cast<WsHeader*>(b);
   w.row_user = reinterpret_cast<int32_t*>(b + L.row_user);
+  w.row_loc = reinterpret_cast<int2*>(b + L.row_loc);
   w.qb_base = reinterpret_cast<int32_t*>(b + L.qb_base);
   w.qb_first = reinterpret_cast<int32_t*>(b + L.qb_first);
   w.qb_nch = reinterpret_cast<int32_t*>(b + L.qb_nch);
@@ -102,7 +104,7 @@ hstu_status check_layer(const hstu_layer_desc* d) {
 
 hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
                        const int32_t* hist_len, const int32_t* page_table, void* k_pool, void* v_pool,
-                       const void* w1, const void* w2, const float* pos_bias, const float* ts_bias,
+                       const void* w1t, const void* w2t, const float* pos_bias, const float* ts_bias,
                        const int64_t* timestamps, const int32_t* ts_offsets, void* y, void* workspace,
                        size_t workspace_bytes, void* hip_stream, void* const* ev) {
   hstu_status s = check_layer(desc);
@@ -110,7 +112,7 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   const hstu_layer_desc& d = *desc;
   const bool any_rows = d.total_new > 0;
   if (new_offsets == nullptr || hist_len == nullptr || page_table == nullptr || k_pool == nullptr ||
-      v_pool == nullptr || w1 == nullptr || w2 == nullptr || pos_bias == nullptr || workspace == nullptr)
+      v_pool == nullptr || w1t == nullptr || w2t == nullptr || pos_bias == nullptr || workspace == nullptr)
     return HSTU_ERR_INVALID_ARG;
   if (any_rows && (x == nullptr || y == nullptr)) return HSTU_ERR_INVALID_ARG;
   if (any_rows && x == y) return HSTU_ERR_INVALID_ARG;
@@ -137,7 +139,7 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   if (!any_rows) return HSTU_OK;
 
   if (!rec(2 * HSTU_STAGE_PROJ)) return HSTU_ERR_HIP;
-  e = launch_gemm_qkv(d, x, w1, new_offsets, hist_len, page_table, k_pool, v_pool, ws, st);
+  e = launch_gemm_qkv(d, x, w1t, k_pool, v_pool, ws, st);
   if (e != hipSuccess || !rec(2 * HSTU_STAGE_PROJ + 1)) return HSTU_ERR_HIP;
 
   if (!rec(2 * HSTU_STAGE_ATTN)) return HSTU_ERR_HIP;
@@ -150,7 +152,7 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   if (e != hipSuccess || !rec(2 * HSTU_STAGE_NORM + 1)) return HSTU_ERR_HIP;
 
   if (!rec(2 * HSTU_STAGE_OUT)) return HSTU_ERR_HIP;
-  e = launch_gemm_out(d, ws.q, w2, y, &ws.hdr->status, st);
+  e = launch_gemm_out(d, ws.q, w2t, y, &ws.hdr->status, st);
   if (e != hipSuccess || !rec(2 * HSTU_STAGE_OUT + 1)) return HSTU_ERR_HIP;
   return HSTU_OK;
 }
@@ -169,20 +171,20 @@ hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes
 
 hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
                            const int32_t* hist_len, const int32_t* page_table, void* k_pool, void* v_pool,
-                           const void* w1, const void* w2, const float* pos_bias, const float* ts_bias,
+                           const void* w1t, const void* w2t, const float* pos_bias, const float* ts_bias,
                            const int64_t* timestamps, const int32_t* ts_offsets, void* y, void* workspace,
                            size_t workspace_bytes, void* hip_stream) {
-  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1, w2, pos_bias, ts_bias,
+  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1t, w2t, pos_bias, ts_bias,
                     timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
                                  const int32_t* hist_len, const int32_t* page_table, void* k_pool,
-                                 void* v_pool, const void* w1, const void* w2, const float* pos_bias,
+                                 void* v_pool, const void* w1t, const void* w2t, const float* pos_bias,
                                  const float* ts_bias, const int64_t* timestamps, const int32_t* ts_offsets,
                                  void* y, void* workspace, size_t workspace_bytes, void* hip_stream,
                                  void* const* stage_events) {
-  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1, w2, pos_bias, ts_bias,
+  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1t, w2t, pos_bias, ts_bias,
                     timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, stage_events);
 }
 

@@ -138,6 +138,7 @@ struct AttnItem {
 struct WsPtrs {
   WsHeader* hdr;
   int32_t* row_user;         // [T]
+  int2* row_loc;             // [T] (pool page, slot) of each new row's K/V
   int32_t* qb_base;          // [B+1]   first q-block entry of each user
   int32_t* qb_first;         // [nqb_cap] first work item of a q-block entry (head 0)
   int32_t* qb_nch;           // [nqb_cap] key chunks of a q-block entry
@@ -151,10 +152,9 @@ struct WsPtrs {
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
                        const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream);
-hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1,
-                           const int32_t* new_off, const int32_t* hist, const int32_t* pt,
-                           void* k_pool, void* v_pool, const WsPtrs& ws, hipStream_t stream);
-hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2, void* y,
+hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
+                           void* v_pool, const WsPtrs& ws, hipStream_t stream);
+hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
                            const int32_t* status, hipStream_t stream);
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,

@@ -2,33 +2,33 @@
 //   * X W1 with the fused epilogue SiLU -> split U | V | Q | K -> U, Q into the
 //     workspace and K, V appended straight into their pool pages;
 //   * G W2 -> Y.
-// C[M, N] = A[M, K] * B[K, N], all row-major.  64x64 output tile per
-// 256-thread workgroup (2x2 waves, 32x32 per wave = 2x2 MFMA 16x16 blocks),
-// 32-deep K slices staged through LDS; B is transposed on its way into LDS so
-// that both operands are read as contiguous 8-element fragments.
+// C[M, N] = A[M, K] * W^T with W given as [N][K] (out-features x in-features,
+// the usual linear-layer weight layout), so both operands are K-contiguous rows.
+//
+// A BM x BN output tile per 256-thread workgroup (2 x 2 waves).  Operand rows
+// are 128-byte k-tile slices (64 bf16 or 32 fp32) copied global -> LDS by the
+// direct-to-LDS loads, eight rows (1 KiB) per wave instruction, with no
+// register staging.  The LDS is a ring of S k-tile stages: up to S-1 stages
+// are in flight while one is multiplied, which hides the load latency that
+// dominates these short-K products.  Within a row the 16-byte chunks are
+// XOR-permuted by (row & 7) so the MFMA fragment reads are bank-conflict free.
+//
+// Tiles are handed out XCD-aware: workgroup i runs on XCD i % 8, each XCD owns
+// a contiguous range of tiles, and within it groups of kGroupM row blocks walk
+// the column blocks together so both operand panels stay in that XCD's L2.
+//
+// The epilogue goes through LDS: row-major outputs (U, Q, Y) and K rows leave
+// as 16-byte stores, the transposed V columns as runs of consecutive slots.
 #include "common.h"
 
 namespace hstu {
 namespace {
 
-constexpr int BM = 64, BN = 64, BK = 32;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-template <typename T> struct Vec8 { T v[8]; };
-
-template <typename T>
-__device__ __forceinline__ Vec8<T> ld8(const T* p) {
-  Vec8<T> r;
-  constexpr int n16 = sizeof(Vec8<T>) / 16;
-#pragma unroll
-  for (int i = 0; i < n16; ++i) reinterpret_cast<uint4*>(&r)[i] = reinterpret_cast<const uint4*>(p)[i];
-  return r;
-}
-template <typename T>
-__device__ __forceinline__ void st8(T* p, const Vec8<T>& x) {
-  constexpr int n16 = sizeof(Vec8<T>) / 16;
-#pragma unroll
-  for (int i = 0; i < n16; ++i) reinterpret_cast<uint4*>(p)[i] = reinterpret_cast<const uint4*>(&x)[i];
-}
+constexpr int kRowBytes = 128;   // one k-tile row
+constexpr int kGroupM = 8;
 
 template <typename T>
 struct QkvEpi {
@@ -36,161 +36,315 @@ struct QkvEpi {
   T* u;
   T* k_pool;
   T* v_pool;
-  const int32_t* row_user;
-  const int32_t* new_off;
-  const int32_t* hist;
-  const int32_t* pt;
-  int D, H, hd, ps, maxP;
+  const int2* row_loc;       // (pool page, slot) of each row
+  int D, H, hd, ps;
 };
 
-template <typename T, bool kQkv>
-__global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ Bm,
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima so they do not wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load); LDS visibility of the direct loads is
+// established by the wait_vm each wave does before it.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void tile_of(int id, int Mt, int Nt, int& mt, int& nt) {
+  const int nT = Mt * Nt;
+  const int x = id & 7, local = id >> 3;
+  const int base = nT >> 3, rem = nT & 7;
+  const int t = x * base + min(x, rem) + local;
+  const int per_group = kGroupM * Nt;
+  const int grp = t / per_group, first = grp * kGroupM;
+  const int gsz = min(Mt - first, kGroupM);
+  const int r = t - grp * per_group;
+  mt = first + r % gsz;
+  nt = r / gsz;
+}
+
+__device__ __forceinline__ void read_frag(Frag<bf16>& f, const unsigned char* rowp, int chunk, int sw) {
+  f.v = *reinterpret_cast<const bf16x8*>(rowp + ((chunk ^ sw) << 4));
+}
+__device__ __forceinline__ void read_frag(Frag<float>& f, const unsigned char* rowp, int chunk, int sw) {
+  const float4 lo = *reinterpret_cast<const float4*>(rowp + ((chunk ^ sw) << 4));
+  const float4 hi = *reinterpret_cast<const float4*>(rowp + (((chunk + 1) ^ sw) << 4));
+  f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+  f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+}
+
+template <typename T, int BM, int BN, int S, int WGM, int WGN, bool kQkv>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
                                                    int M, int N, int K, T* __restrict__ Y,
                                                    QkvEpi<T> ep, const int32_t* status) {
+  constexpr int ES = static_cast<int>(sizeof(T));
+  constexpr int BK = kRowBytes / ES;
+  constexpr int CE = 16 / ES;                  // elements per 16-byte chunk
+  constexpr int NT = 64 * WGM * WGN;           // threads (waves laid out WGM x WGN)
+  constexpr int IPW = (BM + BN) / (8 * WGM * WGN);   // direct loads per wave per stage
+  static_assert(IPW * 8 * WGM * WGN == BM + BN, "whole 8-row blocks per wave");
+  constexpr int STAGE = (BM + BN) * kRowBytes;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int KSTEP_CHUNKS = ES == 2 ? 4 : 8;   // chunks consumed per MFMA k-step
+  constexpr int OST = BN + 16 / ES;            // epilogue staging row stride (elements)
+  static_assert(BM * OST * ES <= S * STAGE, "epilogue staging fits the ring");
+  static_assert(IPW * (S - 2) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
+
   if (*status != 0) return;
-  constexpr int PAD = 16 / sizeof(T);
-  __shared__ __attribute__((aligned(16))) T As[BM][BK + PAD];
-  __shared__ __attribute__((aligned(16))) T Bs[BN][BK + PAD];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int wm = w / WGN, wn = w % WGN;
+  const int Mt = (M + BM - 1) / BM, Nt = N / BN;
+  int mt, nt;
+  tile_of(blockIdx.x, Mt, Nt, mt, nt);
+  const int m0 = mt * BM, n0 = nt * BN;
+  int blk = 0;
+  if constexpr (kQkv) blk = n0 / ep.D;        // 0: U, 1: V, 2: Q, 3: K (a tile never straddles blocks)
+  // pool locations of a K or V tile's rows, fetched now and parked in LDS
+  // after the main loop
+  __shared__ int2 s_loc[kQkv ? BM : 1];
+  int2 my_loc = make_int2(0, 0);
+  if constexpr (kQkv)
+    if ((blk & 1) && tid < BM && m0 + tid < M) my_loc = ep.row_loc[m0 + tid];
 
-  const int a_row = tid >> 2, a_k = (tid & 3) * 8;
-  const int b_k = tid >> 3, b_n = (tid & 7) * 8;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    {
-      Vec8<T> va;
-      const int gr = m0 + a_row;
-      if (gr < M) {
-        va = ld8(A + static_cast<size_t>(gr) * K + k0 + a_k);
-      } else {
+  // Lane l of a direct load fills LDS chunk (l & 7) of row (l >> 3) of its
+  // 8-row block; that slot holds source chunk (l & 7) ^ (l >> 3).
+  const int lchunk = (lane & 7) ^ (lane >> 3);
+  const T* src[IPW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) va.v[e] = from_f32<T>(0.0f);
-      }
-      st8(&As[a_row][a_k], va);
-      const Vec8<T> vb = ld8(Bm + static_cast<size_t>(k0 + b_k) * N + n0 + b_n);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Bs[b_n + e][b_k] = vb.v[e];
-    }
-    __syncthreads();
-    Frag<T> af[2], bfr[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) load_frag(af[i], &As[wm * 32 + i * 16 + l16][g * 8]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_frag(bfr[j], &Bs[wn * 32 + j * 16 + l16][g * 8]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mma16(af[i], bfr[j], acc[i][j]);
-    __syncthreads();
+  for (int j = 0; j < IPW; ++j) {
+    const int r = 8 * (w * IPW + j) + (lane >> 3);
+    if (r < BM)
+      src[j] = A + static_cast<size_t>(min(m0 + r, M - 1)) * K + lchunk * CE;   // tail rows unused
+    else
+      src[j] = W + static_cast<size_t>(n0 + r - BM) * K + lchunk * CE;
   }
+  auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+    unsigned char* base = smem + buf * STAGE + w * IPW * 1024;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(src[j] + kt * BK), (lds_void_t*)(base + j * 1024), 16, 0, 0);
+  };
 
-  if constexpr (!kQkv) {
+  f32x4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int sw = l16 & 7;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const unsigned char* As = smem + buf * STAGE + (wm * WM + l16) * kRowBytes;
+    const unsigned char* Bs = smem + buf * STAGE + (BM + wn * WN + l16) * kRowBytes;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = m0 + wm * 32 + i * 16 + g * 4 + r;
-          const int col = n0 + wn * 32 + j * 16 + l16;
-          if (row < M) Y[static_cast<size_t>(row) * N + col] = from_f32<T>(acc[i][j][r]);
-        }
-  } else {
-    const int D = ep.D;
-    const int blk = n0 / D;      // 0: U, 1: V, 2: Q, 3: K (tile never straddles blocks)
+    for (int ks = 0; ks < 8 / KSTEP_CHUNKS; ++ks) {
+      const int chunk = ks * KSTEP_CHUNKS + (ES == 2 ? g : 2 * g);
+      Frag<T> af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i) read_frag(af[i], As + i * 16 * kRowBytes, chunk, sw);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) read_frag(bfr[j], Bs + j * 16 * kRowBytes, chunk, sw);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  const int KT = K / BK;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) issue(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + S - 2 < KT) wait_vm<IPW * (S - 2)>();
+    else wait_vm<0>();
+    bar();                                    // stage kt visible; stage kt-1 no longer read
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    compute(kt % S);
+  }
+  __syncthreads();
+
+  // ---- epilogue: stage the tile (after the epilogue transform) in LDS ----
+  if constexpr (kQkv)
+    if ((blk & 1) && tid < BM) s_loc[tid] = my_loc;
+  T* Os = reinterpret_cast<T*>(smem);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 32 + i * 16 + g * 4 + r;
-        if (row >= M) continue;
-        size_t kbase = 0, vbase = 0;
-        if (blk == 1 || blk == 3) {
-          const int user = ep.row_user[row];
-          const int p = ep.hist[user] + row - ep.new_off[user];
-          const int page = ep.pt[static_cast<size_t>(user) * ep.maxP + p / ep.ps];
-          const int slot = p % ep.ps;
-          kbase = static_cast<size_t>(page) * ep.H * ep.ps * ep.hd + static_cast<size_t>(slot) * ep.hd;
-          vbase = static_cast<size_t>(page) * ep.H * ep.hd * ep.ps + slot;
+        const int row = wm * WM + i * 16 + g * 4 + r;
+        const int col = wn * WN + j * 16 + l16;
+        float z = acc[i][j][r];
+        if constexpr (kQkv) {
+          z = silu(z);
+          // queries are stored pre-scaled by -log2(e) for the exp2-domain SiLU
+          if (blk == 2) z *= -1.4426950408889634f;
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 32 + j * 16 + l16;
-          const int cc = col - blk * D;
-          const T z = from_f32<T>(silu(acc[i][j][r]));
-          if (blk == 0) {
-            ep.u[static_cast<size_t>(row) * D + cc] = z;
-          } else if (blk == 2) {
-            // queries are stored pre-scaled by -log2(e) for the exp2-domain SiLU
-            ep.q[static_cast<size_t>(row) * D + cc] = from_f32<T>(-1.4426950408889634f * silu(acc[i][j][r]));
-          } else {
-            const int h = cc / ep.hd, e = cc % ep.hd;
-            if (blk == 3)
-              ep.k_pool[kbase + static_cast<size_t>(h) * ep.ps * ep.hd + e] = z;
-            else
-              ep.v_pool[vbase + (static_cast<size_t>(h) * ep.hd + e) * ep.ps] = z;
-          }
+        Os[row * OST + col] = from_f32<T>(z);
+      }
+  __syncthreads();
+
+  if (!kQkv || blk != 1) {
+    // row-major rows of BN elements as 16-byte chunks
+    constexpr int CPR = BN / CE;
+    for (int c = tid; c < BM * CPR; c += NT) {
+      const int row = c / CPR, ch = c % CPR;
+      const int gr = m0 + row;
+      if (gr >= M) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Os + row * OST + ch * CE);
+      const int col = n0 + ch * CE;
+      T* dst;
+      if constexpr (!kQkv) {
+        dst = Y + static_cast<size_t>(gr) * N + col;
+      } else {
+        const int cc = col - blk * ep.D;
+        if (blk == 0) {
+          dst = ep.u + static_cast<size_t>(gr) * ep.D + cc;
+        } else if (blk == 2) {
+          dst = ep.q + static_cast<size_t>(gr) * ep.D + cc;
+        } else {                                 // K: pool slot row of head cc / hd
+          const int2 loc = s_loc[row];
+          const int h = cc / ep.hd, e = cc % ep.hd;
+          dst = ep.k_pool + ((static_cast<size_t>(loc.x) * ep.H + h) * ep.ps + loc.y) * ep.hd + e;
         }
       }
+      *reinterpret_cast<u32x4*>(dst) = v;
+    }
+  } else if constexpr (kQkv) {
+    // V^T: a lane takes a pair of consecutive rows of one column, so lanes
+    // walk consecutive slots of a page; a pair that shares a page and starts
+    // at an even slot leaves as one store of two elements.
+    constexpr int RP = BM / 2;
+    static_assert(NT % RP == 0, "whole columns per pass");
+    const int pr = tid % RP;
+    const int r0 = 2 * pr, gr0 = m0 + r0;
+    if (gr0 < M) {
+      const bool has1 = gr0 + 1 < M;
+      const int2 l0 = s_loc[r0], l1 = s_loc[r0 + 1];
+      const bool pair = has1 && l1.x == l0.x && l1.y == l0.y + 1 && (l0.y & 1) == 0;
+      const size_t pb0 = static_cast<size_t>(l0.x) * ep.H, pb1 = static_cast<size_t>(l1.x) * ep.H;
+      const int cc0 = n0 - ep.D;
+      for (int col = tid / RP; col < BN; col += NT / RP) {
+        const int cc = cc0 + col;
+        const int h = cc / ep.hd, e = cc % ep.hd;
+        const T v0 = Os[r0 * OST + col], v1 = Os[(r0 + 1) * OST + col];
+        T* d0 = ep.v_pool + ((pb0 + h) * ep.hd + e) * ep.ps + l0.y;
+        if (pair) {
+          typedef T T2 __attribute__((ext_vector_type(2)));
+          T2 vv;
+          vv.x = v0;
+          vv.y = v1;
+          *reinterpret_cast<T2*>(d0) = vv;
+        } else {
+          *d0 = v0;
+          if (has1) ep.v_pool[((pb1 + h) * ep.hd + e) * ep.ps + l1.y] = v1;
+        }
+      }
+    }
   }
 }
 
-template <typename T>
-hipError_t gemm_qkv_t(const hstu_layer_desc& d, const void* x, const void* w1, const int32_t* new_off,
-                      const int32_t* hist, const int32_t* pt, void* k_pool, void* v_pool,
+template <typename T, int BM, int BN, int S, int WGM, int WGN>
+hipError_t gemm_qkv_t(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool, void* v_pool,
                       const WsPtrs& ws, hipStream_t stream) {
   QkvEpi<T> ep;
   ep.q = static_cast<T*>(ws.q);
   ep.u = static_cast<T*>(ws.u);
   ep.k_pool = static_cast<T*>(k_pool);
   ep.v_pool = static_cast<T*>(v_pool);
-  ep.row_user = ws.row_user;
-  ep.new_off = new_off;
-  ep.hist = hist;
-  ep.pt = pt;
+  ep.row_loc = ws.row_loc;
   ep.D = d.hidden;
   ep.H = d.num_heads;
   ep.hd = d.head_dim;
   ep.ps = d.page_size;
-  ep.maxP = d.max_pages_per_user;
   const int M = d.total_new, N = 4 * d.hidden, K = d.hidden;
-  dim3 grid((M + BM - 1) / BM, N / BN);
-  gemm_kernel<T, true><<<grid, 256, 0, stream>>>(static_cast<const T*>(x), static_cast<const T*>(w1),
-                                                 M, N, K, nullptr, ep, &ws.hdr->status);
+  const int tiles = (M + BM - 1) / BM * (N / BN);
+  gemm_kernel<T, BM, BN, S, WGM, WGN, true><<<tiles, 64 * WGM * WGN, 0, stream>>>(
+      static_cast<const T*>(x), static_cast<const T*>(w1t), M, N, K, nullptr, ep, &ws.hdr->status);
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t gemm_out_t(const hstu_layer_desc& d, const void* g, const void* w2, void* y,
+template <typename T, int BM, int BN, int S, int WGM, int WGN>
+hipError_t gemm_out_t(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
                       const int32_t* status, hipStream_t stream) {
   QkvEpi<T> ep{};
   const int M = d.total_new, N = d.hidden, K = d.hidden;
-  dim3 grid((M + BM - 1) / BM, N / BN);
-  gemm_kernel<T, false><<<grid, 256, 0, stream>>>(static_cast<const T*>(g), static_cast<const T*>(w2),
-                                                  M, N, K, static_cast<T*>(y), ep, status);
+  const int tiles = (M + BM - 1) / BM * (N / BN);
+  gemm_kernel<T, BM, BN, S, WGM, WGN, false><<<tiles, 64 * WGM * WGN, 0, stream>>>(
+      static_cast<const T*>(g), static_cast<const T*>(w2t), M, N, K, static_cast<T*>(y), ep, status);
   return hipGetLastError();
+}
+
+// Tile shape by problem size (two ring stages throughout: several workgroups
+// per CU beat deeper rings here, because a CU's load throughput grows with
+// the waves it has in flight):
+//   >= 1024 tiles of 128 x 128 -> 128 x 128, 8 waves (fewest operand re-reads);
+//   >= 256 such tiles          -> 64 x 128, 4 waves;
+//   otherwise                  -> 64 x 64, 4 waves (most workgroups).
+// Wide tiles need N % 128 == 0 (and, for X W1, every U|V|Q|K block whole).
+enum class Tile { k64x64, k64x128, k128x128 };
+Tile pick_tile(int M, int N, int D) {
+  if (D % 128 != 0 || N % 128 != 0) return Tile::k64x64;
+  const int64_t t128 = static_cast<int64_t>((M + 127) / 128) * (N / 128);
+  if (t128 >= 1024) return Tile::k128x128;
+  if (t128 >= 256) return Tile::k64x128;
+  return Tile::k64x64;
+}
+
+template <typename T>
+hipError_t qkv_dispatch(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool, void* v_pool,
+                        const WsPtrs& ws, hipStream_t st) {
+  if constexpr (sizeof(T) == 4) {
+    return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st);   // fp32: one tile shape
+  } else {
+    switch (pick_tile(d.total_new, 4 * d.hidden, d.hidden)) {
+      case Tile::k128x128: return gemm_qkv_t<T, 128, 128, 2, 2, 4>(d, x, w1t, k_pool, v_pool, ws, st);
+      case Tile::k64x128: return gemm_qkv_t<T, 64, 128, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st);
+      default: return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st);
+    }
+  }
+}
+
+template <typename T>
+hipError_t out_dispatch(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
+                        const int32_t* status, hipStream_t st) {
+  if constexpr (sizeof(T) == 4) {
+    return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st);   // fp32: one tile shape
+  } else {
+    switch (pick_tile(d.total_new, d.hidden, d.hidden)) {
+      case Tile::k128x128: return gemm_out_t<T, 128, 128, 2, 2, 4>(d, g, w2t, y, status, st);
+      case Tile::k64x128: return gemm_out_t<T, 64, 128, 2, 2, 2>(d, g, w2t, y, status, st);
+      default: return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st);
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1,
-                           const int32_t* new_off, const int32_t* hist, const int32_t* pt,
-                           void* k_pool, void* v_pool, const WsPtrs& ws, hipStream_t stream) {
-  if (d.dtype == HSTU_BF16) return gemm_qkv_t<bf16>(d, x, w1, new_off, hist, pt, k_pool, v_pool, ws, stream);
-  return gemm_qkv_t<float>(d, x, w1, new_off, hist, pt, k_pool, v_pool, ws, stream);
+hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
+                           void* v_pool, const WsPtrs& ws, hipStream_t stream) {
+  return d.dtype == HSTU_BF16 ? qkv_dispatch<bf16>(d, x, w1t, k_pool, v_pool, ws, stream)
+                              : qkv_dispatch<float>(d, x, w1t, k_pool, v_pool, ws, stream);
 }
 
-hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2, void* y,
+hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
                            const int32_t* status, hipStream_t stream) {
-  if (d.dtype == HSTU_BF16) return gemm_out_t<bf16>(d, g, w2, y, status, stream);
-  return gemm_out_t<float>(d, g, w2, y, status, stream);
+  return d.dtype == HSTU_BF16 ? out_dispatch<bf16>(d, g, w2t, y, status, stream)
+                              : out_dispatch<float>(d, g, w2t, y, status, stream);
 }
 
 }  // namespace hstu

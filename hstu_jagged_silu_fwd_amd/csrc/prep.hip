@@ -1,6 +1,8 @@
 // Index prep for one layer call: validates the jagged/paged metadata, maps
-// rows to users, and builds the attention work list.  One workgroup; all
-// per-user and per-q-block metadata is kept in LDS while it is built.
+// rows to users and pool slots, and builds the attention work list.
+// Workgroup 0 does the validation and the work list, keeping all per-user
+// and per-q-block metadata in LDS while it is built; workgroups 1.. each map
+// a slice of kRowsPerWg new rows to (user, page, slot).
 //
 // Work decomposition: the new rows of user u are cut into q-blocks of kQB
 // rows; q-block qb sees keys [0, hist + min(n, (qb+1)*kQB)) (causal).  The key
@@ -20,6 +22,8 @@ namespace {
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepWaves = kPrepThreads / kWave;
 constexpr int kMinChunk = 64;
+constexpr int kRowsPerThread = 4;
+constexpr int kRowsPerWg = kPrepThreads * kRowsPerThread;
 
 struct PrepArgs {
   const int32_t* new_off;
@@ -100,6 +104,33 @@ __device__ __forceinline__ int entry_user(const int32_t* qbb, int B, int e) {
   return lo;
 }
 
+// Rows -> user, and the pool (page, slot) their K/V go to.  Positions whose
+// page-table entry would fall outside the table (only possible with metadata
+// that workgroup 0 rejects) get page -1.
+__device__ void map_rows(const PrepArgs& a, const PrepShared& s, int slice) {
+  const int r0 = slice * kRowsPerWg + threadIdx.x;
+  int user[kRowsPerThread], pos[kRowsPerThread], pg[kRowsPerThread];
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int r = r0 + i * kPrepThreads;
+    user[i] = r < a.T ? row_to_user(s.off, a.B, r) : 0;
+    pos[i] = r < a.T ? s.hist[user[i]] + (r - s.off[user[i]]) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const bool ok = pos[i] >= 0 && pos[i] / a.ps < a.maxP;
+    pg[i] = ok ? a.pt[static_cast<size_t>(user[i]) * a.maxP + pos[i] / a.ps] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int r = r0 + i * kPrepThreads;
+    if (r < a.T) {
+      a.ws.row_user[r] = user[i];
+      a.ws.row_loc[r] = make_int2(pg[i], pos[i] >= 0 ? pos[i] % a.ps : 0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   __shared__ PrepShared s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -110,6 +141,10 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   for (int u = tid; u <= B; u += kPrepThreads) s.off[u] = a.new_off[u];
   for (int u = tid; u < B; u += kPrepThreads) s.hist[u] = a.hist[u];
   __syncthreads();
+  if (blockIdx.x > 0) {
+    if (B > 0) map_rows(a, s, blockIdx.x - 1);   // B == 0 with rows is rejected below
+    return;
+  }
 
   // 1. metadata checks
   if (tid == 0 && B == 0 && a.T != 0) set_err(s, HSTU_DEV_BAD_OFFSETS);
@@ -222,9 +257,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   }
   for (int u = tid; u <= B; u += kPrepThreads) a.ws.qb_base[u] = s.qbb[u];
 
-  // 6. row -> user
-  for (int r = tid; r < a.T; r += kPrepThreads) a.ws.row_user[r] = row_to_user(s.off, B, r);
-
   if (tid == 0) {
     hdr->status = 0;
     hdr->n_items = static_cast<int32_t>(n_items);
@@ -253,7 +285,7 @@ hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const i
   a.nqb_cap = nqb_cap;
   a.item_cap = item_cap;
   a.target_items = target_items;
-  prep_kernel<<<1, kPrepThreads, 0, stream>>>(a);
+  prep_kernel<<<1 + (d.total_new + kRowsPerWg - 1) / kRowsPerWg, kPrepThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

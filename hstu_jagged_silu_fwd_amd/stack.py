@@ -49,9 +49,11 @@ class HSTUStack:
         t = torch.as_tensor(a)
         return t.to(device=self.device, dtype=dtype).contiguous()
 
-    def set_layer(self, l: int, *, w1, w2, pos_bias, page_table, ts_bias=None) -> None:
+    def set_layer(self, l: int, *, w1t, w2t, pos_bias, page_table, ts_bias=None) -> None:
+        """Layer l's parameters; w1t [4D, D] and w2t [D, D] are the projection
+        weights in out-features x in-features layout (W1 and W2 transposed)."""
         self.layers[l] = dict(
-            w1=self._dev(w1, self.tdtype), w2=self._dev(w2, self.tdtype),
+            w1t=self._dev(w1t, self.tdtype), w2t=self._dev(w2t, self.tdtype),
             pos_bias=self._dev(pos_bias, torch.float32),
             ts_bias=None if ts_bias is None else self._dev(ts_bias, torch.float32),
             page_table=self._dev(page_table, torch.int32))
@@ -79,7 +81,7 @@ class HSTUStack:
         ws = self.workspace(T) if workspace is None else workspace
         L = self.layers[l]
         _lib.layer_fwd(self.desc(T), x, new_offsets, hist_len, L["page_table"], self.k_pool,
-                       self.v_pool, L["w1"], L["w2"], L["pos_bias"], y, ws,
+                       self.v_pool, L["w1t"], L["w2t"], L["pos_bias"], y, ws,
                        ts_bias=L["ts_bias"], timestamps=timestamps, ts_offsets=ts_offsets,
                        stream=stream, stage_events=stage_events)
 

@@ -121,8 +121,11 @@ hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes
  *                                 for positions [0, hist_len+n) must be valid
  *   k_pool, v_pool                pools (layout above); the new rows' K and V
  *                                 are written at positions hist_len[u] + t
- *   w1           [D, 4D] dtype    columns: U | V | Q | K blocks
- *   w2           [D, D]  dtype
+ *   w1t          [4D, D] dtype    W1 transposed (out-features x in-features,
+ *                                 the usual linear-layer weight layout): row j
+ *                                 holds the weights of output column j, rows
+ *                                 in U | V | Q | K block order
+ *   w2t          [D, D]  dtype    W2 transposed, same convention
  *   pos_bias     [pos_buckets] float32
  *   ts_bias      [ts_buckets]  float32, or NULL when ts_buckets == 0
  *   timestamps   int64, jagged over every position (history then new) of each
@@ -136,7 +139,7 @@ hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes
 hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x,
                            const int32_t* new_offsets, const int32_t* hist_len,
                            const int32_t* page_table, void* k_pool, void* v_pool,
-                           const void* w1, const void* w2, const float* pos_bias,
+                           const void* w1t, const void* w2t, const float* pos_bias,
                            const float* ts_bias, const int64_t* timestamps,
                            const int32_t* ts_offsets, void* y, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
@@ -156,7 +159,7 @@ typedef enum {
 hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x,
                                  const int32_t* new_offsets, const int32_t* hist_len,
                                  const int32_t* page_table, void* k_pool, void* v_pool,
-                                 const void* w1, const void* w2, const float* pos_bias,
+                                 const void* w1t, const void* w2t, const float* pos_bias,
                                  const float* ts_bias, const int64_t* timestamps,
                                  const int32_t* ts_offsets, void* y, void* workspace,
                                  size_t workspace_bytes, void* hip_stream,

@@ -45,7 +45,7 @@ def stack_from_workload(wl, num_layers=None, pool_fill=None, layers=None):
     zeros = np.zeros(wl.B, dtype=np.int32)
     for j, l in enumerate(idx):
         li = wl.layer(l)
-        st.set_layer(j, w1=li.w1, w2=li.w2, pos_bias=li.pos_bias, page_table=li.page_table,
+        st.set_layer(j, w1t=li.w1t, w2t=li.w2t, pos_bias=li.pos_bias, page_table=li.page_table,
                      ts_bias=li.ts_bias)
         if int(hoff[-1]) > 0:
             k = np.concatenate(li.hist_k, axis=0)

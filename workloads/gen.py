@@ -107,6 +107,16 @@ class LayerInputs:
     hist_v: List[np.ndarray]       # per user [hist_len[u], D]
     page_table: np.ndarray         # [B, max_pages] int32, -1 = unused
 
+    @property
+    def w1t(self) -> np.ndarray:
+        """W1 in out-features x in-features layout, [4D, D]."""
+        return np.ascontiguousarray(self.w1.T)
+
+    @property
+    def w2t(self) -> np.ndarray:
+        """W2 in out-features x in-features layout, [D, D]."""
+        return np.ascontiguousarray(self.w2.T)
+
 
 @dataclasses.dataclass
 class Workload:

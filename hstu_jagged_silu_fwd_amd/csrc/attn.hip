@@ -5,26 +5,31 @@
 // article 100093, "HSTU sequential modelling": SiLU weighting instead of
 // softmax plus a relative attention bias).
 //
-// One work item = (user, q-block of up to kQB = 64 new rows, head, key chunk).
-// The q-block's rows form up to 4 groups of 16 queries, taken two at a time
-// by "query sets".  The 4 waves of a workgroup cover QS query sets x KS key
-// splits (QS = 2, KS = 2, or QS = 1, KS = 4 when the q-block has at most two
-// groups): wave w owns query set w / KS and walks the chunk's 32-key steps
-// w % KS, w % KS + KS, ...  A wave streams its own K and V^T fragments from
-// the pool pages into registers one step ahead of use, so the key loop has no
-// barriers, and each fragment feeds both of the wave's query groups.  Per
-// step and group:
-//   S^T[32 keys x 16 queries] = K * Q^T     (2 MFMA blocks; accumulators are
-//                                           seeded with the bias)
-//   A = SiLU(S) on the fp32 scores; masked only on diagonal tiles
+// One work item = (user, q-block of up to kQB = 256 new rows, head, key
+// chunk): a q-block covers all new rows of most users, so each history key is
+// read once per head and chunk.  A workgroup of eight waves takes one item at
+// a time; wave w owns the q-block's query groups w and w + 8 (16 rows each;
+// interleaved so partial blocks spread evenly) and sits out the products of
+// groups the block does not have.  The chunk's keys are walked in 32-key
+// steps.  A step's K rows [32][d] and V^T rows [d][32] are copied from their
+// pool pages into a ring of NST LDS stages with direct-to-LDS loads that the
+// waves share out; the ring runs NST-1 steps ahead of the step being
+// multiplied and one barrier per step hands a stage from the loads to the
+// products and back.
+// Per step and wave:
+//   S^T[32 keys x 16 queries] = K * Q^T     (2 MFMA blocks over d; the
+//                                           accumulators start at the bias)
+//   A = SiLU(S) on the fp32 scores; masked only on diagonal steps
 //   O^T[d x 16]             += V^T * A
-// The S^T accumulator of lane l holds 8 consecutive keys of one query, which
-// is exactly the B-operand fragment of the second product, so scores never
-// leave registers (K rows fed to S^T block b are permuted, row m -> key
-// 8*(m/4) + 4*b + m%4, to make that true).  After the key loop the KS waves
-// of a query set add their partial O through LDS (a two-round tree) and the
-// first of them writes the item's output rows.  Queries are staged in LDS
-// once per item and read back per step.
+// K rows feeding S^T block b are read in the permuted order row m -> key
+// 8*(m/4) + 4*b + m%4, so the S^T accumulator of a lane holds 8 consecutive
+// keys of one query, which is exactly its B-operand fragment for the second
+// product: scores never leave registers.  Each K and V^T fragment read from
+// LDS feeds both of a wave's groups.  The query fragments stay in registers
+// for the whole item, and each wave writes its own groups' partial output
+// rows (no cross-wave reduction).  In LDS the 16-byte chunks of every row are
+// XOR-permuted so that the fragment reads of 16 lanes (16 rows, one chunk
+// each) fall into distinct banks.
 //
 // Exponent domain: the projection stores Q' = -log2(e) * Q, and the bias
 // tables here are scaled the same way, so S' = -log2(e) * s and
@@ -36,11 +41,13 @@
 // below kLut; a step whose distances all lie at or beyond kLut and span no
 // more than one bucket width (2^(11-m) there) touches at most two buckets and
 // takes a compare/select between two values; any other step takes the
-// generic per-element bucket path.
+// generic per-element bucket path.  Timestamps, when present, travel with
+// their keys through the ring; each lane keeps its query's in a register.
+//
 // Partial outputs (fp32) go to the workspace; the chunks of a row are added
 // by the norm kernel (no softmax, so partial sums over key ranges simply
-// add).  Work items are fetched dynamically by a persistent grid (two
-// workgroups per CU), one item ahead.
+// add).  The grid is persistent, one workgroup per CU: workgroup i takes
+// item i first and then fetches further items dynamically, one ahead.
 #include <type_traits>
 
 #include "common.h"
@@ -49,8 +56,8 @@ namespace hstu {
 namespace {
 
 constexpr int kLut = 2048;
+constexpr int kStepKeys = 32;
 constexpr int kMaxChunkPages = kMaxChunkKeys / 16 + 1;
-constexpr int kGroupsPerWave = 4;   // 16-query groups held by one wave
 constexpr float kNegLog2e = -1.4426950408889634f;
 
 template <typename T>
@@ -77,218 +84,268 @@ __device__ __forceinline__ int bucket_start(int b, int m) {
   return (s + r) << (q - 1);
 }
 
-template <typename T, int NC, int NO>
-struct StepBuf {
-  Frag<T> kf[2][NC];
-  Frag<T> vf[NO];
+constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kGpw = 2;            // 16-query groups per wave
+static_assert(kQB == 16 * kWaves * kGpw, "a q-block is one group per wave slot");
+
+// Sizes of one ring stage (one 32-key step of K and V^T) for element type T
+// and head dim HD.
+template <typename T, int HD>
+struct StepGeo {
+  static constexpr int ES = static_cast<int>(sizeof(T));
+  static constexpr int CE = 16 / ES;                   // elements per 16-byte chunk
+  static constexpr int KCH = HD / CE;                  // chunks per K row
+  static constexpr int VCH = kStepKeys / CE;           // chunks per V^T row
+  static constexpr int KBYTES = kStepKeys * HD * ES;   // the K rows of a step
+  static constexpr int STAGE = 2 * KBYTES;             // K rows, then V^T rows
+  static constexpr int NBLK = STAGE / 1024;            // 1 KiB loads per stage
+  static constexpr int IPW = (NBLK + kWaves - 1) / kWaves;   // loads per wave (at most)
+  static constexpr int NST_FIT = 49152 / STAGE;        // stages in 48 KiB
+  static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 6 ? 6 : NST_FIT);
+  // chunk permutation of K row `key`: (m >> KSH) with m = (key & 3) | (((key >> 3) & 3) << 2),
+  // m being the lane (mod 16) that reads the row; V^T row e: (e >> VSH) & (VCH - 1)
+  static constexpr int KSH = KCH >= 16 ? 0 : (KCH == 8 ? 1 : 2);
+  static constexpr int VSH = VCH == 4 ? 2 : 1;
+  static_assert(KCH >= 4 && (VCH == 4 || VCH == 8), "supported geometry");
+  static_assert(NBLK * 1024 == STAGE, "whole loads per stage");
+  static_assert((kStepKeys * KCH) % 64 == 0, "a load never straddles K and V^T");
+  static_assert((IPW + 1) * (NST - 2) <= 23, "wait count range");
 };
 
-template <typename T, int HD, int GPW>
-__global__ __launch_bounds__(256, GPW == 2 ? 2 : 1) void attn_kernel(AttnArgs<T> a) {
+template <typename T, int HD>
+__global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
+  using G = StepGeo<T, HD>;
+  constexpr int CE = G::CE, KCH = G::KCH, VCH = G::VCH, NST = G::NST, IPW = G::IPW;
+  constexpr int NT = 64 * kWaves;
   constexpr int NC = HD / 32;        // 32-wide slices of the head dim (contraction of S^T)
   constexpr int NO = HD / 16;        // 16-row blocks of O^T
-  constexpr int RCH = HD / 4;        // float4 chunks per output row
-  constexpr int ES = static_cast<int>(sizeof(T));
-  constexpr int QCH = HD * ES / 16;  // 16-byte chunks per query row
-  constexpr int FCH = 8 * ES / 16;   // chunks per 8-element fragment
-  constexpr int SET_ROWS = 16 * GPW; // query rows of a query set (GPW groups)
-  // The item's query tile (during the key loop) and the reduction buffers
-  // (after it) share one LDS region: two slots of one query set's partial O.
-  constexpr int RED_FLOATS = 2 * SET_ROWS * HD;
-  constexpr int Q_FLOATS = kQB * HD * ES / 4;
-  __shared__ __attribute__((aligned(16))) float s_big[RED_FLOATS > Q_FLOATS ? RED_FLOATS : Q_FLOATS];
-  float* const s_red = s_big;
-  T* const s_q = reinterpret_cast<T*>(s_big);
+  __shared__ __attribute__((aligned(1024))) unsigned char s_ring[NST * G::STAGE];
+  __shared__ __attribute__((aligned(256))) int64_t s_ts[NST][kStepKeys];
   __shared__ float s_lut[kLut];
   __shared__ float s_pb[kMaxBuckets];
   __shared__ float s_tb[kMaxBuckets];
   __shared__ int s_pages[kMaxChunkPages];
   __shared__ int s_next;
-  if (a.hdr->status != 0) return;
+
+  // status and item count in one load; the bias tables are loaded alongside
+  const int4 hv = *reinterpret_cast<const int4*>(a.hdr);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  for (int i = tid; i < a.nb; i += 256) s_pb[i] = kNegLog2e * a.pos_bias[i];
-  for (int i = tid; i < a.ntsb; i += 256) s_tb[i] = kNegLog2e * a.ts_bias[i];
-  if (tid == 0) s_next = atomicAdd(&a.hdr->counter, 1);
+  for (int i = tid; i < a.nb; i += NT) s_pb[i] = kNegLog2e * a.pos_bias[i];
+  for (int i = tid; i < a.ntsb; i += NT) s_tb[i] = kNegLog2e * a.ts_bias[i];
+  if (hv.x != 0) return;                   // status: prep rejected the call
+  const int n_items = hv.y;
+  if (tid == 0) s_next = blockIdx.x;       // first item: static
   __syncthreads();
-  for (int i = tid; i < kLut; i += 256) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];
-  const int n_items = a.hdr->n_items;
+  for (int i = tid; i < kLut; i += NT) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];
   const int ps = 1 << a.ps_shift;
   const bool has_ts = a.ntsb > 0;
-  const size_t page_elems = static_cast<size_t>(a.H) * ps * HD;
+  const int g = lane >> 4, l16 = lane & 15;
+  // K row read by this lane for S^T block b is krow0 + 4*b; both rows share
+  // one chunk permutation.  V^T rows 16*ob + l16 share one too.
+  const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
+  const int ksw = l16 >> G::KSH;
+  const int vsw = (l16 >> G::VSH) & (VCH - 1);
+  // loads this wave issues per stage (its K/V^T blocks, plus the key
+  // timestamps for wave 0), and the count to wait for NST-2 stages of them
+  const int my_blk = min(max(G::NBLK - w * IPW, 0), IPW);
+  const int my_wait = (my_blk + ((has_ts && w == 0) ? 1 : 0)) * (NST - 2);
+  // Source of this lane's 16 bytes in load j, relative to the step's page
+  // base: element offset lo[j] inside the (page, head) block, and whether it
+  // lies in the step's second page (16-token pages only: a 32-key step then
+  // spans two pages).
+  uint32_t lo[IPW];
+  bool hi[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int q = (w * IPW + j) * 64 + lane;             // 16-byte chunk of the stage
+    if (q < kStepKeys * KCH) {                           // K row `row`, chunk position p
+      const int row = q / KCH, p = q % KCH;
+      const int m = (row & 3) | (((row >> 3) & 3) << 2);
+      const int cch = p ^ (m >> G::KSH);
+      hi[j] = row >= ps;
+      lo[j] = static_cast<uint32_t>((row & (ps - 1)) * HD + cch * CE);
+    } else {                                             // V^T row e, chunk position p
+      const int qv = q - kStepKeys * KCH;
+      const int e = qv / VCH, p = qv % VCH;
+      const int key = (p ^ ((e >> G::VSH) & (VCH - 1))) * CE;
+      hi[j] = key >= ps;
+      lo[j] = static_cast<uint32_t>(e * ps + (key & (ps - 1)));
+    }
+  }
 
   for (;;) {
-    __syncthreads();                       // previous item fully consumed; s_next published
+    __syncthreads();                       // previous item consumed; s_next published
     const int it = s_next;
     if (it >= n_items) break;
     const AttnItem item = a.items[it];
-    // Per-lane values are re-derived from an opaque copy of the lane id in
-    // every item so the compiler does not keep dozens of lane-dependent
-    // addresses alive across the whole kernel.
-    int tid_i = tid;
-    asm volatile("" : "+v"(tid_i));
-    const int lane_i = tid_i & 63;
-    const int g = lane_i >> 4, l16 = lane_i & 15;
-    const int koff0 = 8 * (l16 >> 2) + (l16 & 3);   // K row of S^T block b is koff0 + 4*b
-    const int voff = 8 * g;                          // this lane's first key in a step
     const int u = item.a.x, q0 = item.a.y, h = item.a.z, k_lo = item.a.w;
     const int k_hi = item.b.x, off_u = item.b.y, n = item.b.z, c = item.b.w;
     const int len = c + n;
     const int nq = min(kQB, n - q0);
     const int ngroups = (nq + 15) >> 4;
-    // page ids of the chunk, staged once per item; fetch the next item index
     const int32_t* ptu = a.pt + static_cast<size_t>(u) * a.maxP;
     const int pg0 = k_lo >> a.ps_shift;
-    const int kst_end = min(k_hi, len);               // keys with a staged page
+    const int kst_end = min(k_hi, len);                // keys whose pages are staged
     const int npg = ((kst_end - 1) >> a.ps_shift) - pg0 + 1;
-    for (int i = tid_i; i < npg; i += 256) s_pages[i] = ptu[pg0 + i];
-    // query tile [kQB rows][HD], 16-byte chunks XOR-swizzled by row
-    for (int q = tid_i; q < kQB * QCH; q += 256) {
-      const int row = q / QCH, ch = q % QCH;
-      const int t = min(q0 + row, n - 1);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(a.q + static_cast<size_t>(off_u + t) * a.D + h * HD + ch * (16 / ES));
-      const int sw = ((row & 15) * FCH) & (QCH - 1);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s_q) + row * HD * ES + ((ch ^ sw) * 16)) = v;
-    }
-    __syncthreads();                       // all threads have read s_next; pages and queries staged
-    if (tid == 0) s_next = atomicAdd(&a.hdr->counter, 1);
-
-    // keys up to the q-block's last query position, in 32-key steps
-    const int kend = min(k_hi, c + q0 + nq);
-    const int nsteps = (kend - k_lo + 31) >> 5;
-
-    // query sets x key splits of this item (see the top of the file)
-    const int QS = ngroups > GPW ? 2 : 1;
-    const int KS = 4 / QS;
-    const int qs = w / KS, ks = w % KS;
-    const int gb = GPW * qs;                           // first group of this wave's query set
-    const int wg = min(GPW, ngroups - gb);             // its groups: 1..GPW
-
-    f32x4 o[GPW][NO];
+    for (int i = tid; i < npg; i += NT) s_pages[i] = ptu[pg0 + i];
+    // this wave's query groups w and w + kWaves: fragments and timestamps
+    const int ng_w = (ngroups > w) + (ngroups > w + kWaves);   // 0, 1 or 2
+    Frag<T> qf[kGpw][NC];
+    int64_t tq[kGpw];
+    const int64_t* tsu = has_ts ? a.ts + a.ts_off[u] : nullptr;
 #pragma unroll
-    for (int i = 0; i < GPW; ++i)
+    for (int i = 0; i < kGpw; ++i) {
+      const int qrow = min(q0 + 16 * (w + kWaves * i) + l16, n - 1);
+      const T* qp = a.q + static_cast<size_t>(off_u + qrow) * a.D + h * HD + 8 * g;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) load_frag(qf[i][cc], qp + cc * 32);
+      tq[i] = has_ts ? tsu[c + qrow] : 0;
+    }
+    const int kend = min(k_hi, c + q0 + nq);           // keys up to the block's last query
+    const int nsteps = (kend - k_lo + kStepKeys - 1) / kStepKeys;
+    // Let the query loads land before the ring starts: the compiler cannot
+    // count outstanding loads across the key loop, so it would otherwise
+    // wait for every in-flight stage at the first use of a query fragment.
+    wait_vm<0>();
+    __syncthreads();                       // pages staged; everyone has read s_next
+    if (tid == 0) s_next = static_cast<int>(gridDim.x) + atomicAdd(&a.hdr->counter, 1);
+
+    // ---- loads of step s into stage s % NST ----
+    const size_t kv_head = static_cast<size_t>(h) * ps * HD;      // head block inside a page
+    const size_t page_elems = static_cast<size_t>(a.H) * ps * HD;
+    // Keys past the staged range (last step only) read rows of the step's
+    // own pages: in bounds, and masked (K) or zeroed (V) by the products.
+    // Page ids of step s (the second one only differs with 16-token pages);
+    // read one step ahead of their use so the LDS latency hides behind a
+    // step's products.
+    auto pages_of = [&](int s) __attribute__((always_inline)) {
+      const int kb = k_lo + kStepKeys * min(s, nsteps - 1);
+      const int pa = s_pages[(kb >> a.ps_shift) - pg0];
+      const int pb = (ps < kStepKeys && kb + ps < kst_end) ? s_pages[((kb + ps) >> a.ps_shift) - pg0] : pa;
+      return make_int2(pa, pb);
+    };
+    auto issue = [&](int s, int2 pgs) __attribute__((always_inline)) {
+      const int kb = k_lo + kStepKeys * s;
+      unsigned char* stg = s_ring + (s % NST) * G::STAGE;
+      const int pa = __builtin_amdgcn_readfirstlane(pgs.x);
+      const int pb = __builtin_amdgcn_readfirstlane(pgs.y);
+      const size_t in_page = static_cast<size_t>(kb & (ps - 1));   // 0 for 16-token pages
+      const size_t ha = static_cast<size_t>(pa) * page_elems + kv_head;
+      const size_t hb = static_cast<size_t>(pb) * page_elems + kv_head;
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int blk = w * IPW + j;                   // 1 KiB block of the stage
+        if (blk >= G::NBLK) break;                     // uniform
+        const T* src;
+        if (blk * 64 < kStepKeys * KCH)                // K rows
+          src = a.k_pool + (hi[j] ? hb : ha) + in_page * HD + lo[j];
+        else                                           // V^T rows
+          src = a.v_pool + (hi[j] ? hb : ha) + in_page + lo[j];
+        dma_lds16(src, stg + blk * 1024);
+      }
+      if (has_ts && w == 0) {                          // the step's key timestamps
+        const int key = min(kb + (lane >> 1), len - 1);
+        const int32_t* tsrc = reinterpret_cast<const int32_t*>(tsu + key) + (lane & 1);
+        dma_lds4(tsrc, &s_ts[s % NST][0]);
+      }
+    };
+
+    f32x4 o[kGpw][NO];
+#pragma unroll
+    for (int i = 0; i < kGpw; ++i)
 #pragma unroll
       for (int ob = 0; ob < NO; ++ob) o[i][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // B-operand fragment of query group i, head-dim slice cc, from the LDS tile
-    // (row & 15) == l16 for every group, so the swizzle is per lane only.
-    const int q_sw = (l16 * FCH) & (QCH - 1);
-    auto qfrag = [&](int qlane, int i, int cc, Frag<T>& f) __attribute__((always_inline)) {
-      const int ch = (cc * 32 + g * 8) * ES / 16;
-      load_frag(f, reinterpret_cast<const T*>(reinterpret_cast<const char*>(s_q) + qlane +
-                                              (16 * i) * HD * ES + ((ch ^ q_sw) * 16)));
-    };
-    const size_t head_off = static_cast<size_t>(h) * ps * HD;
-    const int64_t* tsu = has_ts ? a.ts + a.ts_off[u] : nullptr;
 
-    // Per-lane element offsets inside a (page, head) block; together with a
-    // wave-uniform page base they address every fragment of a step.
-    // (A 32-key step lies in one page when page_size >= 32; with 16-token
-    // pages its second half lives in the next page of the table.)
-    const uint32_t k_lane0 = static_cast<uint32_t>(((koff0) & (ps - 1)) * HD + g * 8);
-    const uint32_t k_lane1 = static_cast<uint32_t>(((koff0 + 4) & (ps - 1)) * HD + g * 8);
-    const uint32_t v_lane = static_cast<uint32_t>(l16 * ps + (voff & (ps - 1)));
-    const bool k_hi_half = koff0 >= 16;               // only matters for 16-token pages
-    const bool v_hi_half = voff >= 16;
-
-    // Loads the fragments of step s (steps past the end are clamped, so every
-    // path issues the same load sequence).
-    auto load_step = [&](int s, StepBuf<T, NC, NO>& sb) __attribute__((always_inline)) {
-      const int kb = k_lo + 32 * min(s, nsteps - 1);
-      const int pa = __builtin_amdgcn_readfirstlane(s_pages[(kb >> a.ps_shift) - pg0]);
-      const int pb = (kb + 16 < kst_end) ? __builtin_amdgcn_readfirstlane(s_pages[((kb + 16) >> a.ps_shift) - pg0]) : pa;
-      const size_t in_page = static_cast<size_t>(kb & (ps - 1));   // 0 for 16-token pages
-      const T* ka = a.k_pool + static_cast<size_t>(pa) * page_elems + head_off + in_page * HD;
-      const T* kz = a.k_pool + static_cast<size_t>(pb) * page_elems + head_off + in_page * HD;
-      const T* va = a.v_pool + static_cast<size_t>(pa) * page_elems + head_off + in_page;
-      const T* vz = a.v_pool + static_cast<size_t>(pb) * page_elems + head_off + in_page;
-      const T* k0 = (ps >= 32 || !k_hi_half) ? ka : kz;
-      const T* vb = (ps >= 32 || !v_hi_half) ? va : vz;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        load_frag(sb.kf[0][cc], k0 + k_lane0 + cc * 32);
-        load_frag(sb.kf[1][cc], k0 + k_lane1 + cc * 32);
-      }
-#pragma unroll
-      for (int ob = 0; ob < NO; ++ob) load_frag(sb.vf[ob], vb + v_lane + static_cast<uint32_t>(ob * 16 * ps));
-    };
-
-    // One 32-key step for the wave's local groups [I0, I0 + NG), as
-    // straight-line code per bias case so that the S^T products, the SiLU of
-    // one group and the O^T products of another can overlap.
-    auto block = [&](auto i0c, auto ngc, int kb, StepBuf<T, NC, NO>& sb) __attribute__((always_inline)) {
-      constexpr int I0 = decltype(i0c)::value;
+    // ---- products of step s for this wave's first NG query groups ----
+    auto compute = [&](auto ngc, auto tailc, int s) __attribute__((always_inline)) {
       constexpr int NG = decltype(ngc)::value;
-      // distance of element (local group I0 + i, block b, row r) is dl0 + 16*i - 4*b - r
-      const int pset = c + q0 + 16 * (gb + I0);       // first query position of the block
-      const int dl0 = pset + l16 - (kb + voff);
-      const int dmin = pset - (kb + 31);
-      const int dmax = pset + 16 * NG - 1 - kb;
+      constexpr bool kTail = decltype(tailc)::value;   // the step reaches past the staged keys
+      const int kb = k_lo + kStepKeys * s;
+      const unsigned char* stg = s_ring + (s % NST) * G::STAGE;
       f32x4 st[NG][2];
-      if (dmax < kLut) {
-        if (dmin >= 0) {
+      int dl0[NG], dmn[NG];
 #pragma unroll
-          for (int i = 0; i < NG; ++i)
+      for (int i = 0; i < NG; ++i) {
+        // distance of element (block b, row r) is dl0 - 4*b - r
+        const int pq = c + q0 + 16 * (w + kWaves * i);   // first query position of the group
+        dl0[i] = pq + l16 - (kb + 8 * g);
+        const int dmin = pq - (kb + kStepKeys - 1);
+        const int dmax = pq + 15 - kb;
+        dmn[i] = dmin;
+        if (dmax < kLut) {
+          if (dmin >= 0) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) st[i][b][r] = s_lut[dl0 + 16 * i - 4 * b - r];
+              for (int r = 0; r < 4; ++r) st[i][b][r] = s_lut[dl0[i] - 4 * b - r];
+          } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) st[i][b][r] = s_lut[max(dl0[i] - 4 * b - r, 0)];
+          }
+        } else if (dmin >= kLut && (kLut >> a.mbits) >= dmax - dmin + 1) {
+          // every distance here falls into one or two adjacent buckets
+          const int blo = bucket32(dmin, a.mbits, a.nb), bhi = bucket32(dmax, a.mbits, a.nb);
+          const float vlo = s_pb[blo], vhi = s_pb[bhi];
+          const int bnd = blo == bhi ? 0x7fffffff : bucket_start(bhi, a.mbits);
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st[i][b][r] = (dl0[i] - 4 * b - r) >= bnd ? vhi : vlo;
         } else {
 #pragma unroll
-          for (int i = 0; i < NG; ++i)
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) st[i][b][r] = s_lut[max(dl0 + 16 * i - 4 * b - r, 0)];
+            for (int r = 0; r < 4; ++r) st[i][b][r] = s_pb[bucket32(dl0[i] - 4 * b - r, a.mbits, a.nb)];
         }
-      } else if (dmin >= kLut && (kLut >> a.mbits) >= dmax - dmin + 1) {
-        // every distance here falls into one or two adjacent buckets
-        const int blo = bucket32(dmin, a.mbits, a.nb), bhi = bucket32(dmax, a.mbits, a.nb);
-        const float vlo = s_pb[blo], vhi = s_pb[bhi];
-        const int bnd = blo == bhi ? 0x7fffffff : bucket_start(bhi, a.mbits);
-#pragma unroll
-        for (int i = 0; i < NG; ++i)
+        if (has_ts) {
+          const int64_t* tk = &s_ts[s % NST][8 * g];
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[i][b][r] = (dl0 + 16 * i - 4 * b - r) >= bnd ? vhi : vlo;
-      } else {
-#pragma unroll
-        for (int i = 0; i < NG; ++i)
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st[i][b][r] = s_pb[bucket32(dl0 + 16 * i - 4 * b - r, a.mbits, a.nb)];
+            for (int r = 0; r < 4; ++r) st[i][b][r] += s_tb[bucket64(tq[i] - tk[4 * b + r], a.tsmbits, a.ntsb)];
+        }
       }
-      if (has_ts) {
+      // S^T = K * Q^T over the head dim; each K fragment feeds every group
+      const unsigned char* k0p = stg + krow0 * (KCH * 16);
+      const unsigned char* k1p = k0p + 4 * (KCH * 16);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const int chunk = (cc * 32 + 8 * g) / CE;
+        Frag<T> kf0, kf1;
+        read_frag(kf0, k0p, chunk, ksw);
+        read_frag(kf1, k1p, chunk, ksw);
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
-          const int64_t tp = tsu[min(pset + 16 * i + l16, len - 1)];
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = min(kb + voff + 4 * b + r, len - 1);
-              st[i][b][r] += s_tb[bucket64(tp - tsu[key], a.tsmbits, a.ntsb)];
-            }
+          st[i][0] = mma16(kf0, qf[i][cc], st[i][0]);
+          st[i][1] = mma16(kf1, qf[i][cc], st[i][1]);
         }
       }
-      // The query tile is read from LDS at every step (an opaque offset keeps
-      // the compiler from hoisting all query fragments into registers).
-      int qlane = l16 * HD * ES;
-      asm volatile("" : "+v"(qlane));
+      // V^T fragments are read now so that their LDS latency overlaps the
+      // SiLU below.  V of keys past the staged range (only in the last step,
+      // where A is masked anyway) is zeroed so stale pool memory cannot
+      // turn into NaN.
+      Frag<T> vf[NO];
+      {
+        const unsigned char* vp = stg + G::KBYTES + l16 * (VCH * 16);
+        const int vchunk = (8 * g) / CE;
 #pragma unroll
-      for (int i = 0; i < NG; ++i)
+        for (int ob = 0; ob < NO; ++ob) read_frag(vf[ob], vp + ob * 16 * (VCH * 16), vchunk, vsw);
+        if constexpr (kTail) {
+          const int nvalid = kst_end - (kb + 8 * g);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          Frag<T> qf;
-          qfrag(qlane, gb + I0 + i, cc, qf);
+          for (int ob = 0; ob < NO; ++ob)
 #pragma unroll
-          for (int b = 0; b < 2; ++b) st[i][b] = mma16(sb.kf[b][cc], qf, st[i][b]);
+            for (int e = 0; e < 8; ++e)
+              if (e >= nvalid) set_elem(vf[ob], e, 0.0f);
         }
+      }
       Frag<T> af[NG];
-      if (dmin >= 0) {
 #pragma unroll
-        for (int i = 0; i < NG; ++i)
+      for (int i = 0; i < NG; ++i) {
+        if (dmn[i] >= 0) {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -296,111 +353,57 @@ __global__ __launch_bounds__(256, GPW == 2 ? 2 : 1) void attn_kernel(AttnArgs<T>
               const float sv = st[i][b][r];
               set_elem(af[i], 4 * b + r, sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv)));
             }
-      } else {                                       // causal mask on the diagonal
-#pragma unroll
-        for (int i = 0; i < NG; ++i)
+        } else {                                     // causal mask on the diagonal
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float sv = st[i][b][r];
               const float av = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv));
-              set_elem(af[i], 4 * b + r, (dl0 + 16 * i - 4 * b - r) >= 0 ? av : 0.0f);
+              set_elem(af[i], 4 * b + r, (dl0[i] - 4 * b - r) >= 0 ? av : 0.0f);
             }
-      }
-#pragma unroll
-      for (int i = 0; i < NG; ++i)
-#pragma unroll
-        for (int ob = 0; ob < NO; ++ob) o[I0 + i][ob] = mma16(sb.vf[ob], af[i], o[I0 + i][ob]);
-    };
-
-    // One 32-key step for the wave's NG groups, two groups at a time.
-    auto compute = [&](auto ngc, int kb, StepBuf<T, NC, NO>& sb) __attribute__((always_inline)) {
-      constexpr int NG = decltype(ngc)::value;
-      if (kb + 32 > len) {                           // zero V of keys past the sequence
-        const int nvalid = len - (kb + voff);
-#pragma unroll
-        for (int ob = 0; ob < NO; ++ob)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nvalid) set_elem(sb.vf[ob], e, 0.0f);
-      }
-      block(std::integral_constant<int, 0>{}, std::integral_constant<int, (NG < 2 ? NG : 2)>{}, kb, sb);
-      if constexpr (NG > 2)
-        block(std::integral_constant<int, 2>{}, std::integral_constant<int, NG - 2>{}, kb, sb);
-    };
-
-    // The wave walks steps ks, ks + KS, ...; two register buffers alternate
-    // so the next step's fragments are in flight while one is computed.
-    const int my_steps = nsteps > ks ? (nsteps - ks + KS - 1) / KS : 0;
-    auto walk = [&](auto ngc) __attribute__((always_inline)) {
-      StepBuf<T, NC, NO> b0, b1;
-      load_step(ks, b0);
-      for (int j = 0; j < my_steps; j += 2) {
-        load_step(ks + KS * (j + 1), b1);
-        compute(ngc, k_lo + 32 * (ks + KS * j), b0);
-        if (j + 1 >= my_steps) break;
-        load_step(ks + KS * (j + 2), b0);
-        compute(ngc, k_lo + 32 * (ks + KS * (j + 1)), b1);
-      }
-    };
-    if (my_steps > 0) {
-      if constexpr (GPW == 4) {
-        switch (wg) {
-          case 4: walk(std::integral_constant<int, 4>{}); break;
-          case 3: walk(std::integral_constant<int, 3>{}); break;
-          case 2: walk(std::integral_constant<int, 2>{}); break;
-          default: walk(std::integral_constant<int, 1>{}); break;
         }
-      } else {
-        if (wg == 2) walk(std::integral_constant<int, 2>{});
-        else walk(std::integral_constant<int, 1>{});
       }
-    }
+      // O^T += V^T * A
+#pragma unroll
+      for (int ob = 0; ob < NO; ++ob)
+#pragma unroll
+        for (int i = 0; i < NG; ++i) o[i][ob] = mma16(vf[ob], af[i], o[i][ob]);
+    };
 
-    // Add up the KS partial O of each query set through LDS (slot layout:
-    // [32 rows][d], 16-byte chunks XOR-swizzled by row; every lane reads back
-    // exactly the elements it holds), then the set's first wave writes out.
-    __syncthreads();                       // every wave is done with the query tile
-    int lane_r = lane;
-    asm volatile("" : "+v"(lane_r));
-    const int gr = lane_r >> 4, lr = lane_r & 15;
-    auto slot_ptr = [&](int sl, int i, int ob) __attribute__((always_inline)) -> float* {
-      const int row = 16 * i + lr;
-      const int ch = (ob * 4 + gr) ^ (row & (RCH - 1));
-      return s_red + sl * SET_ROWS * HD + row * HD + ch * 4;
-    };
-    auto park = [&](int sl) __attribute__((always_inline)) {
+    // ---- the key loop: one barrier per step (the wave's group count is
+    // fixed for the item, so each count gets a loop of its own) ----
 #pragma unroll
-      for (int i = 0; i < GPW; ++i)
-#pragma unroll
-        for (int ob = 0; ob < NO; ++ob) *reinterpret_cast<f32x4*>(slot_ptr(sl, i, ob)) = o[i][ob];
-    };
-    auto gather = [&](int sl) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < GPW; ++i)
-#pragma unroll
-        for (int ob = 0; ob < NO; ++ob) o[i][ob] += *reinterpret_cast<const f32x4*>(slot_ptr(sl, i, ob));
-    };
-    // round 1: odd splits hand their sums to the even split below them
-    if (ks & 1) park(KS == 2 ? qs : (ks >> 1));
-    __syncthreads();
-    if (!(ks & 1)) gather(KS == 2 ? qs : (ks >> 1));
-    if (KS == 4) {                          // round 2: split 2 hands over to split 0
-      __syncthreads();
-      if (ks == 2) park(0);
-      __syncthreads();
-      if (ks == 0) gather(0);
-    }
-    if (ks == 0) {
-#pragma unroll
-      for (int i = 0; i < GPW; ++i) {
-        const int row = 16 * (gb + i) + lr;             // row inside the q-block
-        if (i < wg && q0 + row < n) {
-          float* dst = a.part + (static_cast<size_t>(it) * kQB + row) * HD + 4 * gr;
-#pragma unroll
-          for (int ob = 0; ob < NO; ++ob) *reinterpret_cast<f32x4*>(dst + ob * 16) = o[i][ob];
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < nsteps) issue(s, pages_of(s));
+    int2 pg_next = pages_of(NST - 1);
+    auto key_loop = [&](auto ngc) __attribute__((always_inline)) {
+      for (int s = 0; s < nsteps; ++s) {
+        if (s + NST - 2 < nsteps) wait_vm_n(my_wait);
+        else wait_vm<0>();
+        bar();                             // stage s visible; stage s-1 no longer read
+        if (s + NST - 1 < nsteps) {
+          issue(s + NST - 1, pg_next);
+          pg_next = pages_of(s + NST);
         }
+        if constexpr (decltype(ngc)::value > 0) {
+          // a branch per step, not per fragment, for the tail zeroing
+          if (k_lo + kStepKeys * (s + 1) > kst_end) compute(ngc, std::true_type{}, s);
+          else compute(ngc, std::false_type{}, s);
+        }
+      }
+    };
+    if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});
+    else if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
+    else key_loop(std::integral_constant<int, 0>{});
+
+#pragma unroll
+    for (int i = 0; i < kGpw; ++i) {
+      const int row = 16 * (w + kWaves * i) + l16;     // row inside the q-block
+      if (i < ng_w && q0 + row < n) {
+        float* dst = a.part + (static_cast<size_t>(it) * kQB + row) * HD + 4 * g;
+#pragma unroll
+        for (int ob = 0; ob < NO; ++ob) *reinterpret_cast<f32x4*>(dst + ob * 16) = o[i][ob];
       }
     }
   }
@@ -430,7 +433,7 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.mbits = d.pos_mbits;
   a.ntsb = d.ts_buckets;
   a.tsmbits = d.ts_mbits;
-  attn_kernel<T, HD, kGroupsPerWave><<<grid, 256, 0, stream>>>(a);
+  attn_kernel<T, HD><<<grid, 64 * kWaves, 0, stream>>>(a);
   return hipGetLastError();
 }
 

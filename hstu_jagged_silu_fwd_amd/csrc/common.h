@@ -14,7 +14,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kQB = 64;          // query rows per attention work item (q-block)
+constexpr int kQB = 256;         // query rows per attention work item (q-block)
 constexpr int kMaxUsers = 4096;  // users per call (metadata is cached in LDS)
 constexpr float kNegLn2 = -0.6931471805599453f;
 constexpr int kMaxBuckets = 1024;
@@ -64,6 +64,19 @@ __device__ __forceinline__ void zero_frag(Frag<float>& f) {
 __device__ __forceinline__ void set_elem(Frag<bf16>& f, int e, float x) { f.v[e] = static_cast<bf16>(x); }
 __device__ __forceinline__ void set_elem(Frag<float>& f, int e, float x) { f.v[e] = x; }
 
+// Fragment read from an LDS row whose 16-byte chunks are XOR-permuted by
+// `sw`: the 8 elements starting at logical chunk `chunk` (bf16: one chunk,
+// fp32: two).
+__device__ __forceinline__ void read_frag(Frag<bf16>& f, const unsigned char* rowp, int chunk, int sw) {
+  f.v = *reinterpret_cast<const bf16x8*>(rowp + ((chunk ^ sw) << 4));
+}
+__device__ __forceinline__ void read_frag(Frag<float>& f, const unsigned char* rowp, int chunk, int sw) {
+  const float4 lo = *reinterpret_cast<const float4*>(rowp + ((chunk ^ sw) << 4));
+  const float4 hi = *reinterpret_cast<const float4*>(rowp + (((chunk + 1) ^ sw) << 4));
+  f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
+  f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
+}
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
@@ -99,6 +112,65 @@ __device__ __forceinline__ int bucket64(int64_t delta, int m, int nb) {
     b = (static_cast<int64_t>(e - m + 1) << m) + static_cast<int64_t>(d >> (e - m)) - (1ll << m);
   }
   return b < nb - 1 ? static_cast<int>(b) : nb - 1;
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads.  __builtin_amdgcn_global_load_lds(src, dst, 16,
+// 0, 0) copies 16 bytes per lane: lane l's bytes land at dst + 16 * l (dst is
+// wave-uniform), so one wave instruction fills 1 KiB of LDS.  They count as
+// vector-memory operations; wait_vm<N>() waits until at most N of this
+// wave's vector-memory operations are outstanding (gfx9 s_waitcnt encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+// bar() is a workgroup barrier without the memory fence of __syncthreads
+// (which would wait for every outstanding load); the empty asm statements
+// keep the compiler from moving memory accesses across it.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// The same copies issued from inline assembly (16 or 4 bytes per lane, to
+// lds_base + size * lane).  The compiler does not see these as LDS writes, so
+// it adds no waits of its own before later LDS reads; the caller orders them
+// with wait_vm and bar.  M0, which holds the LDS base, is restored after
+// the issue (the instruction reads it when issued).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+__device__ __forceinline__ void dma_lds16(const void* src, const void* lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
+}
+__device__ __forceinline__ void dma_lds4(const void* src, const void* lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// wait_vm with a wave-uniform run-time count (0..23).
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define HSTU_WAIT_CASE(k) case k: wait_vm<k>(); break;
+    HSTU_WAIT_CASE(0) HSTU_WAIT_CASE(1) HSTU_WAIT_CASE(2) HSTU_WAIT_CASE(3) HSTU_WAIT_CASE(4)
+    HSTU_WAIT_CASE(5) HSTU_WAIT_CASE(6) HSTU_WAIT_CASE(7) HSTU_WAIT_CASE(8) HSTU_WAIT_CASE(9)
+    HSTU_WAIT_CASE(10) HSTU_WAIT_CASE(11) HSTU_WAIT_CASE(12) HSTU_WAIT_CASE(13) HSTU_WAIT_CASE(14)
+    HSTU_WAIT_CASE(15) HSTU_WAIT_CASE(16) HSTU_WAIT_CASE(17) HSTU_WAIT_CASE(18) HSTU_WAIT_CASE(19)
+    HSTU_WAIT_CASE(20) HSTU_WAIT_CASE(21) HSTU_WAIT_CASE(22) HSTU_WAIT_CASE(23)
+#undef HSTU_WAIT_CASE
+    default: wait_vm<0>(); break;
+  }
+}
+
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -24,9 +24,6 @@
 namespace hstu {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
 constexpr int kRowBytes = 128;   // one k-tile row
 constexpr int kGroupM = 8;
 
@@ -40,25 +37,6 @@ struct QkvEpi {
   int D, H, hd, ps;
 };
 
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
-// left at their maxima so they do not wait).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads (which would
-// wait for every outstanding load); LDS visibility of the direct loads is
-// established by the wait_vm each wave does before it.  The empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void bar() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 __device__ __forceinline__ void tile_of(int id, int Mt, int Nt, int& mt, int& nt) {
   const int nT = Mt * Nt;
   const int x = id & 7, local = id >> 3;
@@ -70,16 +48,6 @@ __device__ __forceinline__ void tile_of(int id, int Mt, int Nt, int& mt, int& nt
   const int r = t - grp * per_group;
   mt = first + r % gsz;
   nt = r / gsz;
-}
-
-__device__ __forceinline__ void read_frag(Frag<bf16>& f, const unsigned char* rowp, int chunk, int sw) {
-  f.v = *reinterpret_cast<const bf16x8*>(rowp + ((chunk ^ sw) << 4));
-}
-__device__ __forceinline__ void read_frag(Frag<float>& f, const unsigned char* rowp, int chunk, int sw) {
-  const float4 lo = *reinterpret_cast<const float4*>(rowp + ((chunk ^ sw) << 4));
-  const float4 hi = *reinterpret_cast<const float4*>(rowp + (((chunk + 1) ^ sw) << 4));
-  f.v[0] = lo.x; f.v[1] = lo.y; f.v[2] = lo.z; f.v[3] = lo.w;
-  f.v[4] = hi.x; f.v[5] = hi.y; f.v[6] = hi.z; f.v[7] = hi.w;
 }
 
 template <typename T, int BM, int BN, int S, int WGM, int WGN, bool kQkv>

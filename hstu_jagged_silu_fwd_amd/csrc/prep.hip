@@ -6,14 +6,14 @@
 //
 // Work decomposition: the new rows of user u are cut into q-blocks of kQB
 // rows; q-block qb sees keys [0, hist + min(n, (qb+1)*kQB)) (causal).  The key
-// range of every (q-block, head) is split into chunks of `chunk_keys` keys
-// (fixed absolute boundaries), one work item per (user, q-block, head, chunk).
+// range of every (q-block, head) is split into near-equal chunks, one work
+// item per (user, q-block, head, chunk).
 // Because the attention has no softmax, the partial outputs of the chunks of
 // a row simply add; the norm kernel sums them in chunk order.
-// The chunk length bound ck = clamp(round_up(total_keys / budget, 64), 64,
-// kMaxChunkKeys) keeps the item count within the number of resident attention
-// workgroups; each entry's keys are then cut into ceil(keys / ck) chunks of
-// near-equal length (multiples of 64).
+// The chunk length bound ck is the smallest multiple of 32 keys (at least 128,
+// at most kMaxChunkKeys) that keeps the item count within the number of
+// resident attention workgroups; each entry's keys are then cut into
+// ceil(keys / ck) chunks of near-equal length (multiples of 32).
 #include "common.h"
 
 namespace hstu {
@@ -21,7 +21,8 @@ namespace {
 
 constexpr int kPrepThreads = 1024;
 constexpr int kPrepWaves = kPrepThreads / kWave;
-constexpr int kMinChunk = 64;
+constexpr int kStepKeys = 32;   // attention key step
+constexpr int kMinChunk = 128;  // one step for each of the four waves
 constexpr int kRowsPerThread = 4;
 constexpr int kRowsPerWg = kPrepThreads * kRowsPerThread;
 
@@ -38,6 +39,7 @@ struct PrepArgs {
 
 struct PrepShared {
   int err;
+  int ck;                          // chunk length bound of the call
   int64_t wsum[kPrepWaves];
   int32_t off[kMaxUsers + 1];
   int32_t hist[kMaxUsers];
@@ -194,31 +196,37 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   if (tid == 0) s.qbb[B] = nqb;
   __syncthreads();
 
-  // 3. chunk size from the total key work
-  int64_t local = 0;
+  // 3. chunk length: the smallest multiple of kStepKeys, at least kMinChunk,
+  //    for which the items H * sum_e ceil(keys_e / L) fit the target (one
+  //    item per resident attention workgroup), capped at kMaxChunkKeys.
+  //    The entry key counts are parked in qbn meanwhile.
   for (int e = tid; e < nqb; e += kPrepThreads) {
     const int u = entry_user(s.qbb, B, e);
     const int qb = e - s.qbb[u];
     const int n = s.off[u + 1] - s.off[u];
-    local += s.hist[u] + min(n, (qb + 1) * kQB);
+    s.qbn[e] = s.hist[u] + min(n, (qb + 1) * kQB);
   }
-  const int64_t total = block_sum(local, s) * a.H;
-  // Rounding adds at most one item per (entry, head); aim below the target
-  // by that much so one pass of resident workgroups covers every item.
-  const int64_t slack = static_cast<int64_t>(a.H) * nqb;
-  const int64_t budget = max(a.target_items - slack, static_cast<int64_t>(a.target_items / 2));
-  int64_t ck = (total + budget - 1) / budget;
-  ck = (ck + 63) / 64 * 64;
-  if (ck < kMinChunk) ck = kMinChunk;
-  if (ck > kMaxChunkKeys) ck = kMaxChunkKeys;
+  __syncthreads();
+  // one wave searches (no barriers); the others wait at the next barrier
+  if (w == 0) {
+    int lo = kMinChunk / kStepKeys, hi = kMaxChunkKeys / kStepKeys;
+    while (lo < hi) {                        // uniform across the wave
+      const int mid = (lo + hi) >> 1;
+      const int len = mid * kStepKeys;
+      int64_t cnt = 0;
+      for (int e = lane; e < nqb; e += kWave) cnt += (s.qbn[e] + len - 1) / len;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
+      if (cnt * a.H <= a.target_items) hi = mid; else lo = mid + 1;
+    }
+    if (lane == 0) s.ck = lo * kStepKeys;
+  }
+  __syncthreads();
+  const int ck = s.ck;
 
   // 4. chunks per entry, then first item of each entry
   for (int e = tid; e < nqb; e += kPrepThreads) {
-    const int u = entry_user(s.qbb, B, e);
-    const int qb = e - s.qbb[u];
-    const int n = s.off[u + 1] - s.off[u];
-    const int64_t keys = s.hist[u] + min(n, (qb + 1) * kQB);
-    const int nch = static_cast<int>((keys + ck - 1) / ck);
+    const int nch = (s.qbn[e] + ck - 1) / ck;
     s.qbn[e] = nch;
     s.qbf[e] = nch * a.H;
   }
@@ -244,8 +252,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     const int n = s.off[u + 1] - s.off[u];
     const int c = s.hist[u];
     const int keys = c + min(n, (qb + 1) * kQB);
-    // the entry's keys are cut into nch near-equal chunks (multiples of 64)
-    const int csz = ((keys + nch - 1) / nch + 63) / 64 * 64;
+    // the entry's keys are cut into nch near-equal chunks (multiples of a
+    // step); csz <= ck, so (nch - 1) * csz < keys and no chunk is empty
+    const int csz = ((keys + nch - 1) / nch + kStepKeys - 1) / kStepKeys * kStepKeys;
     for (int h = 0; h < a.H; ++h)
       for (int kc = 0; kc < nch; ++kc) {
         const int k_lo = kc * csz;

@@ -153,15 +153,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// wait_vm with a wave-uniform run-time count (0..23).
+// wait_vm with a wave-uniform run-time count (0..47).
 __device__ __forceinline__ void wait_vm_n(int n) {
   switch (n) {
 #define HSTU_WAIT_CASE(k) case k: wait_vm<k>(); break;
-    HSTU_WAIT_CASE(0) HSTU_WAIT_CASE(1) HSTU_WAIT_CASE(2) HSTU_WAIT_CASE(3) HSTU_WAIT_CASE(4)
-    HSTU_WAIT_CASE(5) HSTU_WAIT_CASE(6) HSTU_WAIT_CASE(7) HSTU_WAIT_CASE(8) HSTU_WAIT_CASE(9)
-    HSTU_WAIT_CASE(10) HSTU_WAIT_CASE(11) HSTU_WAIT_CASE(12) HSTU_WAIT_CASE(13) HSTU_WAIT_CASE(14)
-    HSTU_WAIT_CASE(15) HSTU_WAIT_CASE(16) HSTU_WAIT_CASE(17) HSTU_WAIT_CASE(18) HSTU_WAIT_CASE(19)
-    HSTU_WAIT_CASE(20) HSTU_WAIT_CASE(21) HSTU_WAIT_CASE(22) HSTU_WAIT_CASE(23)
+#define HSTU_WAIT_8(k) HSTU_WAIT_CASE(k) HSTU_WAIT_CASE(k + 1) HSTU_WAIT_CASE(k + 2) HSTU_WAIT_CASE(k + 3) \
+  HSTU_WAIT_CASE(k + 4) HSTU_WAIT_CASE(k + 5) HSTU_WAIT_CASE(k + 6) HSTU_WAIT_CASE(k + 7)
+    HSTU_WAIT_8(0) HSTU_WAIT_8(8) HSTU_WAIT_8(16) HSTU_WAIT_8(24) HSTU_WAIT_8(32) HSTU_WAIT_8(40)
+#undef HSTU_WAIT_8
 #undef HSTU_WAIT_CASE
     default: wait_vm<0>(); break;
   }

@@ -19,7 +19,7 @@
 namespace hstu {
 namespace {
 
-constexpr int kPrepThreads = 1024;
+constexpr int kPrepThreads = 256;
 constexpr int kPrepWaves = kPrepThreads / kWave;
 constexpr int kStepKeys = 32;   // attention key step
 constexpr int kMinChunk = 128;  // one step for each of the four waves
@@ -39,14 +39,20 @@ struct PrepArgs {
 
 struct PrepShared {
   int err;
-  int ck;                          // chunk length bound of the call
   int64_t wsum[kPrepWaves];
   int32_t off[kMaxUsers + 1];
   int32_t hist[kMaxUsers];
   int32_t qbb[kMaxUsers + 1];      // first q-block entry of each user
   int32_t qbn[kMaxQBlocks];        // chunks per q-block entry
   int32_t qbf[kMaxQBlocks];        // first work item of each q-block entry
+  int32_t qbu[kMaxQBlocks];        // user of each q-block entry
+  int32_t pgp[kMaxUsers + 1];      // first flat page index of each user
+  int32_t cnt[16];                 // which candidate chunk lengths fit
 };
+
+// Candidate chunk lengths tried at once by the chunk-length search.
+constexpr int kCand = 16;
+constexpr int kCandPerWave = kCand / kPrepWaves;
 
 __device__ void set_err(PrepShared& s, int code) { atomicCAS(&s.err, 0, code); }
 
@@ -167,16 +173,35 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   }
   __syncthreads();
   if (s.err == 0) {
-    // page ids of every position in use: one wavefront per user
-    for (int u = w; u < B; u += kPrepWaves) {
-      const int len = s.hist[u] + (s.off[u + 1] - s.off[u]);
-      const int npg = (len + a.ps - 1) / a.ps;
-      const int32_t* row = a.pt + static_cast<size_t>(u) * a.maxP;
-      for (int j = lane; j < npg; j += kWave) {
-        const int32_t pg = row[j];
-        if (pg < 0 || pg >= a.P) set_err(s, HSTU_DEV_BAD_PAGE);
+    // page ids of every position in use, over a flat (user, page) index so
+    // that each thread issues its loads back to back
+    for (int u = tid; u < B; u += kPrepThreads)
+      s.pgp[u] = (s.hist[u] + (s.off[u + 1] - s.off[u]) + a.ps - 1) / a.ps;
+    __syncthreads();
+    const int64_t total_pages = block_scan(s.pgp, B, s);
+    if (tid == 0) s.pgp[B] = static_cast<int32_t>(total_pages);
+    __syncthreads();
+    constexpr int kU = 4;
+    bool bad = false;
+    for (int64_t i0 = tid; i0 < total_pages; i0 += kU * kPrepThreads) {
+      int32_t pg[kU];
+#pragma unroll
+      for (int k = 0; k < kU; ++k) {
+        const int i = static_cast<int>(i0) + k * kPrepThreads;
+        pg[k] = 0;
+        if (i < total_pages) {
+          int lo = 0, hi = B - 1;              // user owning flat page i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s.pgp[mid] <= i) lo = mid; else hi = mid - 1;
+          }
+          pg[k] = a.pt[static_cast<size_t>(lo) * a.maxP + (i - s.pgp[lo])];
+        }
       }
+#pragma unroll
+      for (int k = 0; k < kU; ++k) bad |= pg[k] < 0 || pg[k] >= a.P;
     }
+    if (bad) set_err(s, HSTU_DEV_BAD_PAGE);
   }
   __syncthreads();
   if (s.err != 0) {
@@ -205,24 +230,45 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     const int qb = e - s.qbb[u];
     const int n = s.off[u + 1] - s.off[u];
     s.qbn[e] = s.hist[u] + min(n, (qb + 1) * kQB);
+    s.qbu[e] = u;
   }
   __syncthreads();
-  // one wave searches (no barriers); the others wait at the next barrier
-  if (w == 0) {
-    int lo = kMinChunk / kStepKeys, hi = kMaxChunkKeys / kStepKeys;
-    while (lo < hi) {                        // uniform across the wave
-      const int mid = (lo + hi) >> 1;
-      const int len = mid * kStepKeys;
-      int64_t cnt = 0;
+  // H * sum_e ceil(k_e / L) lies in [H*K/L, H*K/L + H*nqb] for K = sum_e k_e,
+  // so the answer sits between L_lo = H*K/T and L_hi = H*K/(T - H*nqb); up to
+  // 16 candidates spread over that window are tried at once (four per wave).
+  int64_t part = 0;
+  for (int e = tid; e < nqb; e += kPrepThreads) part += s.qbn[e];
+  const int64_t hk = block_sum(part, s) * a.H;
+  const int64_t target = a.target_items;
+  const int64_t slack = static_cast<int64_t>(a.H) * nqb;
+  auto round_step = [](int64_t x) { return (x + kStepKeys - 1) / kStepKeys; };   // keys -> steps
+  int ck;
+  if (target <= slack) {
+    ck = kMaxChunkKeys;                      // every entry already has an item per head
+  } else {
+    const int64_t cap = kMaxChunkKeys / kStepKeys;
+    const int64_t lo_s = min(cap, max<int64_t>(kMinChunk / kStepKeys, round_step((hk + target - 1) / target)));
+    const int64_t hi_s = min(cap, max(lo_s, round_step((hk + (target - slack) - 1) / (target - slack))));
+    const int stride = static_cast<int>((hi_s - lo_s + kCand) / kCand);   // >= 1
+    auto count_items = [&](int steps) {        // wave-cooperative; the same in every lane
+      const int len = steps * kStepKeys;
+      int cnt = 0;
       for (int e = lane; e < nqb; e += kWave) cnt += (s.qbn[e] + len - 1) / len;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
-      if (cnt * a.H <= a.target_items) hi = mid; else lo = mid + 1;
+      return static_cast<int64_t>(cnt) * a.H;
+    };
+    for (int k = w * kCandPerWave; k < (w + 1) * kCandPerWave; ++k) {
+      const int cand = static_cast<int>(min<int64_t>(lo_s + static_cast<int64_t>(k) * stride, hi_s));
+      const bool fits = cand == hi_s || count_items(cand) <= target;
+      if (lane == 0) s.cnt[k] = fits ? 1 : 0;
     }
-    if (lane == 0) s.ck = lo * kStepKeys;
+    __syncthreads();
+    int j = kCand - 1;
+    for (int k = kCand - 1; k >= 0; --k)
+      if (s.cnt[k]) j = k;
+    ck = static_cast<int>(min<int64_t>(lo_s + static_cast<int64_t>(j) * stride, hi_s)) * kStepKeys;
   }
-  __syncthreads();
-  const int ck = s.ck;
 
   // 4. chunks per entry, then first item of each entry
   for (int e = tid; e < nqb; e += kPrepThreads) {
@@ -242,27 +288,31 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     return;
   }
 
-  // 5. the work list and the per-entry tables used by the norm kernel
+  // 5. the work list (one thread per item) and the per-entry tables used by
+  //    the norm kernel
   for (int e = tid; e < nqb; e += kPrepThreads) {
-    const int u = entry_user(s.qbb, B, e);
-    const int qb = e - s.qbb[u];
-    const int f = s.qbf[e], nch = s.qbn[e];
-    a.ws.qb_first[e] = f;
-    a.ws.qb_nch[e] = nch;
+    a.ws.qb_first[e] = s.qbf[e];
+    a.ws.qb_nch[e] = s.qbn[e];
+  }
+  for (int i = tid; i < n_items; i += kPrepThreads) {
+    int lo = 0, hi = nqb - 1;                // last entry whose first item <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s.qbf[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo, u = s.qbu[e], qb = e - s.qbb[u], nch = s.qbn[e];
+    const int r = i - s.qbf[e], h = r / nch, kc = r - h * nch;
     const int n = s.off[u + 1] - s.off[u];
     const int c = s.hist[u];
     const int keys = c + min(n, (qb + 1) * kQB);
     // the entry's keys are cut into nch near-equal chunks (multiples of a
     // step); csz <= ck, so (nch - 1) * csz < keys and no chunk is empty
     const int csz = ((keys + nch - 1) / nch + kStepKeys - 1) / kStepKeys * kStepKeys;
-    for (int h = 0; h < a.H; ++h)
-      for (int kc = 0; kc < nch; ++kc) {
-        const int k_lo = kc * csz;
-        AttnItem it;
-        it.a = make_int4(u, qb * kQB, h, k_lo);
-        it.b = make_int4(min(keys, k_lo + csz), s.off[u], n, c);
-        a.ws.items[f + h * nch + kc] = it;
-      }
+    const int k_lo = kc * csz;
+    AttnItem it;
+    it.a = make_int4(u, qb * kQB, h, k_lo);
+    it.b = make_int4(min(keys, k_lo + csz), s.off[u], n, c);
+    a.ws.items[i] = it;
   }
   for (int u = tid; u <= B; u += kPrepThreads) a.ws.qb_base[u] = s.qbb[u];
 

@@ -128,32 +128,29 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   const int64_t* ts = d.ts_buckets > 0 ? timestamps : nullptr;
   const float* tsb = d.ts_buckets > 0 ? ts_bias : nullptr;
 
-  auto rec = [&](int idx) -> bool {
-    return ev == nullptr || ev[idx] == nullptr ||
-           hipEventRecord(static_cast<hipEvent_t>(ev[idx]), st) == hipSuccess;
+  // stage k's kernel is bracketed by events ev[2k] (start) and ev[2k+1] (stop)
+  auto kev = [&](int stage) -> KernelEvents {
+    KernelEvents k;
+    if (ev != nullptr) {
+      k.start = static_cast<hipEvent_t>(ev[2 * stage]);
+      k.stop = static_cast<hipEvent_t>(ev[2 * stage + 1]);
+    }
+    return k;
   };
   hipError_t e;
-  if (!rec(2 * HSTU_STAGE_PREP)) return HSTU_ERR_HIP;
-  e = launch_prep(d, new_offsets, hist_len, page_table, ts_off, ws, L.nqb_cap, L.item_cap, grid, st);
-  if (e != hipSuccess || !rec(2 * HSTU_STAGE_PREP + 1)) return HSTU_ERR_HIP;
+  e = launch_prep(d, new_offsets, hist_len, page_table, ts_off, ws, L.nqb_cap, L.item_cap, grid, st,
+                  kev(HSTU_STAGE_PREP));
+  if (e != hipSuccess) return HSTU_ERR_HIP;
   if (!any_rows) return HSTU_OK;
-
-  if (!rec(2 * HSTU_STAGE_PROJ)) return HSTU_ERR_HIP;
-  e = launch_gemm_qkv(d, x, w1t, k_pool, v_pool, ws, st);
-  if (e != hipSuccess || !rec(2 * HSTU_STAGE_PROJ + 1)) return HSTU_ERR_HIP;
-
-  if (!rec(2 * HSTU_STAGE_ATTN)) return HSTU_ERR_HIP;
+  e = launch_gemm_qkv(d, x, w1t, k_pool, v_pool, ws, st, kev(HSTU_STAGE_PROJ));
+  if (e != hipSuccess) return HSTU_ERR_HIP;
   e = launch_attn(d, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ws,
-                  grid < L.item_cap ? grid : L.item_cap, st);
-  if (e != hipSuccess || !rec(2 * HSTU_STAGE_ATTN + 1)) return HSTU_ERR_HIP;
-
-  if (!rec(2 * HSTU_STAGE_NORM)) return HSTU_ERR_HIP;
-  e = launch_norm_gate(d, new_offsets, ws, st);
-  if (e != hipSuccess || !rec(2 * HSTU_STAGE_NORM + 1)) return HSTU_ERR_HIP;
-
-  if (!rec(2 * HSTU_STAGE_OUT)) return HSTU_ERR_HIP;
-  e = launch_gemm_out(d, ws.q, w2t, y, &ws.hdr->status, st);
-  if (e != hipSuccess || !rec(2 * HSTU_STAGE_OUT + 1)) return HSTU_ERR_HIP;
+                  grid < L.item_cap ? grid : L.item_cap, st, kev(HSTU_STAGE_ATTN));
+  if (e != hipSuccess) return HSTU_ERR_HIP;
+  e = launch_norm_gate(d, new_offsets, ws, st, kev(HSTU_STAGE_NORM));
+  if (e != hipSuccess) return HSTU_ERR_HIP;
+  e = launch_gemm_out(d, ws.q, w2t, y, &ws.hdr->status, st, kev(HSTU_STAGE_OUT));
+  if (e != hipSuccess) return HSTU_ERR_HIP;
   return HSTU_OK;
 }
 

@@ -412,7 +412,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
 template <typename T, int HD>
 hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                   const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,
-                  const WsPtrs& ws, int grid, hipStream_t stream) {
+                  const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
   AttnArgs<T> a;
   a.pt = pt;
   a.k_pool = static_cast<const T*>(k_pool);
@@ -433,18 +433,17 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.mbits = d.pos_mbits;
   a.ntsb = d.ts_buckets;
   a.tsmbits = d.ts_mbits;
-  attn_kernel<T, HD><<<grid, 64 * kWaves, 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_kernel(attn_kernel<T, HD>, dim3(grid), dim3(64 * kWaves), stream, ev, a);
 }
 
 template <typename T>
 hipError_t attn_dt(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                    const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,
-                   const WsPtrs& ws, int grid, hipStream_t stream) {
+                   const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
   switch (d.head_dim) {
-    case 32: return attn_t<T, 32>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream);
-    case 64: return attn_t<T, 64>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream);
-    default: return attn_t<T, 128>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream);
+    case 32: return attn_t<T, 32>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
+    case 64: return attn_t<T, 64>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
+    default: return attn_t<T, 128>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
   }
 }
 
@@ -452,10 +451,11 @@ hipError_t attn_dt(const hstu_layer_desc& d, const int32_t* pt, const void* k_po
 
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,
-                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream) {
+                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream,
+                       const KernelEvents& ev) {
   if (d.dtype == HSTU_BF16)
-    return attn_dt<bf16>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream);
-  return attn_dt<float>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream);
+    return attn_dt<bf16>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
+  return attn_dt<float>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
 }
 
 }  // namespace hstu

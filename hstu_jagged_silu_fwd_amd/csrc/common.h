@@ -1,6 +1,7 @@
 // Internal definitions shared by the gfx950 kernels of libhstu.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -219,19 +220,42 @@ struct WsPtrs {
   float* part;               // [item_cap, kQB, d] fp32 partial attention outputs
 };
 
+// Optional events that the runtime stamps at the start and the end of one
+// kernel's execution (hipExtLaunchKernel), so that their difference is that
+// kernel's duration alone.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launch `kernel` on `stream`; with events, through hipExtLaunchKernel so
+// that they bracket exactly this kernel.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                                const KernelEvents& ev, Args... args) {
+  if (ev.start == nullptr && ev.stop == nullptr) {
+    kernel<<<grid, block, 0, stream>>>(args...);
+    return hipGetLastError();
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  return hipGetLastError();
+}
+
 // Host launchers (one per kernel family), all enqueue on `stream`.
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
                        const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
-                       int nqb_cap, int item_cap, int target_items, hipStream_t stream);
+                       int nqb_cap, int item_cap, int target_items, hipStream_t stream,
+                       const KernelEvents& ev = {});
 hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
-                           void* v_pool, const WsPtrs& ws, hipStream_t stream);
+                           void* v_pool, const WsPtrs& ws, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                           const int32_t* status, hipStream_t stream);
+                           const int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,
-                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream);
+                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream,
+                       const KernelEvents& ev = {});
 hipError_t launch_norm_gate(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws,
-                            hipStream_t stream);
+                            hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_append(const hstu_layer_desc& d, const void* k_new, const void* v_new,
                          const int32_t* new_off, const int32_t* hist, const int32_t* pt,
                          void* k_pool, void* v_pool, int32_t* status, hipStream_t stream);

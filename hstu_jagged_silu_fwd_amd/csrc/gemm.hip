@@ -228,7 +228,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const T* __restric
 
 template <typename T, int BM, int BN, int S, int WGM, int WGN>
 hipError_t gemm_qkv_t(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool, void* v_pool,
-                      const WsPtrs& ws, hipStream_t stream) {
+                      const WsPtrs& ws, hipStream_t stream, const KernelEvents& ev) {
   QkvEpi<T> ep;
   ep.q = static_cast<T*>(ws.q);
   ep.u = static_cast<T*>(ws.u);
@@ -241,20 +241,20 @@ hipError_t gemm_qkv_t(const hstu_layer_desc& d, const void* x, const void* w1t, 
   ep.ps = d.page_size;
   const int M = d.total_new, N = 4 * d.hidden, K = d.hidden;
   const int tiles = (M + BM - 1) / BM * (N / BN);
-  gemm_kernel<T, BM, BN, S, WGM, WGN, true><<<tiles, 64 * WGM * WGN, 0, stream>>>(
-      static_cast<const T*>(x), static_cast<const T*>(w1t), M, N, K, nullptr, ep, &ws.hdr->status);
-  return hipGetLastError();
+  return launch_kernel(gemm_kernel<T, BM, BN, S, WGM, WGN, true>, dim3(tiles), dim3(64 * WGM * WGN), stream, ev,
+                       static_cast<const T*>(x), static_cast<const T*>(w1t), M, N, K, static_cast<T*>(nullptr),
+                       ep, static_cast<const int32_t*>(&ws.hdr->status));
 }
 
 template <typename T, int BM, int BN, int S, int WGM, int WGN>
 hipError_t gemm_out_t(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                      const int32_t* status, hipStream_t stream) {
+                      const int32_t* status, hipStream_t stream, const KernelEvents& ev) {
   QkvEpi<T> ep{};
   const int M = d.total_new, N = d.hidden, K = d.hidden;
   const int tiles = (M + BM - 1) / BM * (N / BN);
-  gemm_kernel<T, BM, BN, S, WGM, WGN, false><<<tiles, 64 * WGM * WGN, 0, stream>>>(
-      static_cast<const T*>(g), static_cast<const T*>(w2t), M, N, K, static_cast<T*>(y), ep, status);
-  return hipGetLastError();
+  return launch_kernel(gemm_kernel<T, BM, BN, S, WGM, WGN, false>, dim3(tiles), dim3(64 * WGM * WGN), stream,
+                       ev, static_cast<const T*>(g), static_cast<const T*>(w2t), M, N, K, static_cast<T*>(y), ep,
+                       status);
 }
 
 // Tile shape by problem size (two ring stages throughout: several workgroups
@@ -275,28 +275,28 @@ Tile pick_tile(int M, int N, int D) {
 
 template <typename T>
 hipError_t qkv_dispatch(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool, void* v_pool,
-                        const WsPtrs& ws, hipStream_t st) {
+                        const WsPtrs& ws, hipStream_t st, const KernelEvents& ev) {
   if constexpr (sizeof(T) == 4) {
-    return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st);   // fp32: one tile shape
+    return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st, ev);   // fp32: one tile shape
   } else {
     switch (pick_tile(d.total_new, 4 * d.hidden, d.hidden)) {
-      case Tile::k128x128: return gemm_qkv_t<T, 128, 128, 2, 2, 4>(d, x, w1t, k_pool, v_pool, ws, st);
-      case Tile::k64x128: return gemm_qkv_t<T, 64, 128, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st);
-      default: return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st);
+      case Tile::k128x128: return gemm_qkv_t<T, 128, 128, 2, 2, 4>(d, x, w1t, k_pool, v_pool, ws, st, ev);
+      case Tile::k64x128: return gemm_qkv_t<T, 64, 128, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st, ev);
+      default: return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st, ev);
     }
   }
 }
 
 template <typename T>
 hipError_t out_dispatch(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                        const int32_t* status, hipStream_t st) {
+                        const int32_t* status, hipStream_t st, const KernelEvents& ev) {
   if constexpr (sizeof(T) == 4) {
-    return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st);   // fp32: one tile shape
+    return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st, ev);   // fp32: one tile shape
   } else {
     switch (pick_tile(d.total_new, d.hidden, d.hidden)) {
-      case Tile::k128x128: return gemm_out_t<T, 128, 128, 2, 2, 4>(d, g, w2t, y, status, st);
-      case Tile::k64x128: return gemm_out_t<T, 64, 128, 2, 2, 2>(d, g, w2t, y, status, st);
-      default: return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st);
+      case Tile::k128x128: return gemm_out_t<T, 128, 128, 2, 2, 4>(d, g, w2t, y, status, st, ev);
+      case Tile::k64x128: return gemm_out_t<T, 64, 128, 2, 2, 2>(d, g, w2t, y, status, st, ev);
+      default: return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st, ev);
     }
   }
 }
@@ -304,15 +304,15 @@ hipError_t out_dispatch(const hstu_layer_desc& d, const void* g, const void* w2t
 }  // namespace
 
 hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
-                           void* v_pool, const WsPtrs& ws, hipStream_t stream) {
-  return d.dtype == HSTU_BF16 ? qkv_dispatch<bf16>(d, x, w1t, k_pool, v_pool, ws, stream)
-                              : qkv_dispatch<float>(d, x, w1t, k_pool, v_pool, ws, stream);
+                           void* v_pool, const WsPtrs& ws, hipStream_t stream, const KernelEvents& ev) {
+  return d.dtype == HSTU_BF16 ? qkv_dispatch<bf16>(d, x, w1t, k_pool, v_pool, ws, stream, ev)
+                              : qkv_dispatch<float>(d, x, w1t, k_pool, v_pool, ws, stream, ev);
 }
 
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                           const int32_t* status, hipStream_t stream) {
-  return d.dtype == HSTU_BF16 ? out_dispatch<bf16>(d, g, w2t, y, status, stream)
-                              : out_dispatch<float>(d, g, w2t, y, status, stream);
+                           const int32_t* status, hipStream_t stream, const KernelEvents& ev) {
+  return d.dtype == HSTU_BF16 ? out_dispatch<bf16>(d, g, w2t, y, status, stream, ev)
+                              : out_dispatch<float>(d, g, w2t, y, status, stream, ev);
 }
 
 }  // namespace hstu

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(NormArgs<T> a) {
 }
 
 template <typename T>
-hipError_t norm_t(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws, hipStream_t stream) {
+hipError_t norm_t(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws, hipStream_t stream,
+                  const KernelEvents& ev) {
   NormArgs<T> a;
   a.new_off = new_off;
   a.row_user = ws.row_user;
@@ -149,16 +150,15 @@ hipError_t norm_t(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs
   a.scale = d.attn_scale * kNegLn2;   // the attention accumulates -log2(e) * SiLU
   a.eps = d.norm_eps;
   const int grid = (d.total_new + 3) / 4;
-  norm_gate_kernel<T><<<grid, 256, 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_kernel(norm_gate_kernel<T>, dim3(grid), dim3(256), stream, ev, a);
 }
 
 }  // namespace
 
 hipError_t launch_norm_gate(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws,
-                            hipStream_t stream) {
-  if (d.dtype == HSTU_BF16) return norm_t<bf16>(d, new_off, ws, stream);
-  return norm_t<float>(d, new_off, ws, stream);
+                            hipStream_t stream, const KernelEvents& ev) {
+  if (d.dtype == HSTU_BF16) return norm_t<bf16>(d, new_off, ws, stream, ev);
+  return norm_t<float>(d, new_off, ws, stream, ev);
 }
 
 }  // namespace hstu

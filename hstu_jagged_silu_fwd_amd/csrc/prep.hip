@@ -328,7 +328,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
 
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
                        const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
-                       int nqb_cap, int item_cap, int target_items, hipStream_t stream) {
+                       int nqb_cap, int item_cap, int target_items, hipStream_t stream,
+                       const KernelEvents& ev) {
   PrepArgs a;
   a.new_off = new_off;
   a.hist = hist;
@@ -344,8 +345,8 @@ hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const i
   a.nqb_cap = nqb_cap;
   a.item_cap = item_cap;
   a.target_items = target_items;
-  prep_kernel<<<1 + (d.total_new + kRowsPerWg - 1) / kRowsPerWg, kPrepThreads, 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_kernel(prep_kernel, dim3(1 + (d.total_new + kRowsPerWg - 1) / kRowsPerWg), dim3(kPrepThreads),
+                       stream, ev, a);
 }
 
 }  // namespace hstu

@@ -144,10 +144,13 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x,
                            const int32_t* ts_offsets, void* y, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
 
-/* Same as hstu_layer_fwd, and additionally records caller-created hipEvent_t
- * handles around each stage so a caller can time the stages on the stream the
- * kernels run on.  stage_events holds 2*HSTU_NUM_STAGES events (start, stop
- * per stage, in the order of hstu_stage); NULL behaves like hstu_layer_fwd. */
+/* Same as hstu_layer_fwd, and additionally has the runtime stamp
+ * caller-created hipEvent_t handles at the start and the end of each stage's
+ * kernel (hipExtLaunchKernel), so that hipEventElapsedTime of a pair is that
+ * kernel's execution time alone, without launch gaps.  stage_events holds
+ * 2*HSTU_NUM_STAGES events (start, stop per stage, in the order of
+ * hstu_stage); a NULL array or NULL entries record nothing.  Ownership of the
+ * events stays with the caller. */
 typedef enum {
   HSTU_STAGE_PREP = 0,         /* index prep / validation / work list */
   HSTU_STAGE_PROJ = 1,         /* X W1 + SiLU + split + K/V append */

@@ -8,14 +8,17 @@
 // One work item = (user, q-block of up to kQB = 256 new rows, head, key
 // chunk): a q-block covers all new rows of most users, so each history key is
 // read once per head and chunk.  A workgroup of eight waves takes one item at
-// a time; wave w owns the q-block's query groups w and w + 8 (16 rows each;
-// interleaved so partial blocks spread evenly) and sits out the products of
-// groups the block does not have.  The chunk's keys are walked in 32-key
-// steps.  A step's K rows [32][d] and V^T rows [d][32] are copied from their
-// pool pages into a ring of NST LDS stages with direct-to-LDS loads that the
-// waves share out; the ring runs NST-1 steps ahead of the step being
-// multiplied and one barrier per step hands a stage from the loads to the
-// products and back.
+// a time.  The q-block's 16-row query groups are taken in adjacent pairs, one
+// pair per wave; when the block has few groups the waves also split the key
+// steps: they form P phases (P = 4, 2 or 1, as many as the waves allow) and
+// the waves of phase p multiply the steps s = p (mod P), so every wave has
+// products to do even for a single 16-row group.  The chunk's keys are walked
+// in 32-key steps.  A step's K rows [32][d] and V^T rows [d][32] are copied
+// from their pool pages into a ring of NST LDS stages with direct-to-LDS
+// loads that the waves share out; one barrier per round of P steps hands the
+// round's stages from the loads to the products, and the loads of the round D
+// rounds ahead (D = NST/P - 1) go into the stages the previous round freed.
+// At the end of an item the phases' partial sums meet in LDS.
 // Per step and wave:
 //   S^T[32 keys x 16 queries] = K * Q^T     (2 MFMA blocks over d; the
 //                                           accumulators start at the bias)
@@ -26,8 +29,7 @@
 // keys of one query, which is exactly its B-operand fragment for the second
 // product: scores never leave registers.  Each K and V^T fragment read from
 // LDS feeds both of a wave's groups.  The query fragments stay in registers
-// for the whole item, and each wave writes its own groups' partial output
-// rows (no cross-wave reduction).  In LDS the 16-byte chunks of every row are
+// for the whole item.  In LDS the 16-byte chunks of every row are
 // XOR-permuted so that the fragment reads of 16 lanes (16 rows, one chunk
 // each) fall into distinct banks.
 //
@@ -47,7 +49,8 @@
 // Partial outputs (fp32) go to the workspace; the chunks of a row are added
 // by the norm kernel (no softmax, so partial sums over key ranges simply
 // add).  The grid is persistent, one workgroup per CU: workgroup i takes
-// item i first and then fetches further items dynamically, one ahead.
+// item i first and, when there are more items than workgroups, fetches
+// further items dynamically, one ahead.
 #include <type_traits>
 
 #include "common.h"
@@ -85,11 +88,11 @@ __device__ __forceinline__ int bucket_start(int b, int m) {
 }
 
 constexpr int kWaves = 8;          // waves per workgroup
-constexpr int kGpw = 2;            // 16-query groups per wave
-static_assert(kQB == 16 * kWaves * kGpw, "a q-block is one group per wave slot");
+constexpr int kGpw = 2;            // 16-query groups per wave (an adjacent pair)
+static_assert(kQB == 16 * kWaves * kGpw, "a q-block is two groups per wave");
 
 // Sizes of one ring stage (one 32-key step of K and V^T) for element type T
-// and head dim HD.
+// and head dim HD, and of the ring.
 template <typename T, int HD>
 struct StepGeo {
   static constexpr int ES = static_cast<int>(sizeof(T));
@@ -99,9 +102,11 @@ struct StepGeo {
   static constexpr int KBYTES = kStepKeys * HD * ES;   // the K rows of a step
   static constexpr int STAGE = 2 * KBYTES;             // K rows, then V^T rows
   static constexpr int NBLK = STAGE / 1024;            // 1 KiB loads per stage
-  static constexpr int IPW = (NBLK + kWaves - 1) / kWaves;   // loads per wave (at most)
-  static constexpr int NST_FIT = 49152 / STAGE;        // stages in 48 KiB
-  static constexpr int NST = NST_FIT < 2 ? 2 : (NST_FIT > 6 ? 6 : NST_FIT);
+  static constexpr int IPW = (NBLK + kWaves - 1) / kWaves;   // loads per wave and stage (at most)
+  // ring: 8 stages, or as many as fit in 128 KiB (a power of two)
+  static constexpr int NST_FIT = 131072 / STAGE;
+  static constexpr int NST = NST_FIT >= 8 ? 8 : (NST_FIT >= 4 ? 4 : 2);
+  static constexpr int PMAX = NST / 2;                 // phases: the ring holds two rounds of PMAX steps
   // chunk permutation of K row `key`: (m >> KSH) with m = (key & 3) | (((key >> 3) & 3) << 2),
   // m being the lane (mod 16) that reads the row; V^T row e: (e >> VSH) & (VCH - 1)
   static constexpr int KSH = KCH >= 16 ? 0 : (KCH == 8 ? 1 : 2);
@@ -110,6 +115,9 @@ struct StepGeo {
   static_assert(NBLK * 1024 == STAGE, "whole loads per stage");
   static_assert((kStepKeys * KCH) % 64 == 0, "a load never straddles K and V^T");
   static_assert((IPW + 1) * (NST - 2) <= 23, "wait count range");
+  // the phase reduction reuses the ring: at most (PMAX-1) * (kWaves/PMAX)
+  // waves hand over two 16 x HD fp32 tiles each
+  static_assert(NST * STAGE >= (PMAX - 1) * (kWaves / PMAX) * kGpw * 16 * HD * 4, "reduction fits the ring");
 };
 
 template <typename T, int HD>
@@ -119,6 +127,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   constexpr int NT = 64 * kWaves;
   constexpr int NC = HD / 32;        // 32-wide slices of the head dim (contraction of S^T)
   constexpr int NO = HD / 16;        // 16-row blocks of O^T
+  static_assert(kMaxChunkPages <= 2 * NT, "two page ids per thread");
   __shared__ __attribute__((aligned(1024))) unsigned char s_ring[NST * G::STAGE];
   __shared__ __attribute__((aligned(256))) int64_t s_ts[NST][kStepKeys];
   __shared__ float s_lut[kLut];
@@ -127,15 +136,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   __shared__ int s_pages[kMaxChunkPages];
   __shared__ int s_next;
 
-  // status and item count in one load; the bias tables are loaded alongside
-  const int4 hv = *reinterpret_cast<const int4*>(a.hdr);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  // Status and item count, the first item (static: workgroup i takes item i;
+  // the grid never exceeds the item capacity) and the bias tables are all
+  // loaded at once.
+  const int4 hv = *reinterpret_cast<const int4*>(a.hdr);
+  AttnItem item = a.items[blockIdx.x];
   for (int i = tid; i < a.nb; i += NT) s_pb[i] = kNegLog2e * a.pos_bias[i];
   for (int i = tid; i < a.ntsb; i += NT) s_tb[i] = kNegLog2e * a.ts_bias[i];
   if (hv.x != 0) return;                   // status: prep rejected the call
   const int n_items = hv.y;
-  if (tid == 0) s_next = blockIdx.x;       // first item: static
+  const bool dynamic = n_items > static_cast<int>(gridDim.x);
   __syncthreads();
   for (int i = tid; i < kLut; i += NT) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];
   const int ps = 1 << a.ps_shift;
@@ -146,10 +158,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
   const int ksw = l16 >> G::KSH;
   const int vsw = (l16 >> G::VSH) & (VCH - 1);
-  // loads this wave issues per stage (its K/V^T blocks, plus the key
-  // timestamps for wave 0), and the count to wait for NST-2 stages of them
+  // loads this wave issues per step (its K/V^T blocks, plus the key
+  // timestamps for wave 0)
   const int my_blk = min(max(G::NBLK - w * IPW, 0), IPW);
-  const int my_wait = (my_blk + ((has_ts && w == 0) ? 1 : 0)) * (NST - 2);
+  const int my_cnt = my_blk + ((has_ts && w == 0) ? 1 : 0);
   // Source of this lane's 16 bytes in load j, relative to the step's page
   // base: element offset lo[j] inside the (page, head) block, and whether it
   // lies in the step's second page (16-token pages only: a 32-key step then
@@ -174,29 +186,47 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     }
   }
 
+  int it = blockIdx.x;
   for (;;) {
-    __syncthreads();                       // previous item consumed; s_next published
-    const int it = s_next;
     if (it >= n_items) break;
-    const AttnItem item = a.items[it];
-    const int u = item.a.x, q0 = item.a.y, h = item.a.z, k_lo = item.a.w;
-    const int k_hi = item.b.x, off_u = item.b.y, n = item.b.z, c = item.b.w;
+    const int u = __builtin_amdgcn_readfirstlane(item.a.x);
+    const int q0 = __builtin_amdgcn_readfirstlane(item.a.y);
+    const int h = __builtin_amdgcn_readfirstlane(item.a.z);
+    const int k_lo = __builtin_amdgcn_readfirstlane(item.a.w);
+    const int k_hi = __builtin_amdgcn_readfirstlane(item.b.x);
+    const int off_u = __builtin_amdgcn_readfirstlane(item.b.y);
+    const int n = __builtin_amdgcn_readfirstlane(item.b.z);
+    const int c = __builtin_amdgcn_readfirstlane(item.b.w);
     const int len = c + n;
     const int nq = min(kQB, n - q0);
     const int ngroups = (nq + 15) >> 4;
+    // Phases: the waves form P phases of NW waves; wave (phase p, column j)
+    // owns query groups 2j and 2j+1 and multiplies the steps s = p (mod P).
+    // Few groups -> several phases, so that every wave has products to do.
+    const int NW = (ngroups + 1) >> 1;
+    const int P = (G::PMAX >= 4 && 4 * NW <= kWaves) ? 4 : ((G::PMAX >= 2 && 2 * NW <= kWaves) ? 2 : 1);
+    const int D = NST / P - 1;                         // rounds of loads in flight ahead
+    const int ph = w / NW, col = w - (w / NW) * NW;
+    const int gi0 = 2 * col;                           // this wave's first group
+    const int ng_w = ph < P ? min(2, ngroups - gi0) : 0;   // its groups: 0, 1 or 2
     const int32_t* ptu = a.pt + static_cast<size_t>(u) * a.maxP;
     const int pg0 = k_lo >> a.ps_shift;
     const int kst_end = min(k_hi, len);                // keys whose pages are staged
     const int npg = ((kst_end - 1) >> a.ps_shift) - pg0 + 1;
-    for (int i = tid; i < npg; i += NT) s_pages[i] = ptu[pg0 + i];
-    // this wave's query groups w and w + kWaves: fragments and timestamps
-    const int ng_w = (ngroups > w) + (ngroups > w + kWaves);   // 0, 1 or 2
+    // the next item's index is fetched now, alongside the page ids and the
+    // query fragments; all three have landed at the wait below.  (With no
+    // more items than workgroups nothing is fetched: the shared counter's
+    // atomics would only queue up behind each other.)
+    int nxt = 0;
+    if (dynamic && tid == 0) nxt = atomicAdd(&a.hdr->counter, 1);
+    const int pid0 = tid < npg ? ptu[pg0 + tid] : 0;
+    const int pid1 = tid + NT < npg ? ptu[pg0 + tid + NT] : 0;
     Frag<T> qf[kGpw][NC];
     int64_t tq[kGpw];
     const int64_t* tsu = has_ts ? a.ts + a.ts_off[u] : nullptr;
 #pragma unroll
     for (int i = 0; i < kGpw; ++i) {
-      const int qrow = min(q0 + 16 * (w + kWaves * i) + l16, n - 1);
+      const int qrow = min(q0 + 16 * (gi0 + i) + l16, n - 1);
       const T* qp = a.q + static_cast<size_t>(off_u + qrow) * a.D + h * HD + 8 * g;
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) load_frag(qf[i][cc], qp + cc * 32);
@@ -204,32 +234,31 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     }
     const int kend = min(k_hi, c + q0 + nq);           // keys up to the block's last query
     const int nsteps = (kend - k_lo + kStepKeys - 1) / kStepKeys;
-    // Let the query loads land before the ring starts: the compiler cannot
-    // count outstanding loads across the key loop, so it would otherwise
-    // wait for every in-flight stage at the first use of a query fragment.
+    const int nrounds = (nsteps + P - 1) / P;
+    // Let these loads land before the ring starts: the compiler cannot count
+    // outstanding loads across the key loop, so it would otherwise wait for
+    // every in-flight stage at the first use of a query fragment.
     wait_vm<0>();
-    __syncthreads();                       // pages staged; everyone has read s_next
-    if (tid == 0) s_next = static_cast<int>(gridDim.x) + atomicAdd(&a.hdr->counter, 1);
+    if (tid < npg) s_pages[tid] = pid0;
+    if (tid + NT < npg) s_pages[tid + NT] = pid1;
+    if (tid == 0) s_next = dynamic ? static_cast<int>(gridDim.x) + nxt : n_items;
+    __syncthreads();                       // pages staged; s_next published
+    // the next item's descriptor, in flight during this item's key loop
+    const int it_next = s_next;
+    AttnItem item_next = item;
+    if (it_next < n_items) item_next = a.items[it_next];
 
     // ---- loads of step s into stage s % NST ----
     const size_t kv_head = static_cast<size_t>(h) * ps * HD;      // head block inside a page
     const size_t page_elems = static_cast<size_t>(a.H) * ps * HD;
     // Keys past the staged range (last step only) read rows of the step's
     // own pages: in bounds, and masked (K) or zeroed (V) by the products.
-    // Page ids of step s (the second one only differs with 16-token pages);
-    // read one step ahead of their use so the LDS latency hides behind a
-    // step's products.
-    auto pages_of = [&](int s) __attribute__((always_inline)) {
-      const int kb = k_lo + kStepKeys * min(s, nsteps - 1);
-      const int pa = s_pages[(kb >> a.ps_shift) - pg0];
-      const int pb = (ps < kStepKeys && kb + ps < kst_end) ? s_pages[((kb + ps) >> a.ps_shift) - pg0] : pa;
-      return make_int2(pa, pb);
-    };
-    auto issue = [&](int s, int2 pgs) __attribute__((always_inline)) {
+    auto issue = [&](int s) __attribute__((always_inline)) {
       const int kb = k_lo + kStepKeys * s;
       unsigned char* stg = s_ring + (s % NST) * G::STAGE;
-      const int pa = __builtin_amdgcn_readfirstlane(pgs.x);
-      const int pb = __builtin_amdgcn_readfirstlane(pgs.y);
+      const int pa = __builtin_amdgcn_readfirstlane(s_pages[(kb >> a.ps_shift) - pg0]);
+      const int pb = (ps < kStepKeys && kb + ps < kst_end)
+                         ? __builtin_amdgcn_readfirstlane(s_pages[((kb + ps) >> a.ps_shift) - pg0]) : pa;
       const size_t in_page = static_cast<size_t>(kb & (ps - 1));   // 0 for 16-token pages
       const size_t ha = static_cast<size_t>(pa) * page_elems + kv_head;
       const size_t hb = static_cast<size_t>(pb) * page_elems + kv_head;
@@ -268,7 +297,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
         // distance of element (block b, row r) is dl0 - 4*b - r
-        const int pq = c + q0 + 16 * (w + kWaves * i);   // first query position of the group
+        const int pq = c + q0 + 16 * (gi0 + i);        // first query position of the group
         dl0[i] = pq + l16 - (kb + 8 * g);
         const int dmin = pq - (kb + kStepKeys - 1);
         const int dmax = pq + 15 - kb;
@@ -371,25 +400,27 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
         for (int i = 0; i < NG; ++i) o[i][ob] = mma16(vf[ob], af[i], o[i][ob]);
     };
 
-    // ---- the key loop: one barrier per step (the wave's group count is
-    // fixed for the item, so each count gets a loop of its own) ----
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s < nsteps) issue(s, pages_of(s));
-    int2 pg_next = pages_of(NST - 1);
+    // ---- the key loop: one barrier per round of P steps.  Round r's steps
+    // sit in stages rP .. rP+P-1 (mod NST); the loads of round r+D are
+    // issued once round r-1's stages are free, so D rounds are in flight
+    // while one is multiplied.  (The wave's group count is fixed for the
+    // item, so each count gets a loop of its own.) ----
+    for (int s = 0; s < min(D * P, nsteps); ++s) issue(s);
     auto key_loop = [&](auto ngc) __attribute__((always_inline)) {
-      for (int s = 0; s < nsteps; ++s) {
-        if (s + NST - 2 < nsteps) wait_vm_n(my_wait);
+      for (int r = 0; r < nrounds; ++r) {
+        // round r's loads have landed once only those issued after them remain
+        const int later = min((r + D) * P, nsteps) - (r + 1) * P;
+        if (later > 0) wait_vm_n(later * my_cnt);
         else wait_vm<0>();
-        bar();                             // stage s visible; stage s-1 no longer read
-        if (s + NST - 1 < nsteps) {
-          issue(s + NST - 1, pg_next);
-          pg_next = pages_of(s + NST);
-        }
+        bar();                             // round r visible; round r-1 no longer read
+        for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
         if constexpr (decltype(ngc)::value > 0) {
-          // a branch per step, not per fragment, for the tail zeroing
-          if (k_lo + kStepKeys * (s + 1) > kst_end) compute(ngc, std::true_type{}, s);
-          else compute(ngc, std::false_type{}, s);
+          const int s = r * P + ph;
+          if (s < nsteps) {
+            // a branch per step, not per fragment, for the tail zeroing
+            if (k_lo + kStepKeys * (s + 1) > kst_end) compute(ngc, std::true_type{}, s);
+            else compute(ngc, std::false_type{}, s);
+          }
         }
       }
     };
@@ -397,18 +428,45 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     else if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
     else key_loop(std::integral_constant<int, 0>{});
 
+    // ---- phases 1..P-1 hand their partial sums to phase 0 through the
+    // (now idle) ring; phase 0 adds them and writes the item's rows ----
+    if (P > 1) {
+      __syncthreads();                     // every wave is done with the ring
+      f32x4* red = reinterpret_cast<f32x4*>(s_ring);
+      if (ph > 0 && ph < P) {
+        f32x4* dst = red + ((ph - 1) * NW + col) * (kGpw * NO * 64);
 #pragma unroll
-    for (int i = 0; i < kGpw; ++i) {
-      const int row = 16 * (w + kWaves * i) + l16;     // row inside the q-block
-      if (i < ng_w && q0 + row < n) {
-        float* dst = a.part + (static_cast<size_t>(it) * kQB + row) * HD + 4 * g;
+        for (int i = 0; i < kGpw; ++i)
 #pragma unroll
-        for (int ob = 0; ob < NO; ++ob) *reinterpret_cast<f32x4*>(dst + ob * 16) = o[i][ob];
+          for (int ob = 0; ob < NO; ++ob) dst[(i * NO + ob) * 64 + lane] = o[i][ob];
+      }
+      __syncthreads();
+      if (ph == 0) {
+        for (int p = 1; p < P; ++p) {
+          const f32x4* srcp = red + ((p - 1) * NW + col) * (kGpw * NO * 64);
+#pragma unroll
+          for (int i = 0; i < kGpw; ++i)
+#pragma unroll
+            for (int ob = 0; ob < NO; ++ob) o[i][ob] += srcp[(i * NO + ob) * 64 + lane];
+        }
       }
     }
+    if (ph == 0) {
+#pragma unroll
+      for (int i = 0; i < kGpw; ++i) {
+        const int row = 16 * (gi0 + i) + l16;          // row inside the q-block
+        if (i < ng_w && q0 + row < n) {
+          float* dst = a.part + (static_cast<size_t>(it) * kQB + row) * HD + 4 * g;
+#pragma unroll
+          for (int ob = 0; ob < NO; ++ob) *reinterpret_cast<f32x4*>(dst + ob * 16) = o[i][ob];
+        }
+      }
+    }
+    __syncthreads();                       // the ring and s_pages are free for the next item
+    it = it_next;
+    item = item_next;
   }
 }
-
 template <typename T, int HD>
 hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                   const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,

@@ -196,7 +196,7 @@ __device__ __forceinline__ int row_to_user(const int32_t* offsets, int B, int r)
 struct WsHeader {            // first 256 bytes of the workspace
   int32_t status;            // hstu_device_code of this call
   int32_t n_items;           // attention work items
-  int32_t chunk_keys;        // keys per attention split
+  int32_t item_budget;       // attention cost units per work item (chunk sizing)
   int32_t counter;           // dynamic work-fetch counter
 };
 

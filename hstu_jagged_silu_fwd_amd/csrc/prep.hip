@@ -10,10 +10,14 @@
 // item per (user, q-block, head, chunk).
 // Because the attention has no softmax, the partial outputs of the chunks of
 // a row simply add; the norm kernel sums them in chunk order.
-// The chunk length bound ck is the smallest multiple of 32 keys (at least 128,
-// at most kMaxChunkKeys) that keeps the item count within the number of
-// resident attention workgroups; each entry's keys are then cut into
-// ceil(keys / ck) chunks of near-equal length (multiples of 32).
+// Chunks are sized by cost, not by keys: a 32-key step of an entry with G
+// query groups costs w(G) = max(kStepFloor, G) units (the products grow with
+// G above a floor set by streaming the step's K and V).  With a budget of
+// `budget` units per item an entry's chunks are at most
+// clamp(budget / w, kMinSteps, kCapSteps) steps long, and the budget is the
+// smallest one found that keeps the item count within the number of resident
+// attention workgroups.  Each entry's keys are then cut into near-equal
+// chunks (multiples of 32 keys).
 #include "common.h"
 
 namespace hstu {
@@ -22,7 +26,12 @@ namespace {
 constexpr int kPrepThreads = 256;
 constexpr int kPrepWaves = kPrepThreads / kWave;
 constexpr int kStepKeys = 32;   // attention key step
-constexpr int kMinChunk = 128;  // one step for each of the four waves
+constexpr int kMinSteps = 4;    // shortest chunk: a step for each of up to four phases
+constexpr int kCapSteps = kMaxChunkKeys / kStepKeys;
+constexpr int kStepFloor = 6;   // step cost floor, in query groups
+constexpr int kMaxWeight = kQB / 16;
+constexpr int kWShift = 25;     // entry word: steps (bits 0..24) | weight << 25
+constexpr int kStepMask = (1 << kWShift) - 1;
 constexpr int kRowsPerThread = 4;
 constexpr int kRowsPerWg = kPrepThreads * kRowsPerThread;
 
@@ -43,14 +52,14 @@ struct PrepShared {
   int32_t off[kMaxUsers + 1];
   int32_t hist[kMaxUsers];
   int32_t qbb[kMaxUsers + 1];      // first q-block entry of each user
-  int32_t qbn[kMaxQBlocks];        // chunks per q-block entry
+  int32_t qbn[kMaxQBlocks];        // chunks per q-block entry (steps | weight while searching)
   int32_t qbf[kMaxQBlocks];        // first work item of each q-block entry
   int32_t qbu[kMaxQBlocks];        // user of each q-block entry
   int32_t pgp[kMaxUsers + 1];      // first flat page index of each user
-  int32_t cnt[16];                 // which candidate chunk lengths fit
+  int32_t cnt[16];                 // which candidate budgets fit
 };
 
-// Candidate chunk lengths tried at once by the chunk-length search.
+// Candidate budgets tried at once by the budget search.
 constexpr int kCand = 16;
 constexpr int kCandPerWave = kCand / kPrepWaves;
 
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     if (tid == 0) {
       hdr->status = s.err;
       hdr->n_items = 0;
-      hdr->chunk_keys = 0;
+      hdr->item_budget = 0;
       hdr->counter = 0;
     }
     return;
@@ -221,58 +230,81 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   if (tid == 0) s.qbb[B] = nqb;
   __syncthreads();
 
-  // 3. chunk length: the smallest multiple of kStepKeys, at least kMinChunk,
-  //    for which the items H * sum_e ceil(keys_e / L) fit the target (one
-  //    item per resident attention workgroup), capped at kMaxChunkKeys.
-  //    The entry key counts are parked in qbn meanwhile.
+  // 3. item budget (see the top of this file).  The entries' step counts and
+  //    weights are parked in qbn meanwhile.  With S = H * sum_e steps_e * w_e
+  //    an entry gets at least steps_e * w_e / budget chunks and, while no
+  //    chunk sits at its cap, fewer than steps_e * w_e / (budget - w_max) + 1,
+  //    so the smallest fitting budget lies in [S / target, S / (target -
+  //    H * nqb) + w_max]; kCand candidates spread over that window are tried
+  //    at once (four per wave) and the smallest that fits is taken (the top
+  //    one when none does, which can only happen through the cap).
+  int64_t part = 0;
   for (int e = tid; e < nqb; e += kPrepThreads) {
     const int u = entry_user(s.qbb, B, e);
     const int qb = e - s.qbb[u];
     const int n = s.off[u + 1] - s.off[u];
-    s.qbn[e] = s.hist[u] + min(n, (qb + 1) * kQB);
+    const int keys = s.hist[u] + min(n, (qb + 1) * kQB);
+    const int steps = (keys + kStepKeys - 1) / kStepKeys;
+    const int wt = max(kStepFloor, (min(kQB, n - qb * kQB) + 15) / 16);
+    s.qbn[e] = steps | (wt << kWShift);
     s.qbu[e] = u;
+    part += static_cast<int64_t>(steps) * wt;
   }
-  __syncthreads();
-  // H * sum_e ceil(k_e / L) lies in [H*K/L, H*K/L + H*nqb] for K = sum_e k_e,
-  // so the answer sits between L_lo = H*K/T and L_hi = H*K/(T - H*nqb); up to
-  // 16 candidates spread over that window are tried at once (four per wave).
-  int64_t part = 0;
-  for (int e = tid; e < nqb; e += kPrepThreads) part += s.qbn[e];
-  const int64_t hk = block_sum(part, s) * a.H;
+  const int64_t hs = block_sum(part, s) * a.H;       // ends with a barrier
   const int64_t target = a.target_items;
   const int64_t slack = static_cast<int64_t>(a.H) * nqb;
-  auto round_step = [](int64_t x) { return (x + kStepKeys - 1) / kStepKeys; };   // keys -> steps
-  int ck;
-  if (target <= slack) {
-    ck = kMaxChunkKeys;                      // every entry already has an item per head
-  } else {
-    const int64_t cap = kMaxChunkKeys / kStepKeys;
-    const int64_t lo_s = min(cap, max<int64_t>(kMinChunk / kStepKeys, round_step((hk + target - 1) / target)));
-    const int64_t hi_s = min(cap, max(lo_s, round_step((hk + (target - slack) - 1) / (target - slack))));
-    const int stride = static_cast<int>((hi_s - lo_s + kCand) / kCand);   // >= 1
-    auto count_items = [&](int steps) {        // wave-cooperative; the same in every lane
-      const int len = steps * kStepKeys;
-      int cnt = 0;
-      for (int e = lane; e < nqb; e += kWave) cnt += (s.qbn[e] + len - 1) / len;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
-      return static_cast<int64_t>(cnt) * a.H;
+  auto chunk_steps = [](int budget, int weight) { return min(kCapSteps, max(kMinSteps, budget / weight)); };
+  constexpr int kBudgetLo = kStepFloor * kMinSteps, kBudgetHi = kMaxWeight * kCapSteps;
+  int budget = kBudgetHi;
+  if (target > slack) {
+    const int64_t b_lo = min<int64_t>(kBudgetHi, max<int64_t>(kBudgetLo, (hs + target - 1) / target));
+    const int64_t b_hi = min<int64_t>(kBudgetHi, max(b_lo, (hs + (target - slack) - 1) / (target - slack) + kMaxWeight));
+    auto cand = [&](int k) {
+      return static_cast<int>(k == kCand - 1 ? b_hi : b_lo + (b_hi - b_lo) * k / (kCand - 1));
     };
-    for (int k = w * kCandPerWave; k < (w + 1) * kCandPerWave; ++k) {
-      const int cand = static_cast<int>(min<int64_t>(lo_s + static_cast<int64_t>(k) * stride, hi_s));
-      const bool fits = cand == hi_s || count_items(cand) <= target;
-      if (lane == 0) s.cnt[k] = fits ? 1 : 0;
+    // whether each of this wave's kCandPerWave budgets fits the target; the
+    // wave counts them in one pass and reduces them together, so that the
+    // shuffle latencies overlap.  Per-lane counts saturate at 2^24 (far
+    // above any target), which keeps the lane sums inside int32.
+    int bud[kCandPerWave], cnt[kCandPerWave];
+#pragma unroll
+    for (int k = 0; k < kCandPerWave; ++k) {
+      bud[k] = cand(w * kCandPerWave + k);
+      cnt[k] = 0;
+    }
+    for (int e = lane; e < nqb; e += kWave) {
+      const int v = s.qbn[e];
+      const int steps = v & kStepMask, wt = v >> kWShift;
+#pragma unroll
+      for (int k = 0; k < kCandPerWave; ++k) {
+        const int L = chunk_steps(bud[k], wt);
+        cnt[k] = min(cnt[k] + (steps + L - 1) / L, 1 << 24);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int k = 0; k < kCandPerWave; ++k) cnt[k] += __shfl_xor(cnt[k], o, kWave);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < kCandPerWave; ++k) {
+        const int kk = w * kCandPerWave + k;
+        s.cnt[kk] = (kk == kCand - 1 || static_cast<int64_t>(cnt[k]) * a.H <= target) ? 1 : 0;
+      }
     }
     __syncthreads();
     int j = kCand - 1;
     for (int k = kCand - 1; k >= 0; --k)
       if (s.cnt[k]) j = k;
-    ck = static_cast<int>(min<int64_t>(lo_s + static_cast<int64_t>(j) * stride, hi_s)) * kStepKeys;
+    budget = cand(j);
   }
 
   // 4. chunks per entry, then first item of each entry
+  __syncthreads();                           // every wave is done counting
   for (int e = tid; e < nqb; e += kPrepThreads) {
-    const int nch = (s.qbn[e] + ck - 1) / ck;
+    const int v = s.qbn[e];
+    const int L = chunk_steps(budget, v >> kWShift);
+    const int nch = ((v & kStepMask) + L - 1) / L;
     s.qbn[e] = nch;
     s.qbf[e] = nch * a.H;
   }
@@ -282,7 +314,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     if (tid == 0) {
       hdr->status = HSTU_DEV_CAPACITY;
       hdr->n_items = 0;
-      hdr->chunk_keys = 0;
+      hdr->item_budget = 0;
       hdr->counter = 0;
     }
     return;
@@ -306,7 +338,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     const int c = s.hist[u];
     const int keys = c + min(n, (qb + 1) * kQB);
     // the entry's keys are cut into nch near-equal chunks (multiples of a
-    // step); csz <= ck, so (nch - 1) * csz < keys and no chunk is empty
+    // step); csz is at most the entry's chunk bound, so (nch - 1) * csz <
+    // keys and no chunk is empty
     const int csz = ((keys + nch - 1) / nch + kStepKeys - 1) / kStepKeys * kStepKeys;
     const int k_lo = kc * csz;
     AttnItem it;
@@ -319,7 +352,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   if (tid == 0) {
     hdr->status = 0;
     hdr->n_items = static_cast<int32_t>(n_items);
-    hdr->chunk_keys = static_cast<int32_t>(ck);
+    hdr->item_budget = budget;
     hdr->counter = 0;
   }
 }

@@ -1,0 +1,267 @@
+"""GPU tests of the paged KV indexing and of the layer's exact properties.
+
+* kv_pages_append places every element exactly where the oracle's scatter
+  does and touches nothing else (canary-filled pools, bit-exact), for both
+  element types and every supported page size, with ragged users (no new
+  rows, no history, histories ending on and off page boundaries).
+* The projection's fused append writes the same pool elements as the
+  standalone append given the same rows (whole pools compared bit for bit).
+* Page-order permutation invariance, run-to-run determinism and the K = 0 /
+  zero-bias closed form (Y == 0 exactly) are bit-exact properties of the
+  layer call.
+* Cached history == full recompute and batched == one user at a time hold
+  to the bf16 tolerance (the key chunking differs between the runs).
+* Metadata errors are reported through the device status word and leave y
+  and both pools untouched; an empty call is a no-op.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import stack_from_workload, tol_check, to_np
+from hstu_jagged_silu_fwd_amd import _lib
+from oracle import paging
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+CANARY = 3.140625            # exactly representable in bf16 and fp32
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy()
+    return t.view(torch.int32).cpu().numpy()
+
+
+def append_case(rng, B, ps, H, d):
+    """Ragged users: (hist, new) pairs covering empty, page-aligned and
+    unaligned cases, and a page table of distinct random pool pages."""
+    hist = np.array([[0, ps - 1, ps, 3 * ps + 5, 0, 2 * ps][u % 6] for u in range(B)], np.int32)
+    new = np.array([[1, 0, ps, 2 * ps + 3, 5, ps - 1][u % 6] for u in range(B)], np.int32)
+    maxp = int(np.max((hist + new + ps - 1) // ps)) + 1
+    P = B * maxp + 7
+    pt = rng.permutation(P)[:B * maxp].reshape(B, maxp).astype(np.int32)
+    return hist, new, pt, P
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ps", [16, 32, 64, 128])
+def test_append_bit_exact_with_canaries(dtype, ps):
+    print(f"case append {dtype} ps={ps}", flush=True)
+    rng = np.random.default_rng(ps)
+    B, H, d = 6, 2, 32 if dtype == "f32" else 64
+    D = H * d
+    hist, new, pt, P = append_case(rng, B, ps, H, d)
+    T = int(new.sum())
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = torch.device("cuda")
+    k_new = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(dev, tdt)
+    v_new = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(dev, tdt)
+    k_pool = torch.full((P, H, ps, d), CANARY, dtype=tdt, device=dev)
+    v_pool = torch.full((P, H, d, ps), CANARY, dtype=tdt, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    off = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    desc = _lib.make_desc(num_users=B, num_heads=H, head_dim=d, page_size=ps, max_pages_per_user=pt.shape[1],
+                          num_pool_pages=P, total_new=T, pos_buckets=1, pos_mbits=0, attn_scale=1.0,
+                          norm_eps=1e-6, dtype=dtype)
+    _lib.kv_pages_append(desc, k_new, v_new, torch.from_numpy(off).to(dev), torch.from_numpy(hist).to(dev),
+                         torch.from_numpy(pt).to(dev), k_pool, v_pool, status)
+    assert _lib.read_device_status(status) == 0
+    kb = np.full((P, H, ps, d), 0, dtype=bits(k_pool).dtype)
+    vb = np.full((P, H, d, ps), 0, dtype=kb.dtype)
+    kb[...] = bits(torch.full((1,), CANARY, dtype=tdt))[0]
+    vb[...] = kb.flat[0]
+    paging.append_scatter(kb, vb, bits(k_new), bits(v_new), new, hist, pt, ps, H)
+    assert np.array_equal(bits(k_pool), kb), "K pool differs from the oracle scatter"
+    assert np.array_equal(bits(v_pool), vb), "V pool differs from the oracle scatter"
+    touched = paging.touched_slots(new, hist, pt, ps)
+    assert len(touched) == T                      # distinct slots: no row overwrote another
+
+
+def small_wl(seed=0, **over):
+    base = dict(B=4, hist=("uniform", 100, 700), new=("uniform", 1, 300), layers=1, pool_pages=512)
+    base.update(over)
+    return make_workload(3, seed=seed, **base)
+
+
+def layer_call(st, wl, x_np=None, pt=None, y_fill=None):
+    dev = st.device
+    x = torch.from_numpy(wl.x0 if x_np is None else x_np).to(dev, st.tdtype)
+    y = torch.empty_like(x) if y_fill is None else torch.full_like(x, y_fill)
+    if pt is not None:
+        st.layers[0]["page_table"] = torch.from_numpy(pt).to(dev)
+    st.layer(0, x, torch.from_numpy(wl.new_offsets).to(dev), torch.from_numpy(wl.hist_len).to(dev), y)
+    return y
+
+
+def test_fused_append_equals_standalone_append():
+    print("case fused append == kv_pages_append", flush=True)
+    wl = small_wl(seed=1)
+    st = stack_from_workload(wl, pool_fill=CANARY)
+    layer_call(st, wl)
+    assert st.read_status() == 0
+    k_after, v_after = bits(st.k_pool), bits(st.v_pool)
+    # rows the projection appended, read back by position through the table
+    pt = wl.layer(0).page_table
+    rows_k, rows_v = [], []
+    for u in range(wl.B):
+        K, V = paging.gather_user(k_after, v_after, pt, u, int(wl.hist_len[u] + wl.new_len[u]), wl.page_size, wl.H)
+        rows_k.append(K[wl.hist_len[u]:])
+        rows_v.append(V[wl.hist_len[u]:])
+    k_new = torch.from_numpy(np.concatenate(rows_k)).view(torch.bfloat16).to(st.device)
+    v_new = torch.from_numpy(np.concatenate(rows_v)).view(torch.bfloat16).to(st.device)
+    st2 = stack_from_workload(wl, pool_fill=CANARY)          # history only
+    st2.append(0, k_new, v_new, wl.new_offsets, wl.hist_len)
+    assert int(st2.status.cpu()[0]) == 0
+    assert np.array_equal(bits(st2.k_pool), k_after)
+    assert np.array_equal(bits(st2.v_pool), v_after)
+
+
+def test_page_permutation_invariance_bit_exact():
+    print("case page permutation invariance", flush=True)
+    wl = small_wl(seed=2)
+    st = stack_from_workload(wl)
+    y0 = layer_call(st, wl)
+    assert st.read_status() == 0
+    # a second pool whose pages hold the same logical contents at other ids
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(wl.num_pool_pages).astype(np.int64)
+    pt = wl.layer(0).page_table
+    pt2 = np.where(pt >= 0, perm[np.maximum(pt, 0)], -1).astype(np.int32)
+    st2 = stack_from_workload(wl)
+    inv = torch.from_numpy(np.argsort(perm)).to(st.device)
+    st2.k_pool.copy_(st.k_pool[inv])       # page perm[i] of the new pool = page i of the old
+    st2.v_pool.copy_(st.v_pool[inv])
+    y1 = layer_call(st2, wl, pt=pt2)
+    assert st2.read_status() == 0
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_determinism_bit_exact():
+    print("case determinism", flush=True)
+    wl = small_wl(seed=3, B=6)
+    st = stack_from_workload(wl)
+    y0 = layer_call(st, wl)
+    y1 = layer_call(st, wl)
+    assert st.read_status() == 0
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_zero_keys_zero_bias_gives_exact_zero():
+    print("case K = 0 and zero bias -> Y = 0", flush=True)
+    wl = small_wl(seed=4)
+    st = stack_from_workload(wl)
+    D = wl.D
+    li = wl.layer(0)
+    w1t = li.w1t.copy()
+    w1t[3 * D:4 * D, :] = 0.0                      # the K block of W1 (out x in layout)
+    st.set_layer(0, w1t=w1t, w2t=li.w2t, pos_bias=np.zeros_like(li.pos_bias), page_table=li.page_table)
+    zeros = [np.zeros_like(k) for k in li.hist_k]
+    hoff = np.concatenate([[0], np.cumsum(wl.hist_len)]).astype(np.int32)
+    st.append(0, np.concatenate(zeros), np.concatenate(li.hist_v), hoff, np.zeros(wl.B, np.int32))
+    y = layer_call(st, wl, y_fill=CANARY)
+    assert st.read_status() == 0
+    assert torch.count_nonzero(y.float()).item() == 0
+
+
+def test_cached_history_equals_full_recompute():
+    print("case cached history == full recompute", flush=True)
+    wl = small_wl(seed=5, B=3, hist=("uniform", 200, 600), new=("uniform", 20, 200))
+    # full recompute: every position is a new row (no history), x for the
+    # history positions drawn from the same generator stream
+    rng = np.random.default_rng(11)
+    L = wl.hist_len + wl.new_len
+    xs, off = [], wl.new_offsets
+    for u in range(wl.B):
+        xh = rng.standard_normal((int(wl.hist_len[u]), wl.D)).astype(np.float32)
+        xs.append(np.concatenate([xh, wl.x0[off[u]:off[u + 1]]]))
+    x_full = torch.from_numpy(np.concatenate(xs)).to("cuda", torch.bfloat16)
+    off_full = np.concatenate([[0], np.cumsum(L)]).astype(np.int32)
+    st = stack_from_workload(wl)                    # same weights and page table
+    dev = st.device
+    y_full = torch.empty_like(x_full)
+    st.layer(0, x_full, torch.from_numpy(off_full).to(dev), torch.zeros(wl.B, dtype=torch.int32, device=dev), y_full)
+    assert st.read_status() == 0
+    # the pool now holds the recomputed history K/V; run only the new rows
+    y_cached = layer_call(st, wl)
+    assert st.read_status() == 0
+    sel = np.concatenate([np.arange(off_full[u] + wl.hist_len[u], off_full[u + 1]) for u in range(wl.B)])
+    tol_check(to_np(y_cached), to_np(y_full)[sel], "bf16", "cached vs recompute")
+
+
+def test_batched_equals_one_user_at_a_time():
+    print("case batched == per user", flush=True)
+    wl = small_wl(seed=6, B=5)
+    st = stack_from_workload(wl)
+    y = to_np(layer_call(st, wl))
+    assert st.read_status() == 0
+    dev = st.device
+    off = wl.new_offsets
+    for u in range(wl.B):
+        n = int(wl.new_len[u])
+        x = torch.from_numpy(wl.x0[off[u]:off[u + 1]]).to(dev, torch.bfloat16)
+        yu = torch.empty_like(x)
+        st1 = stack_from_workload(wl)
+        st1.B = 1
+        st1.common["num_users"] = 1
+        st1.layers[0]["page_table"] = st.layers[0]["page_table"][u:u + 1].contiguous()
+        st1.k_pool, st1.v_pool = st.k_pool, st.v_pool
+        st1.layer(0, x, torch.tensor([0, n], dtype=torch.int32, device=dev),
+                  torch.tensor([int(wl.hist_len[u])], dtype=torch.int32, device=dev), yu)
+        assert st1.read_status() == 0
+        tol_check(to_np(yu), y[off[u]:off[u + 1]], "bf16", f"user {u}")
+
+
+@pytest.mark.parametrize("kind", ["bad_page", "capacity", "bad_offsets", "negative_hist"])
+def test_device_errors_leave_outputs_untouched(kind):
+    print(f"case device error {kind}", flush=True)
+    wl = small_wl(seed=7)
+    st = stack_from_workload(wl)
+    dev = st.device
+    pt = wl.layer(0).page_table.copy()
+    off = wl.new_offsets.copy()
+    hist = wl.hist_len.copy()
+    want = {"bad_page": 4, "capacity": 3, "bad_offsets": 1, "negative_hist": 2}[kind]
+    if kind == "bad_page":
+        u = 1
+        pt[u, (hist[u] + wl.new_len[u] - 1) // wl.page_size] = wl.num_pool_pages   # last page in use
+    elif kind == "capacity":
+        hist[0] = pt.shape[1] * wl.page_size                                         # no room left
+    elif kind == "bad_offsets":
+        off[-1] = off[-1] - 1                  # the offsets no longer end at total_new
+    else:
+        hist[3] = -1
+    k0, v0 = bits(st.k_pool).copy(), bits(st.v_pool).copy()
+    x = torch.from_numpy(wl.x0).to(dev, torch.bfloat16)
+    y = torch.full_like(x, CANARY)
+    st.layers[0]["page_table"] = torch.from_numpy(pt).to(dev)
+    st.layer(0, x, torch.from_numpy(off).to(dev), torch.from_numpy(hist).to(dev), y)
+    assert st.read_status() == want
+    assert torch.all(y.float() == CANARY).item()
+    assert np.array_equal(bits(st.k_pool), k0) and np.array_equal(bits(st.v_pool), v0)
+
+
+def test_empty_call_is_a_no_op():
+    print("case empty call", flush=True)
+    wl = small_wl(seed=8)
+    st = stack_from_workload(wl)
+    dev = st.device
+    k0 = bits(st.k_pool).copy()
+    x = torch.empty((0, wl.D), dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    st.layer(0, x, torch.zeros(wl.B + 1, dtype=torch.int32, device=dev),
+             torch.from_numpy(wl.hist_len).to(dev), y)
+    assert st.read_status() == 0
+    assert np.array_equal(bits(st.k_pool), k0)
+
+
+def test_users_without_new_rows_or_history():
+    print("case users with n = 0 or c = 0", flush=True)
+    wl = make_workload(3, seed=9, B=5, hist=("fixed", [0, 300, 0, 45, 700]), new=("fixed", [7, 0, 1, 64, 0]),
+                       layers=1, pool_pages=512)
+    st = stack_from_workload(wl)
+    y = layer_call(st, wl)
+    assert st.read_status() == 0
+    from gpu_util import oracle_layer
+    tol_check(to_np(y), oracle_layer(wl, 0)["y"], "bf16", "ragged users")

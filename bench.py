@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "HSTU layer new-tokens/sec at batch 8 (paged KV hit); % bf16 MFMA peak, HBM GB/s"
-WORKLOAD_CFG = 3
+WORKLOAD = "3layer-bf16-b8-paged-kv-hit"    # workloads.B8_KV_HIT
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 EPS = 1e-6
@@ -63,7 +63,7 @@ class Bench:
         self.hip = _lib.hip_runtime()
         self.R = args.instances
         B = 8
-        self.wl = wl = make_workload(WORKLOAD_CFG, seed=args.seed, B=B * self.R)
+        self.wl = wl = make_workload(WORKLOAD, seed=args.seed, B=B * self.R)
         self.L, self.D, self.H, self.d = wl.layers, wl.D, wl.H, wl.d
         dev = torch.device("cuda")
         bf = torch.bfloat16
@@ -238,7 +238,7 @@ def main():
     out = dict(metric=METRIC, value=value, unit="new tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=1e3 * wall / args.steps, higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-               config=dict(workload=b.wl.cfg["name"], layers=b.L, batch=8, hidden=b.D, heads=b.H,
+               config=dict(workload=b.wl.name, layers=b.L, batch=8, hidden=b.D, heads=b.H,
                            head_dim=b.d, page_size=b.wl.page_size, pool_pages=b.wl.num_pool_pages,
                            hist="U{256..4096}", new="U{16..256}", instances=b.R,
                            new_tokens_per_step=tokens / args.steps,

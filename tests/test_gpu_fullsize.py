@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from gpu_util import oracle_layer, stack_from_workload, to_np, tol_check, user_rows
-from workloads import make_workload
+from workloads import B8_KV_HIT, B8_KV_HIT_LONG, B8_RECOMPUTE, B64_SERVING, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -50,30 +50,30 @@ def pool_rows(wl, st, users, l=0):
     return to_np(k), to_np(v)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_layer0(cfg):
-    print(f"case full cfg{cfg} layer 0", flush=True)
-    wl = make_workload(cfg, seed=0, layers=1)
+@pytest.mark.parametrize("name", [B8_RECOMPUTE, B8_KV_HIT, B8_KV_HIT_LONG])
+def test_full_layer0(name):
+    print(f"case full {name} layer 0", flush=True)
+    wl = make_workload(name, seed=0, layers=1)
     st = stack_from_workload(wl)
     y = run_layer(wl, st)
     ref = oracle_layer(wl, 0)
-    tol_check(to_np(y), ref["y"], "bf16", f"cfg{cfg} full y")
+    tol_check(to_np(y), ref["y"], "bf16", f"{name} full y")
     users = list(range(wl.B))
     k, v = pool_rows(wl, st, users)
-    tol_check(k, ref["k"], "bf16", f"cfg{cfg} full appended K")
-    tol_check(v, ref["v"], "bf16", f"cfg{cfg} full appended V")
+    tol_check(k, ref["k"], "bf16", f"{name} full appended K")
+    tol_check(v, ref["v"], "bf16", f"{name} full appended V")
 
 
-def test_full_cfg5_sampled_users():
-    print("case full cfg5 layer 0, sampled users", flush=True)
-    wl = make_workload(5, seed=0, layers=1)
+def test_full_serving_sampled_users():
+    print("case full serving workload layer 0, sampled users", flush=True)
+    wl = make_workload(B64_SERVING, seed=0, layers=1)
     users = sorted({0, int(np.argmax(wl.hist_len)), int(np.argmin(wl.new_len)),
                     int(np.argmax(wl.new_len)), wl.B - 1})
     st = stack_from_workload(wl)
     y = run_layer(wl, st)
     ref = oracle_layer(wl, 0, users=users)
     rows = user_rows(wl, users)
-    tol_check(to_np(y)[rows], ref["y"], "bf16", f"cfg5 full users {users} y")
+    tol_check(to_np(y)[rows], ref["y"], "bf16", f"serving full users {users} y")
     k, v = pool_rows(wl, st, users)
-    tol_check(k, ref["k"], "bf16", "cfg5 appended K")
-    tol_check(v, ref["v"], "bf16", "cfg5 appended V")
+    tol_check(k, ref["k"], "bf16", "serving appended K")
+    tol_check(v, ref["v"], "bf16", "serving appended V")

@@ -21,7 +21,7 @@ import torch
 from gpu_util import stack_from_workload, tol_check, to_np
 from hstu_jagged_silu_fwd_amd import _lib
 from oracle import paging
-from workloads import make_workload
+from workloads import B8_KV_HIT, make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +82,7 @@ def test_append_bit_exact_with_canaries(dtype, ps):
 def small_wl(seed=0, **over):
     base = dict(B=4, hist=("uniform", 100, 700), new=("uniform", 1, 300), layers=1, pool_pages=512)
     base.update(over)
-    return make_workload(3, seed=seed, **base)
+    return make_workload(B8_KV_HIT, seed=seed, **base)
 
 
 def layer_call(st, wl, x_np=None, pt=None, y_fill=None):
@@ -258,7 +258,7 @@ def test_empty_call_is_a_no_op():
 
 def test_users_without_new_rows_or_history():
     print("case users with n = 0 or c = 0", flush=True)
-    wl = make_workload(3, seed=9, B=5, hist=("fixed", [0, 300, 0, 45, 700]), new=("fixed", [7, 0, 1, 64, 0]),
+    wl = make_workload(B8_KV_HIT, seed=9, B=5, hist=("fixed", [0, 300, 0, 45, 700]), new=("fixed", [7, 0, 1, 64, 0]),
                        layers=1, pool_pages=512)
     st = stack_from_workload(wl)
     y = layer_call(st, wl)

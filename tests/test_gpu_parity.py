@@ -10,15 +10,15 @@ import torch
 
 from gpu_util import oracle_layer, stack_from_workload, to_np, tol_check
 from oracle import layer as olayer
-from workloads import make_workload
+from workloads import B8_KV_HIT, B8_KV_HIT_LONG, B8_RECOMPUTE, B64_SERVING, TINY_FP32, make_workload
 
 pytestmark = pytest.mark.gpu
 
 REDUCED = {
-    2: dict(B=3, new=("uniform", 256, 700), layers=1),
-    3: dict(B=4, hist=("uniform", 256, 1500), new=("uniform", 16, 256), layers=1, pool_pages=4096),
-    4: dict(B=2, hist=("uniform", 4096, 6000), layers=1, pool_pages=1024),
-    5: dict(B=6, hist=("zipf", 1.2, 32, 3000), new=("uniform", 1, 512), layers=1, pool_pages=4096,
+    B8_RECOMPUTE: dict(B=3, new=("uniform", 256, 700), layers=1),
+    B8_KV_HIT: dict(B=4, hist=("uniform", 256, 1500), new=("uniform", 16, 256), layers=1, pool_pages=4096),
+    B8_KV_HIT_LONG: dict(B=2, hist=("uniform", 4096, 6000), layers=1, pool_pages=1024),
+    B64_SERVING: dict(B=6, hist=("zipf", 1.2, 32, 3000), new=("uniform", 1, 512), layers=1, pool_pages=4096,
             miss_frac=0.34),
 }
 
@@ -39,38 +39,38 @@ def run_layer(wl, st, l=0):
     return y
 
 
-def test_cfg1_fp32_full():
-    print("case cfg1 fp32 full", flush=True)
-    wl = make_workload(1, seed=0)
+def test_tiny_fp32_full():
+    print("case tiny fp32 full", flush=True)
+    wl = make_workload(TINY_FP32, seed=0)
     st = stack_from_workload(wl)
     y = run_layer(wl, st)
     ref = oracle_layer(wl, 0)["y"]
-    tol_check(to_np(y), ref, "f32", "cfg1")
+    tol_check(to_np(y), ref, "f32", "tiny fp32")
 
 
 @pytest.mark.parametrize("seed", [0, 1])
-def test_cfg1_fp32_seeds_with_history(seed):
+def test_tiny_fp32_seeds_with_history(seed):
     # The tiny fp32 model with a cached history prefix and a random pool.
-    print(f"case cfg1-with-history seed={seed}", flush=True)
-    wl = make_workload(1, seed=seed, hist=("uniform", 5, 90), new=("uniform", 1, 150), B=5,
+    print(f"case tiny fp32 with history seed={seed}", flush=True)
+    wl = make_workload(TINY_FP32, seed=seed, hist=("uniform", 5, 90), new=("uniform", 1, 150), B=5,
                        pool_pages=64, pos_buckets=32)
     st = stack_from_workload(wl)
     y = run_layer(wl, st)
-    tol_check(to_np(y), oracle_layer(wl, 0)["y"], "f32", f"cfg1h seed {seed}")
+    tol_check(to_np(y), oracle_layer(wl, 0)["y"], "f32", f"tiny fp32 with history seed {seed}")
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_reduced_bf16_layer(cfg):
-    print(f"case reduced cfg{cfg}", flush=True)
-    wl = make_workload(cfg, seed=0, **REDUCED[cfg])
+@pytest.mark.parametrize("name", [B8_RECOMPUTE, B8_KV_HIT, B8_KV_HIT_LONG, B64_SERVING])
+def test_reduced_bf16_layer(name):
+    print(f"case reduced {name}", flush=True)
+    wl = make_workload(name, seed=0, **REDUCED[name])
     st = stack_from_workload(wl)
     y = run_layer(wl, st)
-    tol_check(to_np(y), oracle_layer(wl, 0)["y"], "bf16", f"cfg{cfg} reduced")
+    tol_check(to_np(y), oracle_layer(wl, 0)["y"], "bf16", f"{name} reduced")
 
 
-def test_reduced_cfg3_stack():
-    print("case reduced cfg3 3-layer stack", flush=True)
-    wl = make_workload(3, seed=2, B=3, hist=("uniform", 256, 900), new=("uniform", 16, 256),
+def test_reduced_kv_hit_stack():
+    print("case reduced 3-layer paged-KV-hit stack", flush=True)
+    wl = make_workload(B8_KV_HIT, seed=2, B=3, hist=("uniform", 256, 900), new=("uniform", 16, 256),
                        pool_pages=4096)
     st = stack_from_workload(wl)
     ys = st.forward(wl.x0, wl.new_offsets, wl.hist_len, return_all=True)
@@ -80,15 +80,15 @@ def test_reduced_cfg3_stack():
     refs = olayer.stack_forward(wl.x0, wl.new_len, wl.hist_len, layers, wl.attn_scale, 1e-6, wl.H,
                                 wl.pos_mbits)
     for l in range(wl.layers):
-        tol_check(to_np(ys[l]), refs[l], "bf16", f"cfg3 stack layer {l}")
+        tol_check(to_np(ys[l]), refs[l], "bf16", f"kv-hit stack layer {l}")
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_reduced_bf16_other_layers_fed_x0(cfg):
+@pytest.mark.parametrize("name", [B8_RECOMPUTE, B8_KV_HIT])
+def test_reduced_bf16_other_layers_fed_x0(name):
     # Each layer's own weights/history on the generator's X (per-layer parity).
-    wl = make_workload(cfg, seed=3, **dict(REDUCED[cfg], layers=3))
+    wl = make_workload(name, seed=3, **dict(REDUCED[name], layers=3))
     for l in (1, 2):
-        print(f"case reduced cfg{cfg} layer {l}", flush=True)
+        print(f"case reduced {name} layer {l}", flush=True)
         st = stack_from_workload(wl, layers=[l])
         y = run_layer(wl, st)
-        tol_check(to_np(y), oracle_layer(wl, l)["y"], "bf16", f"cfg{cfg} layer {l}")
+        tol_check(to_np(y), oracle_layer(wl, l)["y"], "bf16", f"{name} layer {l}")

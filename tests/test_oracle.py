@@ -11,7 +11,7 @@ import pytest
 
 from oracle import brute, layer, paging
 from oracle.buckets import bucket
-from workloads import make_workload
+from workloads import B8_KV_HIT, CONFIGS, TINY_FP32, make_workload
 
 EPS = 1e-6
 
@@ -69,7 +69,7 @@ def test_brute_matches_oracle_edge_shapes(seed, ts):
 
 
 def test_brute_matches_oracle_tiny_workload():
-    wl = make_workload(1, seed=0)
+    wl = make_workload(TINY_FP32, seed=0)
     li = wl.layer(0)
     kw = dict(x=wl.x0, new_len=wl.new_len, hist_len=wl.hist_len,
               hist_k=li.hist_k, hist_v=li.hist_v, w1=li.w1, w2=li.w2,
@@ -259,8 +259,8 @@ def test_paging_roundtrip_and_permutation_invariance():
 
 
 def test_workload_generator_structure():
-    for cid in (1, 2, 3, 4, 5):
-        wl = make_workload(cid, seed=0, B=4, layers=2) if cid != 1 else make_workload(1)
+    for name in CONFIGS:
+        wl = make_workload(name, seed=0, B=4, layers=2) if name != TINY_FP32 else make_workload(TINY_FP32)
         T = wl.T
         assert wl.x0.shape == (T, wl.D)
         assert wl.new_offsets[0] == 0 and np.all(np.diff(wl.new_offsets) >= 0)
@@ -276,6 +276,6 @@ def test_workload_generator_structure():
         if wl.dtype == "bf16":
             bits = wl.x0.view(np.uint32)
             assert np.all((bits & 0xFFFF) == 0)
-    a = make_workload(3, seed=5, B=3)
-    b = make_workload(3, seed=5, B=3)
+    a = make_workload(B8_KV_HIT, seed=5, B=3)
+    b = make_workload(B8_KV_HIT, seed=5, B=3)
     assert np.array_equal(a.x0, b.x0) and np.array_equal(a.layer(1).w1, b.layer(1).w1)

@@ -20,7 +20,8 @@ from typing import Dict, List, Optional
 import numpy as np
 
 # ---------------------------------------------------------------------------
-# Workload table.  Length specs:
+# Workload table, keyed by the workload's name.  `stream` is the first
+# entropy word of its seed sequence.  Length specs:
 #   ("fixed", [n0, n1, ...])  one value per user
 #   ("const", v)              every user
 #   ("uniform", lo, hi)       integers uniform in [lo, hi] inclusive
@@ -29,33 +30,39 @@ import numpy as np
 # bucket rule used by the relative-bias tables (fixed per workload).
 # attn_scale is 1/N with N the workload's maximum total sequence length.
 # ---------------------------------------------------------------------------
-CONFIGS: Dict[int, dict] = {
-    1: dict(
-        name="tiny-fp32-1layer-nocache", dtype="f32", layers=1, B=2,
+TINY_FP32 = "tiny-fp32-1layer-nocache"
+B8_RECOMPUTE = "3layer-bf16-b8-full-recompute"
+B8_KV_HIT = "3layer-bf16-b8-paged-kv-hit"
+B8_KV_HIT_LONG = "8layer-bf16-b8-paged-kv-hit-long"
+B64_SERVING = "8layer-bf16-b64-mixed-hit-serving"
+
+CONFIGS: Dict[str, dict] = {
+    TINY_FP32: dict(
+        stream=1, dtype="f32", layers=1, B=2,
         D=64, H=2, d=32, hist=("const", 0), new=("fixed", [37, 64]),
         page_size=32, pool_pages=None, pos_buckets=32, pos_mbits=3,
         ts_buckets=0, ts_mbits=0, attn_scale=1.0 / 64, miss_frac=0.0,
     ),
-    2: dict(
-        name="3layer-bf16-b8-full-recompute", dtype="bf16", layers=3, B=8,
+    B8_RECOMPUTE: dict(
+        stream=2, dtype="bf16", layers=3, B=8,
         D=512, H=4, d=128, hist=("const", 0), new=("uniform", 256, 4096),
         page_size=32, pool_pages=None, pos_buckets=128, pos_mbits=3,
         ts_buckets=0, ts_mbits=0, attn_scale=1.0 / 4096, miss_frac=0.0,
     ),
-    3: dict(
-        name="3layer-bf16-b8-paged-kv-hit", dtype="bf16", layers=3, B=8,
+    B8_KV_HIT: dict(
+        stream=3, dtype="bf16", layers=3, B=8,
         D=512, H=4, d=128, hist=("uniform", 256, 4096), new=("uniform", 16, 256),
         page_size=32, pool_pages=1 << 16, pos_buckets=128, pos_mbits=3,
         ts_buckets=0, ts_mbits=0, attn_scale=1.0 / 4096, miss_frac=0.0,
     ),
-    4: dict(
-        name="8layer-bf16-b8-paged-kv-hit-long", dtype="bf16", layers=8, B=8,
+    B8_KV_HIT_LONG: dict(
+        stream=4, dtype="bf16", layers=8, B=8,
         D=512, H=4, d=128, hist=("uniform", 4096, 16384), new=("const", 64),
         page_size=64, pool_pages=1 << 16, pos_buckets=256, pos_mbits=4,
         ts_buckets=0, ts_mbits=0, attn_scale=1.0 / 16448, miss_frac=0.0,
     ),
-    5: dict(
-        name="8layer-bf16-b64-mixed-hit-serving", dtype="bf16", layers=8, B=64,
+    B64_SERVING: dict(
+        stream=5, dtype="bf16", layers=8, B=64,
         D=1024, H=8, d=128, hist=("zipf", 1.2, 32, 32768), new=("uniform", 1, 512),
         page_size=32, pool_pages=1 << 17, pos_buckets=256, pos_mbits=4,
         ts_buckets=64, ts_mbits=2, attn_scale=1.0 / 33280, miss_frac=0.3,
@@ -120,7 +127,7 @@ class LayerInputs:
 
 @dataclasses.dataclass
 class Workload:
-    cfg_id: int
+    name: str
     cfg: dict
     seed: int
     B: int
@@ -221,12 +228,12 @@ class Workload:
                            hist_k=hist_k, hist_v=hist_v, page_table=pt)
 
 
-def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
-    """Draw workload `cfg_id` (1..5) from `seed`.  Keyword overrides replace
+def make_workload(name: str, seed: int = 0, **over) -> Workload:
+    """Draw workload `name` (a key of CONFIGS) from `seed`.  Keyword overrides replace
     entries of the workload table (e.g. B=3, hist=("uniform", 40, 90),
     layers=1, pool_pages=4096, max_pages=...) so that tests can run the same
     distributions at sizes the oracle finishes quickly."""
-    cfg = dict(CONFIGS[cfg_id])
+    cfg = dict(CONFIGS[name])
     max_pages_over = over.pop("max_pages", None)
     for k, v in over.items():
         if k not in cfg:
@@ -234,7 +241,7 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
         cfg[k] = v
     B, D, H, d = cfg["B"], cfg["D"], cfg["H"], cfg["d"]
     assert D == H * d
-    ss = np.random.SeedSequence([cfg_id, seed])
+    ss = np.random.SeedSequence([cfg["stream"], seed])
     s_len, s_x, s_ts, s_miss, s_pages, s_layers = ss.spawn(6)
     rng_len = np.random.default_rng(s_len)
     hist = _draw_lengths(rng_len, cfg["hist"], B)
@@ -274,7 +281,7 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
         if need > P:
             raise ValueError(f"pool of {P} pages too small for {need} pages")
         perm = np.random.default_rng(s_pages).permutation(P).astype(np.int32)
-    return Workload(cfg_id=cfg_id, cfg=cfg, seed=seed, B=B, D=D, H=H, d=d,
+    return Workload(name=name, cfg=cfg, seed=seed, B=B, D=D, H=H, d=d,
                     dtype=cfg["dtype"], layers=cfg["layers"], page_size=ps,
                     hist_len=hist, new_len=new, new_offsets=offsets, miss=miss,
                     x0=x0, timestamps=timestamps, max_pages=max_pages,
@@ -282,9 +289,9 @@ def make_workload(cfg_id: int, seed: int = 0, **over) -> Workload:
                     _page_perm=perm)
 
 
-def expected_sizes(cfg_id: int) -> dict:
+def expected_sizes(name: str) -> dict:
     """Closed-form expected lengths of a workload (for documentation only)."""
-    cfg = CONFIGS[cfg_id]
+    cfg = CONFIGS[name]
 
     def mean(spec):
         if spec[0] == "const":

@@ -15,7 +15,7 @@ constexpr int kAttnWgPerCu = 1;     // resident attention workgroups per CU
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-  size_t row_user, row_loc, qb_base, qb_first, qb_nch, items, q, u, part, total;
+  size_t row_loc, qb_first, qb_nch, qb_row0, qb_rows, items, q, u, part, total;
   int nqb_cap, item_cap;
 };
 
@@ -40,11 +40,11 @@ Layout make_layout(const hstu_layer_desc& d, int target) {
   const int64_t per_entry = 1 + (max_len + kMaxChunkKeys - 1) / kMaxChunkKeys;
   L.item_cap = static_cast<int>(d.num_heads * L.nqb_cap * per_entry + target);
   size_t off = 256;  // WsHeader
-  L.row_user = off; off = align256(off + 4 * T);
   L.row_loc = off;  off = align256(off + 8 * T);
-  L.qb_base = off;  off = align256(off + 4 * (B + 1));
   L.qb_first = off; off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
   L.qb_nch = off;   off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
+  L.qb_row0 = off;  off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
+  L.qb_rows = off;  off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
   L.items = off;    off = align256(off + sizeof(AttnItem) * static_cast<size_t>(L.item_cap));
   L.q = off;        off = align256(off + es * T * d.hidden);
   L.u = off;        off = align256(off + es * T * d.hidden);
@@ -57,11 +57,11 @@ WsPtrs ws_ptrs(void* base, const Layout& L) {
   char* b = static_cast<char*>(base);
   WsPtrs w;
   w.hdr = reinterpret_cast<WsHeader*>(b);
-  w.row_user = reinterpret_cast<int32_t*>(b + L.row_user);
   w.row_loc = reinterpret_cast<int2*>(b + L.row_loc);
-  w.qb_base = reinterpret_cast<int32_t*>(b + L.qb_base);
   w.qb_first = reinterpret_cast<int32_t*>(b + L.qb_first);
   w.qb_nch = reinterpret_cast<int32_t*>(b + L.qb_nch);
+  w.qb_row0 = reinterpret_cast<int32_t*>(b + L.qb_row0);
+  w.qb_rows = reinterpret_cast<int32_t*>(b + L.qb_rows);
   w.items = reinterpret_cast<AttnItem*>(b + L.items);
   w.q = b + L.q;
   w.u = b + L.u;
@@ -147,7 +147,7 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   e = launch_attn(d, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ws,
                   grid < L.item_cap ? grid : L.item_cap, st, kev(HSTU_STAGE_ATTN));
   if (e != hipSuccess) return HSTU_ERR_HIP;
-  e = launch_norm_gate(d, new_offsets, ws, st, kev(HSTU_STAGE_NORM));
+  e = launch_norm_gate(d, ws, L.nqb_cap, st, kev(HSTU_STAGE_NORM));
   if (e != hipSuccess) return HSTU_ERR_HIP;
   e = launch_gemm_out(d, ws.q, w2t, y, &ws.hdr->status, st, kev(HSTU_STAGE_OUT));
   if (e != hipSuccess) return HSTU_ERR_HIP;

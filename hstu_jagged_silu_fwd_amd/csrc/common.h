@@ -196,6 +196,7 @@ __device__ __forceinline__ int row_to_user(const int32_t* offsets, int B, int r)
 struct WsHeader {            // first 256 bytes of the workspace
   int32_t status;            // hstu_device_code of this call
   int32_t n_items;           // attention work items
+  int32_t n_qb;              // q-block entries
   int32_t item_budget;       // attention cost units per work item (chunk sizing)
   int32_t counter;           // dynamic work-fetch counter
 };
@@ -209,11 +210,11 @@ struct AttnItem {
 
 struct WsPtrs {
   WsHeader* hdr;
-  int32_t* row_user;         // [T]
   int2* row_loc;             // [T] (pool page, slot) of each new row's K/V
-  int32_t* qb_base;          // [B+1]   first q-block entry of each user
   int32_t* qb_first;         // [nqb_cap] first work item of a q-block entry (head 0)
   int32_t* qb_nch;           // [nqb_cap] key chunks of a q-block entry
+  int32_t* qb_row0;          // [nqb_cap] first jagged row of a q-block entry
+  int32_t* qb_rows;          // [nqb_cap] rows of a q-block entry
   AttnItem* items;           // [item_cap]
   void* q;                   // [T, D] dtype; reused for G after attention
   void* u;                   // [T, D] dtype
@@ -248,14 +249,14 @@ hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const i
                        const KernelEvents& ev = {});
 hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
                            void* v_pool, const WsPtrs& ws, hipStream_t stream, const KernelEvents& ev = {});
-hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                           const int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,
                        const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream,
                        const KernelEvents& ev = {});
-hipError_t launch_norm_gate(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws,
-                            hipStream_t stream, const KernelEvents& ev = {});
+hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
+                           const int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
+hipError_t launch_norm_gate(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,
+                            const KernelEvents& ev = {});
 hipError_t launch_append(const hstu_layer_desc& d, const void* k_new, const void* v_new,
                          const int32_t* new_off, const int32_t* hist, const int32_t* pt,
                          void* k_pool, void* v_pool, int32_t* status, hipStream_t stream);

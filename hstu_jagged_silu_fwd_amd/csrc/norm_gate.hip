@@ -1,29 +1,34 @@
 // Row norm and gating: O = attn_scale * (sum of the row's chunk partials, in
 // chunk order; the partials hold -log2(e) * sum SiLU(s) v, undone here), then
 // G = LayerNorm_row(O) * U, the elementwise gating that precedes the output
-// projection (aitrends.kr article 100093, "HSTU
-// sequential modelling").  One wavefront per row; mean and variance come from
-// wavefront reductions over the row's D entries (population variance, no
-// affine).  G overwrites the Q buffer, which is dead after the attention.
+// projection (aitrends.kr article 100093, "HSTU sequential modelling").
+// Population variance over the row's D entries, no affine.  G overwrites the
+// Q buffer, which is dead after the attention.
+//
+// A workgroup takes 256 / TPR consecutive rows of one q-block entry (grid:
+// entry x row block), TPR threads per row (32 when D allows, 16 otherwise);
+// the row statistics are TPR-lane reductions.  The entry's table entries come in one round trip and the
+// partial sums and U in a second; the loads carry no data-dependent branches
+// (columns beyond D load a valid column and are zeroed by a select) so each
+// batch stays in flight together.
 #include "common.h"
 
 namespace hstu {
 namespace {
 
-constexpr int kMaxGroups = 8;    // D <= 64 lanes * 4 * 8 = 2048
+constexpr int kThreads = 256;
 
 template <typename T>
 struct NormArgs {
-  const int32_t* new_off;
-  const int32_t* row_user;
-  const int32_t* qb_base;
-  const int32_t* qb_first;
-  const int32_t* qb_nch;
-  const float* part;
-  const T* u;
-  T* g;
-  const int32_t* status;
-  int T_rows, D, hd;
+  const WsHeader* hdr;
+  const int32_t* qb_first;          // [entries] first work item (head 0)
+  const int32_t* qb_nch;            // [entries] key chunks
+  const int32_t* qb_row0;           // [entries] first jagged row
+  const int32_t* qb_rows;           // [entries] rows
+  const float* part;                // [items][kQB][hd]
+  const T* u;                       // [T][D]
+  T* g;                             // [T][D]
+  int D, hd;
   float scale, eps;
 };
 
@@ -56,109 +61,142 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, const float* x) {
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void norm_gate_kernel(NormArgs<T> a) {
-  if (*a.status != 0) return;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= a.T_rows) return;
-  const int u = a.row_user[r];
-  const int t = r - a.new_off[u];
-  const int qbe = a.qb_base[u] + t / kQB;
-  const int tl = t % kQB;
-  const int first = a.qb_first[qbe];
-  const int nch = a.qb_nch[qbe];
+// TPR: threads per row; MAXNG: (4 * TPR)-column groups per row at most.
+template <typename T, int TPR, int MAXNG>
+__global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
+  constexpr int kRows = kThreads / TPR;           // rows per workgroup
+  constexpr int kBlocks = kQB / kRows;            // row blocks per q-block entry
+  constexpr int GW = 4 * TPR;                     // columns per group
+  const int tid = threadIdx.x;
   const int D = a.D;
+  const int e = blockIdx.x / kBlocks, rb = blockIdx.x % kBlocks;   // q-block entry, row block in it
+  const int4 hv = *reinterpret_cast<const int4*>(a.hdr);   // status, items, entries, budget
+  const int first = a.qb_first[e], nch = a.qb_nch[e], row0 = a.qb_row0[e], rows = a.qb_rows[e];
+  // all five loads are issued before the exit test (no short-circuit chain
+  // of dependent loads)
+  asm volatile("" ::"s"(first), "s"(nch), "s"(row0));
+  if ((hv.x != 0) | (e >= hv.z) | (rb * kRows >= rows)) return;   // uniform
 
-  float x[kMaxGroups][4];
+  // thread (row lr, lane sub) owns columns gi*GW + 4*sub .. +3 of its row
+  const int lr = tid / TPR, sub = tid % TPR;
+  const int rib = rb * kRows + lr;                // row inside the q-block
+  const bool valid = rib < rows;
+  const int r = row0 + min(rib, rows - 1);
+  const int NG = D / GW;
+  float x[MAXNG][4], uu[MAXNG][4];
+  const float* psrc[MAXNG];
+#pragma unroll
+  for (int gi = 0; gi < MAXNG; ++gi) {
+    const int col = min(gi, NG - 1) * GW + 4 * sub;          // a valid column for every gi
+    const int h = col / a.hd, el = col - h * a.hd;
+    psrc[gi] = a.part + (static_cast<size_t>(first + h * nch) * kQB + rib) * a.hd + el;
+    load4<T>(a.u + static_cast<size_t>(r) * D + col, uu[gi]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[gi][j] = 0.f;
+  }
+  // chunks CU at a time: all their loads are issued before the first add
+  // (a chunk index past nch re-reads the last chunk and adds zero), and each
+  // element is still summed in chunk order
+  constexpr int CU = MAXNG >= 32 ? 1 : 32 / MAXNG;
+  const size_t stride = static_cast<size_t>(kQB) * a.hd;      // one chunk further
+  for (int kc0 = 0; kc0 < nch; kc0 += CU) {
+    f32x4 v[CU][MAXNG];
+#pragma unroll
+    for (int c = 0; c < CU; ++c)
+#pragma unroll
+      for (int gi = 0; gi < MAXNG; ++gi)
+        v[c][gi] = *reinterpret_cast<const f32x4*>(psrc[gi] + min(kc0 + c, nch - 1) * stride);
+    // keep the scheduler from interleaving the adds with the loads (it would
+    // otherwise wait for each load before issuing the next)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < CU; ++c) {
+      const float m = kc0 + c < nch ? 1.f : 0.f;
+#pragma unroll
+      for (int gi = 0; gi < MAXNG; ++gi) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[gi][j] += m * v[c][gi][j];
+      }
+    }
+  }
   float s1 = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxGroups; ++k) {
-    const int col = (k * 64 + lane) * 4;
+  for (int gi = 0; gi < MAXNG; ++gi)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[k][j] = 0.f;
-    if (col < D) {
-      const int h = col / a.hd, e = col % a.hd;
-      const float* src = a.part + (static_cast<size_t>(first + h * nch) * kQB + tl) * a.hd + e;
-      const size_t stride = static_cast<size_t>(kQB) * a.hd;
-      int kc = 0;
-      for (; kc + 4 <= nch; kc += 4) {   // four independent loads in flight, summed in chunk order
-        const float4 v0 = *reinterpret_cast<const float4*>(src + (kc + 0) * stride);
-        const float4 v1 = *reinterpret_cast<const float4*>(src + (kc + 1) * stride);
-        const float4 v2 = *reinterpret_cast<const float4*>(src + (kc + 2) * stride);
-        const float4 v3 = *reinterpret_cast<const float4*>(src + (kc + 3) * stride);
-        x[k][0] += v0.x; x[k][1] += v0.y; x[k][2] += v0.z; x[k][3] += v0.w;
-        x[k][0] += v1.x; x[k][1] += v1.y; x[k][2] += v1.z; x[k][3] += v1.w;
-        x[k][0] += v2.x; x[k][1] += v2.y; x[k][2] += v2.z; x[k][3] += v2.w;
-        x[k][0] += v3.x; x[k][1] += v3.y; x[k][2] += v3.z; x[k][3] += v3.w;
-      }
-      for (; kc < nch; ++kc) {
-        const float4 v = *reinterpret_cast<const float4*>(src + kc * stride);
-        x[k][0] += v.x; x[k][1] += v.y; x[k][2] += v.z; x[k][3] += v.w;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[k][j] *= a.scale;
-        s1 += x[k][j];
-      }
+    for (int j = 0; j < 4; ++j) {
+      x[gi][j] = gi < NG ? x[gi][j] * a.scale : 0.f;
+      s1 += x[gi][j];
     }
-  }
-  const float mean = wave_sum(s1) / static_cast<float>(D);
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) s1 += __shfl_xor(s1, o, kWave);
+  const float mean = s1 / static_cast<float>(D);
   float s2 = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxGroups; ++k) {
-    const int col = (k * 64 + lane) * 4;
-    if (col < D) {
+  for (int gi = 0; gi < MAXNG; ++gi)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float dv = x[k][j] - mean;
-        s2 += dv * dv;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float dv = gi < NG ? x[gi][j] - mean : 0.f;
+      s2 += dv * dv;
     }
-  }
-  const float var = wave_sum(s2) / static_cast<float>(D);
-  const float rs = rsqrtf(var + a.eps);
 #pragma unroll
-  for (int k = 0; k < kMaxGroups; ++k) {
-    const int col = (k * 64 + lane) * 4;
-    if (col < D) {
-      float uu[4], gg[4];
-      load4<T>(a.u + static_cast<size_t>(r) * D + col, uu);
+  for (int o = TPR / 2; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o, kWave);
+  const float rs = rsqrtf(s2 / static_cast<float>(D) + a.eps);
+  if (valid) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) gg[j] = (x[k][j] - mean) * rs * uu[j];
-      store4<T>(a.g + static_cast<size_t>(r) * D + col, gg);
+    for (int gi = 0; gi < MAXNG; ++gi) {
+      if (gi < NG) {
+        float gg[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gg[j] = (x[gi][j] - mean) * rs * uu[gi][j];
+        store4<T>(a.g + static_cast<size_t>(r) * D + gi * GW + 4 * sub, gg);
+      }
     }
   }
 }
 
-template <typename T>
-hipError_t norm_t(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws, hipStream_t stream,
+template <typename T, int TPR, int MAXNG>
+hipError_t norm_t(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,
                   const KernelEvents& ev) {
   NormArgs<T> a;
-  a.new_off = new_off;
-  a.row_user = ws.row_user;
-  a.qb_base = ws.qb_base;
+  a.hdr = ws.hdr;
   a.qb_first = ws.qb_first;
   a.qb_nch = ws.qb_nch;
+  a.qb_row0 = ws.qb_row0;
+  a.qb_rows = ws.qb_rows;
   a.part = ws.part;
   a.u = static_cast<const T*>(ws.u);
   a.g = static_cast<T*>(ws.q);
-  a.status = &ws.hdr->status;
-  a.T_rows = d.total_new;
   a.D = d.hidden;
   a.hd = d.head_dim;
   a.scale = d.attn_scale * kNegLn2;   // the attention accumulates -log2(e) * SiLU
   a.eps = d.norm_eps;
-  const int grid = (d.total_new + 3) / 4;
-  return launch_kernel(norm_gate_kernel<T>, dim3(grid), dim3(256), stream, ev, a);
+  constexpr int kRows = kThreads / TPR;
+  return launch_kernel(norm_gate_kernel<T, TPR, MAXNG>, dim3(static_cast<unsigned>(nqb_cap) * (kQB / kRows)),
+                       dim3(kThreads), stream, ev, a);
+}
+
+template <typename T>
+hipError_t norm_dt(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,
+                   const KernelEvents& ev) {
+  if (d.hidden % 128 == 0) {                     // 32 threads per row, 8 rows per workgroup
+    const int ng = d.hidden / 128;
+    if (ng <= 4) return norm_t<T, 32, 4>(d, ws, nqb_cap, stream, ev);
+    if (ng <= 8) return norm_t<T, 32, 8>(d, ws, nqb_cap, stream, ev);
+    return norm_t<T, 32, 16>(d, ws, nqb_cap, stream, ev);
+  }
+  const int ng = d.hidden / 64;                  // 16 threads per row, 16 rows per workgroup
+  if (ng <= 4) return norm_t<T, 16, 4>(d, ws, nqb_cap, stream, ev);
+  if (ng <= 8) return norm_t<T, 16, 8>(d, ws, nqb_cap, stream, ev);
+  if (ng <= 16) return norm_t<T, 16, 16>(d, ws, nqb_cap, stream, ev);
+  return norm_t<T, 16, 32>(d, ws, nqb_cap, stream, ev);
 }
 
 }  // namespace
 
-hipError_t launch_norm_gate(const hstu_layer_desc& d, const int32_t* new_off, const WsPtrs& ws,
-                            hipStream_t stream, const KernelEvents& ev) {
-  if (d.dtype == HSTU_BF16) return norm_t<bf16>(d, new_off, ws, stream, ev);
-  return norm_t<float>(d, new_off, ws, stream, ev);
+hipError_t launch_norm_gate(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,
+                            const KernelEvents& ev) {
+  if (d.dtype == HSTU_BF16) return norm_dt<bf16>(d, ws, nqb_cap, stream, ev);
+  return norm_dt<float>(d, ws, nqb_cap, stream, ev);
 }
 
 }  // namespace hstu

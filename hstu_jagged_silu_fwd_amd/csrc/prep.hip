@@ -142,7 +142,6 @@ __device__ void map_rows(const PrepArgs& a, const PrepShared& s, int slice) {
   for (int i = 0; i < kRowsPerThread; ++i) {
     const int r = r0 + i * kPrepThreads;
     if (r < a.T) {
-      a.ws.row_user[r] = user[i];
       a.ws.row_loc[r] = make_int2(pg[i], pos[i] >= 0 ? pos[i] % a.ps : 0);
     }
   }
@@ -217,6 +216,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     if (tid == 0) {
       hdr->status = s.err;
       hdr->n_items = 0;
+      hdr->n_qb = 0;
       hdr->item_budget = 0;
       hdr->counter = 0;
     }
@@ -314,6 +314,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     if (tid == 0) {
       hdr->status = HSTU_DEV_CAPACITY;
       hdr->n_items = 0;
+      hdr->n_qb = 0;
       hdr->item_budget = 0;
       hdr->counter = 0;
     }
@@ -321,10 +322,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   }
 
   // 5. the work list (one thread per item) and the per-entry tables used by
-  //    the norm kernel
+  //    the norm / output kernel
   for (int e = tid; e < nqb; e += kPrepThreads) {
+    const int u = s.qbu[e], qb = e - s.qbb[u];
     a.ws.qb_first[e] = s.qbf[e];
     a.ws.qb_nch[e] = s.qbn[e];
+    a.ws.qb_row0[e] = s.off[u] + qb * kQB;
+    a.ws.qb_rows[e] = min(kQB, s.off[u + 1] - s.off[u] - qb * kQB);
   }
   for (int i = tid; i < n_items; i += kPrepThreads) {
     int lo = 0, hi = nqb - 1;                // last entry whose first item <= i
@@ -347,11 +351,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     it.b = make_int4(min(keys, k_lo + csz), s.off[u], n, c);
     a.ws.items[i] = it;
   }
-  for (int u = tid; u <= B; u += kPrepThreads) a.ws.qb_base[u] = s.qbb[u];
 
   if (tid == 0) {
     hdr->status = 0;
     hdr->n_items = static_cast<int32_t>(n_items);
+    hdr->n_qb = nqb;
     hdr->item_budget = budget;
     hdr->counter = 0;
   }

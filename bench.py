@@ -48,7 +48,83 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="skip the per-kernel event pass (no roofline or stage split)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn four rocprofv3 --pmc output folders into the attention traffic record")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the attention kernel from rocprofv3 counters.  FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch) are each scaled by what the same counter reads
+# for a plain copy of COPY_BYTES, and kept in TRAFFIC_FILE together with a
+# hash of the sources that shape the kernel's memory traffic; the record is
+# only used while that hash still matches.
+# ---------------------------------------------------------------------------
+COPY_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_silu_attn_3layer_b8_kv_hit_traffic.json")
+TRAFFIC_SOURCES = ("attn.hip", "prep.hip", "common.h")
+
+
+def traffic_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "hstu_jagged_silu_fwd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def _pmc_mean(folder, counter, kernel_substr):
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_substr} under {folder}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_pmc(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    fetch, nf = _pmc_mean(fetch_dir, "FETCH_SIZE", "attn_kernel")
+    write, nw = _pmc_mean(write_dir, "WRITE_SIZE", "attn_kernel")
+    cfetch, _ = _pmc_mean(copy_fetch_dir, "FETCH_SIZE", "opy")      # the copy kernel
+    cwrite, _ = _pmc_mean(copy_write_dir, "WRITE_SIZE", "opy")
+    ff = COPY_BYTES / (cfetch * 1024.0)
+    wf = COPY_BYTES / (cwrite * 1024.0)
+    rec = dict(kernel="paged_silu_attn", sources_sha256=traffic_source_hash(),
+               fetch_kib_per_launch=fetch, write_kib_per_launch=write, launches=nf,
+               copy_fetch_factor=ff, copy_write_factor=wf,
+               traffic_bytes_per_launch=(fetch * ff + write * wf) * 1024.0)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
+
+
+def load_traffic():
+    """Calibrated HBM bytes per attention launch, or None when the record is
+    missing or was taken on other kernel sources."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != traffic_source_hash():
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 class Bench:
@@ -207,6 +283,12 @@ def cpu_baseline(wl, B, R, min_seconds=10.0):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
@@ -261,7 +343,7 @@ def main():
         achieved = attn_bytes / attn_s / 1e9
         out["roofline"] = dict(kernel="paged_silu_attn", bound="hbm", achieved=achieved,
                                peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                               traffic=None, mean_us=1e6 * attn_s / n_launch,
+                               traffic=load_traffic(), mean_us=1e6 * attn_s / n_launch,
                                timing="hipExtLaunchKernel start/stop events per launch, second pass of the same steps",
                                bytes_per_launch=attn_bytes / n_launch,
                                mfma_tflops=attn_flops / attn_s / 1e12,

@@ -413,7 +413,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
         if (later > 0) wait_vm_n(later * my_cnt);
         else wait_vm<0>();
         bar();                             // round r visible; round r-1 no longer read
-        for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
+        const bool early = w >= 4;
+        if (early)
+          for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
         if constexpr (decltype(ngc)::value > 0) {
           const int s = r * P + ph;
           if (s < nsteps) {
@@ -422,6 +424,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
             else compute(ngc, std::false_type{}, s);
           }
         }
+        if (!early)
+          for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
       }
     };
     if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});

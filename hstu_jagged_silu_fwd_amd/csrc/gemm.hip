@@ -257,13 +257,15 @@ hipError_t gemm_out_t(const hstu_layer_desc& d, const void* g, const void* w2t, 
                        status);
 }
 
-// Tile shape by problem size (two ring stages throughout: several workgroups
-// per CU beat deeper rings here, because a CU's load throughput grows with
-// the waves it has in flight):
-//   >= 1024 tiles of 128 x 128 -> 128 x 128, 8 waves (fewest operand re-reads);
-//   >= 256 such tiles          -> 64 x 128, 4 waves;
-//   otherwise                  -> 64 x 64, 4 waves (most workgroups); for G W2
-//                                 32 x 64 when 64 x 64 gives fewer tiles than CUs.
+// Tile shape and ring depth by problem size (large problems: two stages, as
+// several workgroups per CU beat deeper rings there, a CU's load throughput
+// growing with the waves it has in flight; small ones: three stages, since
+// each workgroup's few k-tiles are then latency-bound):
+//   >= 1024 tiles of 128 x 128 -> 128 x 128, 8 waves, 2 stages (fewest re-reads);
+//   >= 256 such tiles          -> 64 x 128, 4 waves, 2 stages;
+//   otherwise                  -> 64 x 64, 4 waves, 3 stages (most workgroups);
+//                                 for G W2 32 x 64 when 64 x 64 gives fewer
+//                                 tiles than CUs.
 // Wide tiles need N % 128 == 0 (and, for X W1, every U|V|Q|K block whole).
 enum class Tile { k64x64, k64x128, k128x128 };
 Tile pick_tile(int M, int N, int D) {
@@ -283,7 +285,7 @@ hipError_t qkv_dispatch(const hstu_layer_desc& d, const void* x, const void* w1t
     switch (pick_tile(d.total_new, 4 * d.hidden, d.hidden)) {
       case Tile::k128x128: return gemm_qkv_t<T, 128, 128, 2, 2, 4>(d, x, w1t, k_pool, v_pool, ws, st, ev);
       case Tile::k64x128: return gemm_qkv_t<T, 64, 128, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st, ev);
-      default: return gemm_qkv_t<T, 64, 64, 2, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st, ev);
+      default: return gemm_qkv_t<T, 64, 64, 3, 2, 2>(d, x, w1t, k_pool, v_pool, ws, st, ev);
     }
   }
 }
@@ -300,8 +302,8 @@ hipError_t out_dispatch(const hstu_layer_desc& d, const void* g, const void* w2t
       default:
         // fewer 64 x 64 tiles than CUs: halve the tile height for more workgroups
         if (static_cast<int64_t>((d.total_new + 63) / 64) * (d.hidden / 64) < 256)
-          return gemm_out_t<T, 32, 64, 2, 2, 2>(d, g, w2t, y, status, st, ev);
-        return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st, ev);
+          return gemm_out_t<T, 32, 64, 3, 2, 2>(d, g, w2t, y, status, st, ev);
+        return gemm_out_t<T, 64, 64, 3, 2, 2>(d, g, w2t, y, status, st, ev);
     }
   }
 }

@@ -11,8 +11,7 @@
 // Because the attention has no softmax, the partial outputs of the chunks of
 // a row simply add; the norm kernel sums them in chunk order.
 // Chunks are sized by cost, not by keys: a 32-key step of an entry with G
-// query groups costs w(G) = max(kStepFloor, G) units (the products grow with
-// G above a floor set by streaming the step's K and V).  With a budget of
+// query groups costs w(G) units (step_weight below).  With a budget of
 // `budget` units per item an entry's chunks are at most
 // clamp(budget / w, kMinSteps, kCapSteps) steps long, and the budget is the
 // smallest one found that keeps the item count within the number of resident
@@ -28,8 +27,14 @@ constexpr int kPrepWaves = kPrepThreads / kWave;
 constexpr int kStepKeys = 32;   // attention key step
 constexpr int kMinSteps = 4;    // shortest chunk: a step for each of up to four phases
 constexpr int kCapSteps = kMaxChunkKeys / kStepKeys;
-constexpr int kStepFloor = 6;   // step cost floor, in query groups
-constexpr int kMaxWeight = kQB / 16;
+// Cost of one 32-key step by the entry's query groups G, in units of about a
+// tenth of a microsecond: the attention workgroup splits the steps of a
+// q-block with G <= 4 over four phases, with G <= 8 over two, and multiplies
+// every step with all its waves otherwise, so the time per step is a step
+// function of G (measured on MI355X: about 0.85, 1.3 and 2.1 us).
+__device__ __forceinline__ int step_weight(int groups) { return groups <= 4 ? 4 : (groups <= 8 ? 6 : 10); }
+constexpr int kMinWeight = 4;
+constexpr int kMaxWeight = 10;
 constexpr int kWShift = 25;     // entry word: steps (bits 0..24) | weight << 25
 constexpr int kStepMask = (1 << kWShift) - 1;
 constexpr int kRowsPerThread = 4;
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     const int n = s.off[u + 1] - s.off[u];
     const int keys = s.hist[u] + min(n, (qb + 1) * kQB);
     const int steps = (keys + kStepKeys - 1) / kStepKeys;
-    const int wt = max(kStepFloor, (min(kQB, n - qb * kQB) + 15) / 16);
+    const int wt = step_weight((min(kQB, n - qb * kQB) + 15) / 16);
     s.qbn[e] = steps | (wt << kWShift);
     s.qbu[e] = u;
     part += static_cast<int64_t>(steps) * wt;
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   const int64_t target = a.target_items;
   const int64_t slack = static_cast<int64_t>(a.H) * nqb;
   auto chunk_steps = [](int budget, int weight) { return min(kCapSteps, max(kMinSteps, budget / weight)); };
-  constexpr int kBudgetLo = kStepFloor * kMinSteps, kBudgetHi = kMaxWeight * kCapSteps;
+  constexpr int kBudgetLo = kMinWeight * kMinSteps, kBudgetHi = kMaxWeight * kCapSteps;
   int budget = kBudgetHi;
   if (target > slack) {
     const int64_t b_lo = min<int64_t>(kBudgetHi, max<int64_t>(kBudgetLo, (hs + target - 1) / target));

@@ -138,15 +138,15 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  // Status and item count, the first item (static: workgroup i takes item i;
+  // Status words and item count, the first item (static: workgroup i takes item i;
   // the grid never exceeds the item capacity) and the bias tables are all
   // loaded at once.
   const int4 hv = *reinterpret_cast<const int4*>(a.hdr);
   AttnItem item = a.items[blockIdx.x];
   for (int i = tid; i < a.nb; i += NT) s_pb[i] = kNegLog2e * a.pos_bias[i];
   for (int i = tid; i < a.ntsb; i += NT) s_tb[i] = kNegLog2e * a.ts_bias[i];
-  if (hv.x != 0) return;                   // status: prep rejected the call
-  const int n_items = hv.y;
+  if ((hv.x | hv.y) != 0) return;          // status words: prep rejected the call
+  const int n_items = hv.z;
   const bool dynamic = n_items > static_cast<int>(gridDim.x);
   __syncthreads();
   for (int i = tid; i < kLut; i += NT) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];

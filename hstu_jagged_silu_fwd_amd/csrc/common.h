@@ -194,7 +194,9 @@ __device__ __forceinline__ int row_to_user(const int32_t* offsets, int B, int r)
 // Workspace of one hstu_layer_fwd call (offsets computed on the host).
 // ---------------------------------------------------------------------------
 struct WsHeader {            // first 256 bytes of the workspace
-  int32_t status;            // hstu_device_code of this call
+  int32_t status;            // hstu_device_code of this call (metadata validation)
+  int32_t wl_status;         // work-list build (nonzero only with metadata that
+                             // `status` rejects, or a workspace too small)
   int32_t n_items;           // attention work items
   int32_t n_qb;              // q-block entries
   int32_t item_budget;       // attention cost units per work item (chunk sizing)
@@ -254,7 +256,7 @@ hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* 
                        const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream,
                        const KernelEvents& ev = {});
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                           const int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
+                           int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_norm_gate(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,
                             const KernelEvents& ev = {});
 hipError_t launch_append(const hstu_layer_desc& d, const void* k_new, const void* v_new,

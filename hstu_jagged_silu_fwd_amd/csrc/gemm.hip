@@ -53,7 +53,7 @@ __device__ __forceinline__ void tile_of(int id, int Mt, int Nt, int& mt, int& nt
 template <typename T, int BM, int BN, int S, int WGM, int WGN, bool kQkv>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const T* __restrict__ A, const T* __restrict__ W,
                                                    int M, int N, int K, T* __restrict__ Y,
-                                                   QkvEpi<T> ep, const int32_t* status) {
+                                                   QkvEpi<T> ep, int32_t* status) {
   constexpr int ES = static_cast<int>(sizeof(T));
   constexpr int BK = kRowBytes / ES;
   constexpr int CE = 16 / ES;                  // elements per 16-byte chunk
@@ -69,7 +69,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const T* __restric
   static_assert(IPW * (S - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
 
-  if (*status != 0) return;
+  // the call's two status words (metadata, work list); the projection folds
+  // a work-list failure into the first, the word the host reads
+  const int2 sv = *reinterpret_cast<const int2*>(status);
+  if (kQkv && blockIdx.x == 0 && threadIdx.x == 0 && sv.x == 0 && sv.y != 0) status[0] = sv.y;
+  if ((sv.x | sv.y) != 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
@@ -243,12 +247,12 @@ hipError_t gemm_qkv_t(const hstu_layer_desc& d, const void* x, const void* w1t, 
   const int tiles = (M + BM - 1) / BM * (N / BN);
   return launch_kernel(gemm_kernel<T, BM, BN, S, WGM, WGN, true>, dim3(tiles), dim3(64 * WGM * WGN), stream, ev,
                        static_cast<const T*>(x), static_cast<const T*>(w1t), M, N, K, static_cast<T*>(nullptr),
-                       ep, static_cast<const int32_t*>(&ws.hdr->status));
+                       ep, &ws.hdr->status);
 }
 
 template <typename T, int BM, int BN, int S, int WGM, int WGN>
 hipError_t gemm_out_t(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                      const int32_t* status, hipStream_t stream, const KernelEvents& ev) {
+                      int32_t* status, hipStream_t stream, const KernelEvents& ev) {
   QkvEpi<T> ep{};
   const int M = d.total_new, N = d.hidden, K = d.hidden;
   const int tiles = (M + BM - 1) / BM * (N / BN);
@@ -292,7 +296,7 @@ hipError_t qkv_dispatch(const hstu_layer_desc& d, const void* x, const void* w1t
 
 template <typename T>
 hipError_t out_dispatch(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                        const int32_t* status, hipStream_t st, const KernelEvents& ev) {
+                        int32_t* status, hipStream_t st, const KernelEvents& ev) {
   if constexpr (sizeof(T) == 4) {
     return gemm_out_t<T, 64, 64, 2, 2, 2>(d, g, w2t, y, status, st, ev);   // fp32: one tile shape
   } else {
@@ -317,7 +321,7 @@ hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* 
 }
 
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
-                           const int32_t* status, hipStream_t stream, const KernelEvents& ev) {
+                           int32_t* status, hipStream_t stream, const KernelEvents& ev) {
   return d.dtype == HSTU_BF16 ? out_dispatch<bf16>(d, g, w2t, y, status, stream, ev)
                               : out_dispatch<float>(d, g, w2t, y, status, stream, ev);
 }

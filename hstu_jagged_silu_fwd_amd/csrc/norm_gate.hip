@@ -70,12 +70,12 @@ __global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
   const int tid = threadIdx.x;
   const int D = a.D;
   const int e = blockIdx.x / kBlocks, rb = blockIdx.x % kBlocks;   // q-block entry, row block in it
-  const int4 hv = *reinterpret_cast<const int4*>(a.hdr);   // status, items, entries, budget
+  const int4 hv = *reinterpret_cast<const int4*>(a.hdr);   // status, wl_status, items, entries
   const int first = a.qb_first[e], nch = a.qb_nch[e], row0 = a.qb_row0[e], rows = a.qb_rows[e];
   // all five loads are issued before the exit test (no short-circuit chain
   // of dependent loads)
   asm volatile("" ::"s"(first), "s"(nch), "s"(row0));
-  if ((hv.x != 0) | (e >= hv.z) | (rb * kRows >= rows)) return;   // uniform
+  if (((hv.x | hv.y) != 0) | (e >= hv.w) | (rb * kRows >= rows)) return;   // uniform
 
   // thread (row lr, lane sub) owns columns gi*GW + 4*sub .. +3 of its row
   const int lr = tid / TPR, sub = tid % TPR;

@@ -152,6 +152,10 @@ __device__ void map_rows(const PrepArgs& a, const PrepShared& s, int slice) {
   }
 }
 
+__device__ void work_list(const PrepArgs& a, PrepShared& s);
+
+// Workgroup 0 validates the metadata (status), workgroup 1 builds the work
+// list (wl_status), workgroups 2.. map the rows.
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   __shared__ PrepShared s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -162,8 +166,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   for (int u = tid; u <= B; u += kPrepThreads) s.off[u] = a.new_off[u];
   for (int u = tid; u < B; u += kPrepThreads) s.hist[u] = a.hist[u];
   __syncthreads();
-  if (blockIdx.x > 0) {
-    if (B > 0) map_rows(a, s, blockIdx.x - 1);   // B == 0 with rows is rejected below
+  if (blockIdx.x >= 2) {
+    if (B > 0) map_rows(a, s, blockIdx.x - 2);   // B == 0 with rows is rejected below
+    return;
+  }
+  if (blockIdx.x == 1) {
+    work_list(a, s);
     return;
   }
 
@@ -217,9 +225,30 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
     if (bad) set_err(s, HSTU_DEV_BAD_PAGE);
   }
   __syncthreads();
+  if (tid == 0) hdr->status = s.err;
+}
+
+// Workgroup 1: the attention work list and the per-entry tables, built at
+// the same time as workgroup 0 validates the metadata.  Its own checks only
+// keep its writes in bounds (offsets and history lengths that workgroup 0
+// rejects make it stop); its result goes to the header's wl_status.
+__device__ void work_list(const PrepArgs& a, PrepShared& s) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  WsHeader* hdr = a.ws.hdr;
+  const int B = a.B;
+  if (tid == 0) s.err = 0;
+  __syncthreads();
+  if (tid == 0 && B == 0 && a.T != 0) set_err(s, HSTU_DEV_BAD_OFFSETS);
+  for (int u = tid; u < B; u += kPrepThreads) {
+    const int o0 = s.off[u], o1 = s.off[u + 1];
+    if ((u == 0 && o0 != 0) || o1 < o0 || (u == B - 1 && o1 != a.T)) set_err(s, HSTU_DEV_BAD_OFFSETS);
+    if (s.hist[u] < 0) set_err(s, HSTU_DEV_BAD_HIST);
+  }
+  __syncthreads();
   if (s.err != 0) {
     if (tid == 0) {
-      hdr->status = s.err;
+      hdr->wl_status = s.err;
       hdr->n_items = 0;
       hdr->n_qb = 0;
       hdr->item_budget = 0;
@@ -317,7 +346,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   const int64_t n_items = block_scan(s.qbf, nqb, s);
   if (n_items > a.item_cap) {
     if (tid == 0) {
-      hdr->status = HSTU_DEV_CAPACITY;
+      hdr->wl_status = HSTU_DEV_CAPACITY;
       hdr->n_items = 0;
       hdr->n_qb = 0;
       hdr->item_budget = 0;
@@ -358,7 +387,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   }
 
   if (tid == 0) {
-    hdr->status = 0;
+    hdr->wl_status = 0;
     hdr->n_items = static_cast<int32_t>(n_items);
     hdr->n_qb = nqb;
     hdr->item_budget = budget;
@@ -387,7 +416,7 @@ hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const i
   a.nqb_cap = nqb_cap;
   a.item_cap = item_cap;
   a.target_items = target_items;
-  return launch_kernel(prep_kernel, dim3(1 + (d.total_new + kRowsPerWg - 1) / kRowsPerWg), dim3(kPrepThreads),
+  return launch_kernel(prep_kernel, dim3(2 + (d.total_new + kRowsPerWg - 1) / kRowsPerWg), dim3(kPrepThreads),
                        stream, ev, a);
 }
 

@@ -69,11 +69,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const T* __restric
   static_assert(IPW * (S - 2) < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
 
-  // the call's two status words (metadata, work list); the projection folds
-  // a work-list failure into the first, the word the host reads
+  // The call's two status words (metadata, work list), loaded now and tested
+  // only before the epilogue writes anything: the operand loads are in
+  // bounds either way, and the test no longer costs a round trip ahead of
+  // them.  The projection folds a work-list failure into the first word,
+  // the one the host reads.
   const int2 sv = *reinterpret_cast<const int2*>(status);
-  if (kQkv && blockIdx.x == 0 && threadIdx.x == 0 && sv.x == 0 && sv.y != 0) status[0] = sv.y;
-  if ((sv.x | sv.y) != 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, l16 = lane & 15;
@@ -146,6 +147,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const T* __restric
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     compute(kt % S);
   }
+  if (kQkv && blockIdx.x == 0 && threadIdx.x == 0 && sv.x == 0 && sv.y != 0) status[0] = sv.y;
+  if ((sv.x | sv.y) != 0) return;            // uniform: nothing is written on error
   __syncthreads();
 
   // ---- epilogue: stage the tile (after the epilogue transform) in LDS ----

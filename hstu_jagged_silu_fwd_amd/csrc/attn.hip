@@ -139,17 +139,24 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
   // Status words and item count, the first item (static: workgroup i takes item i;
-  // the grid never exceeds the item capacity) and the bias tables are all
-  // loaded at once.
+  // the grid never exceeds the item capacity) and the bias tables (up to two
+  // entries of each per thread) are all loaded at once.  The tables reach LDS
+  // (and the distance table is built) inside the first item's set-up, after
+  // its page-id and query loads have gone out, so those round trips overlap.
+  static_assert(kMaxBuckets <= 2 * NT, "two bias entries per thread");
   const int4 hv = *reinterpret_cast<const int4*>(a.hdr);
   AttnItem item = a.items[blockIdx.x];
-  for (int i = tid; i < a.nb; i += NT) s_pb[i] = kNegLog2e * a.pos_bias[i];
-  for (int i = tid; i < a.ntsb; i += NT) s_tb[i] = kNegLog2e * a.ts_bias[i];
+  float pbv[2], tbv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + j * NT;
+    pbv[j] = i < a.nb ? a.pos_bias[i] : 0.f;
+    tbv[j] = i < a.ntsb ? a.ts_bias[i] : 0.f;
+  }
   if ((hv.x | hv.y) != 0) return;          // status words: prep rejected the call
   const int n_items = hv.z;
   const bool dynamic = n_items > static_cast<int>(gridDim.x);
-  __syncthreads();
-  for (int i = tid; i < kLut; i += NT) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];
+  bool tables_ready = false;
   const int ps = 1 << a.ps_shift;
   const bool has_ts = a.ntsb > 0;
   const int g = lane >> 4, l16 = lane & 15;
@@ -238,6 +245,17 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // Let these loads land before the ring starts: the compiler cannot count
     // outstanding loads across the key loop, so it would otherwise wait for
     // every in-flight stage at the first use of a query fragment.
+    if (!tables_ready) {                   // first item: bias tables into LDS meanwhile
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int i = tid + j * NT;
+        if (i < a.nb) s_pb[i] = kNegLog2e * pbv[j];
+        if (i < a.ntsb) s_tb[i] = kNegLog2e * tbv[j];
+      }
+      __syncthreads();
+      for (int i = tid; i < kLut; i += NT) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];
+      tables_ready = true;
+    }
     wait_vm<0>();
     if (tid < npg) s_pages[tid] = pid0;
     if (tid + NT < npg) s_pages[tid + NT] = pid1;

@@ -40,10 +40,12 @@
 // applied with the 1/N scale by the norm kernel.
 //
 // Bias: a per-workgroup LDS table holds the scaled bias of every distance
-// below kLut; a step whose distances all lie at or beyond kLut and span no
-// more than one bucket width (2^(11-m) there) touches at most two buckets and
-// takes a compare/select between two values; any other step takes the
-// generic per-element bucket path.  Timestamps, when present, travel with
+// below kLut, in descending order of distance: the 8 scores a lane holds per
+// group and step have 8 consecutive distances, so they read 8 consecutive
+// entries at immediate offsets from one address.  A step whose distances all
+// lie at or beyond kLut and span no more than one bucket width (2^(12-m)
+// there) touches at most two buckets and takes a compare/select between two
+// values; any other step takes the generic per-element bucket path.  Timestamps, when present, travel with
 // their keys through the ring; each lane keeps its query's in a register.
 //
 // Partial outputs (fp32) go to the workspace; the chunks of a row are added
@@ -58,7 +60,8 @@
 namespace hstu {
 namespace {
 
-constexpr int kLut = 2048;
+constexpr int kLut = 4096;
+constexpr int kLutPad = 64;        // entries past the table (negative distances: masked scores)
 constexpr int kStepKeys = 32;
 constexpr int kMaxChunkPages = kMaxChunkKeys / 16 + 1;
 constexpr float kNegLog2e = -1.4426950408889634f;
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   static_assert(kMaxChunkPages <= 2 * NT, "two page ids per thread");
   __shared__ __attribute__((aligned(1024))) unsigned char s_ring[NST * G::STAGE];
   __shared__ __attribute__((aligned(256))) int64_t s_ts[NST][kStepKeys];
-  __shared__ float s_lut[kLut];
+  __shared__ float s_rlut[kLut + kLutPad];   // s_rlut[x]: bias of distance kLut - 1 - x
   __shared__ float s_pb[kMaxBuckets];
   __shared__ float s_tb[kMaxBuckets];
   __shared__ int s_pages[kMaxChunkPages];
@@ -207,15 +210,28 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     const int len = c + n;
     const int nq = min(kQB, n - q0);
     const int ngroups = (nq + 15) >> 4;
-    // Phases: the waves form P phases of NW waves; wave (phase p, column j)
-    // owns query groups 2j and 2j+1 and multiplies the steps s = p (mod P).
-    // Few groups -> several phases, so that every wave has products to do.
+    // Phases: the waves form P phases of WP = kWaves/P waves (columns);
+    // the waves of phase p multiply the steps s = p (mod P).  Few groups ->
+    // several phases, so that every wave has products to do.  A column owns
+    // one or two query groups (two share every K/V fragment read).  Waves w
+    // and w+4 share a SIMD: they are columns j and j+WP/2 of one phase.  So
+    // that no SIMD holds two pairs while another holds a single group,
+    // columns below WP/2 take groups in pairs from 0, and the others take
+    // the remaining groups, in pairs only as far as needed.
     const int NW = (ngroups + 1) >> 1;
     const int P = (G::PMAX >= 4 && 4 * NW <= kWaves) ? 4 : ((G::PMAX >= 2 && 2 * NW <= kWaves) ? 2 : 1);
     const int D = NST / P - 1;                         // rounds of loads in flight ahead
-    const int ph = w / NW, col = w - (w / NW) * NW;
-    const int gi0 = 2 * col;                           // this wave's first group
-    const int ng_w = ph < P ? min(2, ngroups - gi0) : 0;   // its groups: 0, 1 or 2
+    const int half = kWaves / (2 * P);
+    const int ph = w & (P - 1), col = w / P;
+    int gi0, ng_w;                                     // this wave's first group and group count
+    if (col < half) {
+      gi0 = 2 * col;
+      ng_w = min(max(ngroups - gi0, 0), 2);
+    } else {
+      const int j = col - half, rest = max(ngroups - 2 * half, 0), npairs = max(rest - half, 0);
+      gi0 = j < npairs ? 2 * half + 2 * j : 2 * half + npairs + j;
+      ng_w = j < npairs ? 2 : (gi0 < ngroups ? 1 : 0);
+    }
     const int32_t* ptu = a.pt + static_cast<size_t>(u) * a.maxP;
     const int pg0 = k_lo >> a.ps_shift;
     const int kst_end = min(k_hi, len);                // keys whose pages are staged
@@ -253,7 +269,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
         if (i < a.ntsb) s_tb[i] = kNegLog2e * tbv[j];
       }
       __syncthreads();
-      for (int i = tid; i < kLut; i += NT) s_lut[i] = s_pb[bucket32(i, a.mbits, a.nb)];
+      for (int i = tid; i < kLut + kLutPad; i += NT)
+        s_rlut[i] = i < kLut ? s_pb[bucket32(kLut - 1 - i, a.mbits, a.nb)] : 0.f;
       tables_ready = true;
     }
     wait_vm<0>();
@@ -270,7 +287,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     const size_t kv_head = static_cast<size_t>(h) * ps * HD;      // head block inside a page
     const size_t page_elems = static_cast<size_t>(a.H) * ps * HD;
     // Keys past the staged range (last step only) read rows of the step's
-    // own pages: in bounds, and masked (K) or zeroed (V) by the products.
+    // own pages: in bounds; their scores are masked and their V^T columns
+    // zeroed in LDS before the products.
     auto issue = [&](int s) __attribute__((always_inline)) {
       const int kb = k_lo + kStepKeys * s;
       unsigned char* stg = s_ring + (s % NST) * G::STAGE;
@@ -305,9 +323,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       for (int ob = 0; ob < NO; ++ob) o[i][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- products of step s for this wave's first NG query groups ----
-    auto compute = [&](auto ngc, auto tailc, int s) __attribute__((always_inline)) {
+    auto compute = [&](auto ngc, int s) __attribute__((always_inline)) {
       constexpr int NG = decltype(ngc)::value;
-      constexpr bool kTail = decltype(tailc)::value;   // the step reaches past the staged keys
       const int kb = k_lo + kStepKeys * s;
       const unsigned char* stg = s_ring + (s % NST) * G::STAGE;
       f32x4 st[NG][2];
@@ -321,17 +338,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
         const int dmax = pq + 15 - kb;
         dmn[i] = dmin;
         if (dmax < kLut) {
-          if (dmin >= 0) {
+          // element (b, r) has distance dl0 - (4b + r), entry x0 + 4b + r; a
+          // lane whose distances are all negative reads padding
+          const float* lp = s_rlut + min(kLut - 1 - dl0[i], kLut + kLutPad - 8);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) st[i][b][r] = s_lut[dl0[i] - 4 * b - r];
-          } else {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) st[i][b][r] = s_lut[max(dl0[i] - 4 * b - r, 0)];
-          }
+            for (int r = 0; r < 4; ++r) st[i][b][r] = lp[4 * b + r];
         } else if (dmin >= kLut && (kLut >> a.mbits) >= dmax - dmin + 1) {
           // every distance here falls into one or two adjacent buckets
           const int blo = bucket32(dmin, a.mbits, a.nb), bhi = bucket32(dmax, a.mbits, a.nb);
@@ -355,61 +368,55 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
             for (int r = 0; r < 4; ++r) st[i][b][r] += s_tb[bucket64(tq[i] - tk[4 * b + r], a.tsmbits, a.ntsb)];
         }
       }
-      // S^T = K * Q^T over the head dim; each K fragment feeds every group
+      // S^T = K * Q^T over the head dim; each K fragment feeds every group.
+      // All of the step's K fragment reads go out before the first product,
+      // so their LDS latency is paid once.
       const unsigned char* k0p = stg + krow0 * (KCH * 16);
       const unsigned char* k1p = k0p + 4 * (KCH * 16);
+      Frag<T> kf[NC][2];
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
         const int chunk = (cc * 32 + 8 * g) / CE;
-        Frag<T> kf0, kf1;
-        read_frag(kf0, k0p, chunk, ksw);
-        read_frag(kf1, k1p, chunk, ksw);
+        read_frag(kf[cc][0], k0p, chunk, ksw);
+        read_frag(kf[cc][1], k1p, chunk, ksw);
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
-          st[i][0] = mma16(kf0, qf[i][cc], st[i][0]);
-          st[i][1] = mma16(kf1, qf[i][cc], st[i][1]);
+          st[i][0] = mma16(kf[cc][0], qf[i][cc], st[i][0]);
+          st[i][1] = mma16(kf[cc][1], qf[i][cc], st[i][1]);
         }
-      }
       // V^T fragments are read now so that their LDS latency overlaps the
-      // SiLU below.  V of keys past the staged range (only in the last step,
-      // where A is masked anyway) is zeroed so stale pool memory cannot
-      // turn into NaN.
+      // SiLU below.
       Frag<T> vf[NO];
       {
         const unsigned char* vp = stg + G::KBYTES + l16 * (VCH * 16);
         const int vchunk = (8 * g) / CE;
 #pragma unroll
         for (int ob = 0; ob < NO; ++ob) read_frag(vf[ob], vp + ob * 16 * (VCH * 16), vchunk, vsw);
-        if constexpr (kTail) {
-          const int nvalid = kst_end - (kb + 8 * g);
-#pragma unroll
-          for (int ob = 0; ob < NO; ++ob)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= nvalid) set_elem(vf[ob], e, 0.0f);
-        }
       }
+      // SiLU in independent batches (every exp2, then every reciprocal) so
+      // that no transcendental waits on the one before it
+      float av[NG][8];
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[i][e] = __builtin_amdgcn_exp2f(st[i][e >> 2][e & 3]);
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[i][e] = __builtin_amdgcn_rcpf(1.0f + av[i][e]);
       Frag<T> af[NG];
 #pragma unroll
       for (int i = 0; i < NG; ++i) {
-        if (dmn[i] >= 0) {
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+        for (int e = 0; e < 8; ++e) av[i][e] *= st[i][e >> 2][e & 3];
+        if (dmn[i] < 0) {                            // causal mask on the diagonal
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float sv = st[i][b][r];
-              set_elem(af[i], 4 * b + r, sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv)));
-            }
-        } else {                                     // causal mask on the diagonal
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float sv = st[i][b][r];
-              const float av = sv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sv));
-              set_elem(af[i], 4 * b + r, (dl0[i] - 4 * b - r) >= 0 ? av : 0.0f);
-            }
+          for (int e = 0; e < 8; ++e) av[i][e] = dl0[i] - e >= 0 ? av[i][e] : 0.0f;
         }
+        set_frag(af[i], av[i]);
       }
       // O^T += V^T * A
 #pragma unroll
@@ -424,23 +431,45 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // while one is multiplied.  (The wave's group count is fixed for the
     // item, so each count gets a loop of its own.) ----
     for (int s = 0; s < min(D * P, nsteps); ++s) issue(s);
+    // Only the last step can reach past the staged keys.  Those keys lie
+    // beyond every query of the item, so their scores are masked; their V^T
+    // columns are zeroed in LDS (by the lanes that loaded them, once their
+    // loads have landed) so that stale pool memory cannot turn a masked
+    // product into NaN, and the products need no tail case of their own.
+    const int tail_round = k_lo + kStepKeys * nsteps > kst_end ? (nsteps - 1) / P : -1;
+    auto zero_tail = [&]() __attribute__((always_inline)) {
+      const int kb = k_lo + kStepKeys * (nsteps - 1);
+      const int nvalid = kst_end - kb;                 // staged keys of the step
+      unsigned char* stg = s_ring + ((nsteps - 1) % NST) * G::STAGE;
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int blk = w * IPW + j;
+        if (blk >= G::NBLK) break;                     // uniform
+        if (blk * 64 < kStepKeys * KCH) continue;      // K rows: masked by the scores
+        const int qv = blk * 64 + lane - kStepKeys * KCH;
+        const int e = qv / VCH, p = qv % VCH;
+        const int key0 = (p ^ ((e >> G::VSH) & (VCH - 1))) * CE;   // first key of this lane's chunk
+        T* dst = reinterpret_cast<T*>(stg + blk * 1024 + lane * 16);
+#pragma unroll
+        for (int t = 0; t < CE; ++t)
+          if (key0 + t >= nvalid) dst[t] = from_f32<T>(0.0f);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): the zeros are in LDS
+    };
     auto key_loop = [&](auto ngc) __attribute__((always_inline)) {
       for (int r = 0; r < nrounds; ++r) {
         // round r's loads have landed once only those issued after them remain
         const int later = min((r + D) * P, nsteps) - (r + 1) * P;
         if (later > 0) wait_vm_n(later * my_cnt);
         else wait_vm<0>();
+        if (r == tail_round) zero_tail();
         bar();                             // round r visible; round r-1 no longer read
         const bool early = w >= 4;
         if (early)
           for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
         if constexpr (decltype(ngc)::value > 0) {
           const int s = r * P + ph;
-          if (s < nsteps) {
-            // a branch per step, not per fragment, for the tail zeroing
-            if (k_lo + kStepKeys * (s + 1) > kst_end) compute(ngc, std::true_type{}, s);
-            else compute(ngc, std::false_type{}, s);
-          }
+          if (s < nsteps) compute(ngc, s);
         }
         if (!early)
           for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
@@ -456,7 +485,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       __syncthreads();                     // every wave is done with the ring
       f32x4* red = reinterpret_cast<f32x4*>(s_ring);
       if (ph > 0 && ph < P) {
-        f32x4* dst = red + ((ph - 1) * NW + col) * (kGpw * NO * 64);
+        f32x4* dst = red + ((ph - 1) * (kWaves / P) + col) * (kGpw * NO * 64);
 #pragma unroll
         for (int i = 0; i < kGpw; ++i)
 #pragma unroll
@@ -465,7 +494,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       __syncthreads();
       if (ph == 0) {
         for (int p = 1; p < P; ++p) {
-          const f32x4* srcp = red + ((p - 1) * NW + col) * (kGpw * NO * 64);
+          const f32x4* srcp = red + ((p - 1) * (kWaves / P) + col) * (kGpw * NO * 64);
 #pragma unroll
           for (int i = 0; i < kGpw; ++i)
 #pragma unroll

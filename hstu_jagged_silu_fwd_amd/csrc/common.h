@@ -64,6 +64,18 @@ __device__ __forceinline__ void zero_frag(Frag<float>& f) {
 }
 __device__ __forceinline__ void set_elem(Frag<bf16>& f, int e, float x) { f.v[e] = static_cast<bf16>(x); }
 __device__ __forceinline__ void set_elem(Frag<float>& f, int e, float x) { f.v[e] = x; }
+// All 8 elements at once (bf16: four packed conversions).
+__device__ __forceinline__ void set_frag(Frag<bf16>& f, const float* x) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  f32x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = x[e];
+  f.v = __builtin_convertvector(v, bf16x8);
+}
+__device__ __forceinline__ void set_frag(Frag<float>& f, const float* x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = x[e];
+}
 
 // Fragment read from an LDS row whose 16-byte chunks are XOR-permuted by
 // `sw`: the 8 elements starting at logical chunk `chunk` (bf16: one chunk,
@@ -154,16 +166,25 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// wait_vm with a wave-uniform run-time count (0..47).
+// wait_vm with a wave-uniform run-time count n: waits for the largest of
+// 0, 2, 4, 6, 8, 12, 16, 24 and 32 that does not exceed n (waiting for a few
+// more loads than needed is always safe).  A short tree of uniform branches:
+// a full switch over every count costs more than the waits it saves.
 __device__ __forceinline__ void wait_vm_n(int n) {
-  switch (n) {
-#define HSTU_WAIT_CASE(k) case k: wait_vm<k>(); break;
-#define HSTU_WAIT_8(k) HSTU_WAIT_CASE(k) HSTU_WAIT_CASE(k + 1) HSTU_WAIT_CASE(k + 2) HSTU_WAIT_CASE(k + 3) \
-  HSTU_WAIT_CASE(k + 4) HSTU_WAIT_CASE(k + 5) HSTU_WAIT_CASE(k + 6) HSTU_WAIT_CASE(k + 7)
-    HSTU_WAIT_8(0) HSTU_WAIT_8(8) HSTU_WAIT_8(16) HSTU_WAIT_8(24) HSTU_WAIT_8(32) HSTU_WAIT_8(40)
-#undef HSTU_WAIT_8
-#undef HSTU_WAIT_CASE
-    default: wait_vm<0>(); break;
+  if (n >= 12) {
+    if (n >= 24) {
+      if (n >= 32) wait_vm<32>(); else wait_vm<24>();
+    } else {
+      if (n >= 16) wait_vm<16>(); else wait_vm<12>();
+    }
+  } else if (n >= 6) {
+    if (n >= 8) wait_vm<8>(); else wait_vm<6>();
+  } else if (n >= 4) {
+    wait_vm<4>();
+  } else if (n >= 2) {
+    wait_vm<2>();
+  } else {
+    wait_vm<0>();
   }
 }
 

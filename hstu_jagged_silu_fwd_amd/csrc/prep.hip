@@ -1,8 +1,10 @@
 // Index prep for one layer call: validates the jagged/paged metadata, maps
 // rows to users and pool slots, and builds the attention work list.
-// Workgroup 0 does the validation and the work list, keeping all per-user
-// and per-q-block metadata in LDS while it is built; workgroups 1.. each map
-// a slice of kRowsPerWg new rows to (user, page, slot).
+// Workgroup 0 validates, workgroup 1 builds the work list at the same time
+// (each keeps the per-user and per-q-block metadata in LDS; their scans run
+// inside one wave, so the only workgroup barriers are between phases), and
+// workgroups 2.. each map a slice of kRowsPerWg new rows to (user, page,
+// slot).
 //
 // Work decomposition: the new rows of user u are cut into q-blocks of kQB
 // rows; q-block qb sees keys [0, hist + min(n, (qb+1)*kQB)) (causal).  The key
@@ -52,8 +54,6 @@ struct PrepArgs {
 };
 
 struct PrepShared {
-  int err;
-  int64_t wsum[kPrepWaves];
   int32_t off[kMaxUsers + 1];
   int32_t hist[kMaxUsers];
   int32_t qbb[kMaxUsers + 1];      // first q-block entry of each user
@@ -61,62 +61,47 @@ struct PrepShared {
   int32_t qbf[kMaxQBlocks];        // first work item of each q-block entry
   int32_t qbu[kMaxQBlocks];        // user of each q-block entry
   int32_t pgp[kMaxUsers + 1];      // first flat page index of each user
-  int32_t cnt[16];                 // which candidate budgets fit
+  int32_t cnt[kPrepWaves][16];     // per-wave item counts of the candidate budgets
+  int32_t bad[kPrepWaves];
+  int32_t err, nqb, budget, n_items, b_lo, b_hi;
 };
 
-// Candidate budgets tried at once by the budget search.
+// Candidate budgets tried at once by the budget search: thread t counts for
+// candidate t % kCand over the entries e = t / kCand (mod kPrepThreads / kCand).
 constexpr int kCand = 16;
-constexpr int kCandPerWave = kCand / kPrepWaves;
+constexpr int kCandSlices = kPrepThreads / kCand;
 
-__device__ void set_err(PrepShared& s, int code) { atomicCAS(&s.err, 0, code); }
-
-__device__ __forceinline__ int64_t wave_incl_scan(int64_t x, int lane) {
+// Wave-level exclusive scan; *total receives the wave's sum.  The scans over
+// users and entries run in one wave, 64 values per pass with a carry, so
+// that no workgroup barrier sits between their steps.
+template <typename I>
+__device__ __forceinline__ I wave_excl_scan(I x, int lane, I* total) {
+  I incl = x;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const int64_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
+    const I y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
   }
+  *total = __shfl(incl, kWave - 1, kWave);
+  return incl - x;
+}
+
+template <typename I>
+__device__ __forceinline__ I wave_sum(I x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
   return x;
 }
 
-// In-place exclusive scan of v[0..n) (LDS) by the whole block; returns the total.
-__device__ int64_t block_scan(int32_t* v, int n, PrepShared& s) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int seg = (n + kPrepThreads - 1) / kPrepThreads;
-  const int lo = min(n, tid * seg), hi = min(n, lo + seg);
-  int64_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += v[i];
-  const int64_t incl = wave_incl_scan(sum, lane);
-  if (lane == kWave - 1) s.wsum[w] = incl;
-  __syncthreads();
-  int64_t before = 0, total = 0;
-  for (int i = 0; i < kPrepWaves; ++i) {
-    if (i < w) before += s.wsum[i];
-    total += s.wsum[i];
-  }
-  int64_t run = before + incl - sum;
-  for (int i = lo; i < hi; ++i) {
-    const int32_t x = v[i];
-    v[i] = static_cast<int32_t>(run);
-    run += x;
-  }
-  __syncthreads();
-  return total;
+// ceil(x / y) for 0 <= x < 2^40, y > 0 through double precision: the
+// quotient's fractional part is at least 1/y >= 2^-40 relative to the
+// quotient's integer part whenever it is nonzero, far above the 2^-52
+// rounding of the division, so the ceiling is exact.
+__device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t y) {
+  return static_cast<int64_t>(ceil(static_cast<double>(x) / static_cast<double>(y)));
 }
 
-__device__ int64_t block_sum(int64_t x, PrepShared& s) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  if (lane == 0) s.wsum[w] = x;
-  __syncthreads();
-  int64_t t = 0;
-  for (int i = 0; i < kPrepWaves; ++i) t += s.wsum[i];
-  __syncthreads();
-  return t;
-}
-
-// Entry e -> (user, q-block) by binary search over the user's first entries.
+// Entry e -> user by binary search over the users' first entries.
 __device__ __forceinline__ int entry_user(const int32_t* qbb, int B, int e) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
@@ -152,98 +137,184 @@ __device__ void map_rows(const PrepArgs& a, const PrepShared& s, int slice) {
   }
 }
 
+// Offset and history checks shared by workgroups 0 and 1 (wave 0 only).
+// Returns the first failing code in the order offsets, history lengths.
+__device__ int check_offsets(const PrepArgs& a, const PrepShared& s, int lane) {
+  const int B = a.B;
+  bool bad_off = B == 0 && a.T != 0, bad_hist = false;
+  for (int u0 = 0; u0 < B; u0 += kWave) {
+    const int u = u0 + lane;
+    if (u < B) {
+      const int o0 = s.off[u], o1 = s.off[u + 1];
+      bad_off |= (u == 0 && o0 != 0) || o1 < o0 || (u == B - 1 && o1 != a.T);
+      bad_hist |= s.hist[u] < 0;
+    }
+  }
+  if (__any(bad_off)) return HSTU_DEV_BAD_OFFSETS;
+  if (__any(bad_hist)) return HSTU_DEV_BAD_HIST;
+  return 0;
+}
+
+__device__ void validate(const PrepArgs& a, PrepShared& s);
 __device__ void work_list(const PrepArgs& a, PrepShared& s);
 
 // Workgroup 0 validates the metadata (status), workgroup 1 builds the work
 // list (wl_status), workgroups 2.. map the rows.
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   __shared__ PrepShared s;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  WsHeader* hdr = a.ws.hdr;
+  const int tid = threadIdx.x;
   const int B = a.B;
-  if (tid == 0) s.err = 0;
   for (int u = tid; u <= B; u += kPrepThreads) s.off[u] = a.new_off[u];
   for (int u = tid; u < B; u += kPrepThreads) s.hist[u] = a.hist[u];
   __syncthreads();
   if (blockIdx.x >= 2) {
-    if (B > 0) map_rows(a, s, blockIdx.x - 2);   // B == 0 with rows is rejected below
+    if (B > 0) map_rows(a, s, blockIdx.x - 2);   // B == 0 with rows is rejected by workgroup 0
     return;
   }
-  if (blockIdx.x == 1) {
-    work_list(a, s);
-    return;
-  }
+  if (blockIdx.x == 1) work_list(a, s);
+  else validate(a, s);
+}
 
-  // 1. metadata checks
-  if (tid == 0 && B == 0 && a.T != 0) set_err(s, HSTU_DEV_BAD_OFFSETS);
-  for (int u = tid; u < B; u += kPrepThreads) {
-    const int o0 = s.off[u], o1 = s.off[u + 1];
-    if ((u == 0 && o0 != 0) || o1 < o0 || (u == B - 1 && o1 != a.T)) set_err(s, HSTU_DEV_BAD_OFFSETS);
-    const int c = s.hist[u];
-    if (c < 0) {
-      set_err(s, HSTU_DEV_BAD_HIST);
-    } else if (static_cast<int64_t>(c) + (o1 - o0) > static_cast<int64_t>(a.maxP) * a.ps) {
-      set_err(s, HSTU_DEV_CAPACITY);
+// Workgroup 0: every check of the call's metadata, including every page id
+// in use, into the header's status word (first failure in the order of the
+// status codes' listing in the header, page ids last).
+__device__ void validate(const PrepArgs& a, PrepShared& s) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int B = a.B;
+  if (w == 0) {
+    int err = check_offsets(a, s, lane);
+    bool cap = false, bad_ts = false;
+    int carry = 0;
+    for (int u0 = 0; u0 < B; u0 += kWave) {
+      const int u = u0 + lane;
+      int np = 0;
+      if (u < B) {
+        const int n = s.off[u + 1] - s.off[u];
+        const int64_t len = static_cast<int64_t>(s.hist[u]) + n;
+        cap |= len > static_cast<int64_t>(a.maxP) * a.ps;
+        if (a.ts_off != nullptr)
+          bad_ts |= (u == 0 && a.ts_off[0] != 0) ||
+                    static_cast<int64_t>(a.ts_off[u + 1]) - a.ts_off[u] != len;
+        // pages in use (bounded by the table row once the checks pass)
+        np = static_cast<int>(min<int64_t>((len + a.ps - 1) / a.ps, a.maxP));
+        np = max(np, 0);
+      }
+      int tot;
+      const int ex = wave_excl_scan(np, lane, &tot);
+      if (u < B) s.pgp[u] = carry + ex;
+      carry += tot;
     }
-    if (a.ts_off != nullptr) {
-      if ((u == 0 && a.ts_off[0] != 0) ||
-          static_cast<int64_t>(a.ts_off[u + 1]) - a.ts_off[u] != static_cast<int64_t>(c) + (o1 - o0))
-        set_err(s, HSTU_DEV_BAD_TS);
+    if (err == 0 && __any(cap)) err = HSTU_DEV_CAPACITY;
+    if (err == 0 && __any(bad_ts)) err = HSTU_DEV_BAD_TS;
+    if (lane == 0) {
+      s.pgp[B] = carry;
+      s.err = err;
     }
   }
   __syncthreads();
-  if (s.err == 0) {
-    // page ids of every position in use, over a flat (user, page) index so
-    // that each thread issues its loads back to back
-    for (int u = tid; u < B; u += kPrepThreads)
-      s.pgp[u] = (s.hist[u] + (s.off[u + 1] - s.off[u]) + a.ps - 1) / a.ps;
-    __syncthreads();
-    const int64_t total_pages = block_scan(s.pgp, B, s);
-    if (tid == 0) s.pgp[B] = static_cast<int32_t>(total_pages);
-    __syncthreads();
-    constexpr int kU = 4;
-    bool bad = false;
-    for (int64_t i0 = tid; i0 < total_pages; i0 += kU * kPrepThreads) {
+  const int err = s.err;
+  bool bad = false;
+  if (err == 0) {
+    // page ids of every position in use, over a flat (user, page) index:
+    // thread t takes the contiguous range [t*m, (t+1)*m) in rounds of kU,
+    // finds the user of its first index by a binary search and walks the
+    // users from there, so the kU loads of a round go out back to back
+    const int total_pages = s.pgp[B];
+    constexpr int kU = 16;                           // loads in flight per thread
+    const int m = (total_pages + kPrepThreads - 1) / kPrepThreads;
+    const int i_beg = min(total_pages, tid * m), i_end = min(total_pages, i_beg + m);
+    int u = i_beg < i_end ? entry_user(s.pgp, B, i_beg) : 0;
+    int u_end = s.pgp[u + 1];                        // first flat index past user u
+    for (int i0 = i_beg; i0 < i_end; i0 += kU) {
       int32_t pg[kU];
 #pragma unroll
       for (int k = 0; k < kU; ++k) {
-        const int i = static_cast<int>(i0) + k * kPrepThreads;
+        const int i = i0 + k;
         pg[k] = 0;
-        if (i < total_pages) {
-          int lo = 0, hi = B - 1;              // user owning flat page i
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s.pgp[mid] <= i) lo = mid; else hi = mid - 1;
-          }
-          pg[k] = a.pt[static_cast<size_t>(lo) * a.maxP + (i - s.pgp[lo])];
+        if (i < i_end) {
+          while (i >= u_end) u_end = s.pgp[++u + 1];   // skips users without pages
+          pg[k] = a.pt[static_cast<size_t>(u) * a.maxP + (i - s.pgp[u])];
         }
       }
 #pragma unroll
       for (int k = 0; k < kU; ++k) bad |= pg[k] < 0 || pg[k] >= a.P;
     }
-    if (bad) set_err(s, HSTU_DEV_BAD_PAGE);
   }
+  const bool wave_bad = __any(bad);
+  if (lane == 0) s.bad[w] = wave_bad ? 1 : 0;
   __syncthreads();
-  if (tid == 0) hdr->status = s.err;
+  if (tid == 0) {
+    int code = err;
+    if (code == 0)
+      for (int i = 0; i < kPrepWaves; ++i)
+        if (s.bad[i]) code = HSTU_DEV_BAD_PAGE;
+    a.ws.hdr->status = code;
+  }
 }
 
 // Workgroup 1: the attention work list and the per-entry tables, built at
 // the same time as workgroup 0 validates the metadata.  Its own checks only
 // keep its writes in bounds (offsets and history lengths that workgroup 0
-// rejects make it stop); its result goes to the header's wl_status.
+// rejects make it stop); its result goes to the header's wl_status.  The
+// scans run in wave 0; the candidate counts and the item records use every
+// wave.
 __device__ void work_list(const PrepArgs& a, PrepShared& s) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   WsHeader* hdr = a.ws.hdr;
-  const int B = a.B;
-  if (tid == 0) s.err = 0;
-  __syncthreads();
-  if (tid == 0 && B == 0 && a.T != 0) set_err(s, HSTU_DEV_BAD_OFFSETS);
-  for (int u = tid; u < B; u += kPrepThreads) {
-    const int o0 = s.off[u], o1 = s.off[u + 1];
-    if ((u == 0 && o0 != 0) || o1 < o0 || (u == B - 1 && o1 != a.T)) set_err(s, HSTU_DEV_BAD_OFFSETS);
-    if (s.hist[u] < 0) set_err(s, HSTU_DEV_BAD_HIST);
+  const int B = a.B, H = a.H;
+  constexpr int kBudgetLo = kMinWeight * kMinSteps, kBudgetHi = kMaxWeight * kCapSteps;
+  auto chunk_steps = [](int budget, int weight) { return min(kCapSteps, max(kMinSteps, budget / weight)); };
+  const int64_t target = a.target_items;
+  int64_t b_lo = kBudgetHi, b_hi = kBudgetHi;
+
+  // 1.-2. checks, q-block entries per user, each entry's steps and weight
+  //       (parked in qbn) and the total cost hs = H * sum_e steps_e * w_e
+  if (w == 0) {
+    const int err = check_offsets(a, s, lane);
+    int nqb = 0;
+    int64_t part = 0;
+    if (err == 0) {
+      for (int u0 = 0; u0 < B; u0 += kWave) {
+        const int u = u0 + lane;
+        const int n = u < B ? s.off[u + 1] - s.off[u] : 0;
+        const int nq = (n + kQB - 1) / kQB;
+        int tot;
+        const int ex = nqb + wave_excl_scan(nq, lane, &tot);
+        if (u < B) s.qbb[u] = ex;
+        nqb += tot;
+        const int c = u < B ? s.hist[u] : 0;
+        for (int qb = 0; qb < nq; ++qb) {
+          const int64_t keys = static_cast<int64_t>(c) + min(n, (qb + 1) * kQB);
+          const int steps = static_cast<int>(min<int64_t>((keys + kStepKeys - 1) / kStepKeys, kStepMask));
+          const int wt = step_weight((min(kQB, n - qb * kQB) + 15) / 16);
+          s.qbn[ex + qb] = steps | (wt << kWShift);
+          s.qbu[ex + qb] = u;
+          part += static_cast<int64_t>(steps) * wt;
+        }
+      }
+    }
+    const int64_t hs = wave_sum(part) * H;
+    if (lane == 0) {
+      s.qbb[B] = nqb;
+      s.nqb = nqb;
+      s.err = err;
+    }
+    // 3. the window of the item budget (see the top of this file): with
+    //    S = hs an entry gets at least steps_e * w_e / budget chunks and,
+    //    while no chunk sits at its cap, fewer than steps_e * w_e /
+    //    (budget - w_max) + 1, so the smallest fitting budget lies in
+    //    [S / target, S / (target - H * nqb) + w_max]
+    const int64_t slack = static_cast<int64_t>(H) * nqb;
+    if (err == 0 && target > slack) {
+      b_lo = min<int64_t>(kBudgetHi, max<int64_t>(kBudgetLo, ceil_div(hs, target)));
+      b_hi = min<int64_t>(kBudgetHi, max(b_lo, ceil_div(hs, target - slack) + kMaxWeight));
+    }
+    if (lane == 0) {
+      s.b_lo = static_cast<int32_t>(b_lo);
+      s.b_hi = static_cast<int32_t>(b_hi);
+    }
   }
   __syncthreads();
   if (s.err != 0) {
@@ -256,94 +327,63 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
     }
     return;
   }
+  const int nqb = s.nqb;
+  b_lo = s.b_lo;
+  b_hi = s.b_hi;
 
-  // 2. q-block entries per user
-  for (int u = tid; u < B; u += kPrepThreads) s.qbb[u] = (s.off[u + 1] - s.off[u] + kQB - 1) / kQB;
-  __syncthreads();
-  const int nqb = static_cast<int>(block_scan(s.qbb, B, s));
-  if (tid == 0) s.qbb[B] = nqb;
-  __syncthreads();
-
-  // 3. item budget (see the top of this file).  The entries' step counts and
-  //    weights are parked in qbn meanwhile.  With S = H * sum_e steps_e * w_e
-  //    an entry gets at least steps_e * w_e / budget chunks and, while no
-  //    chunk sits at its cap, fewer than steps_e * w_e / (budget - w_max) + 1,
-  //    so the smallest fitting budget lies in [S / target, S / (target -
-  //    H * nqb) + w_max]; kCand candidates spread over that window are tried
-  //    at once (four per wave) and the smallest that fits is taken (the top
-  //    one when none does, which can only happen through the cap).
-  int64_t part = 0;
-  for (int e = tid; e < nqb; e += kPrepThreads) {
-    const int u = entry_user(s.qbb, B, e);
-    const int qb = e - s.qbb[u];
-    const int n = s.off[u + 1] - s.off[u];
-    const int keys = s.hist[u] + min(n, (qb + 1) * kQB);
-    const int steps = (keys + kStepKeys - 1) / kStepKeys;
-    const int wt = step_weight((min(kQB, n - qb * kQB) + 15) / 16);
-    s.qbn[e] = steps | (wt << kWShift);
-    s.qbu[e] = u;
-    part += static_cast<int64_t>(steps) * wt;
-  }
-  const int64_t hs = block_sum(part, s) * a.H;       // ends with a barrier
-  const int64_t target = a.target_items;
-  const int64_t slack = static_cast<int64_t>(a.H) * nqb;
-  auto chunk_steps = [](int budget, int weight) { return min(kCapSteps, max(kMinSteps, budget / weight)); };
-  constexpr int kBudgetLo = kMinWeight * kMinSteps, kBudgetHi = kMaxWeight * kCapSteps;
-  int budget = kBudgetHi;
-  if (target > slack) {
-    const int64_t b_lo = min<int64_t>(kBudgetHi, max<int64_t>(kBudgetLo, (hs + target - 1) / target));
-    const int64_t b_hi = min<int64_t>(kBudgetHi, max(b_lo, (hs + (target - slack) - 1) / (target - slack) + kMaxWeight));
-    auto cand = [&](int k) {
-      return static_cast<int>(k == kCand - 1 ? b_hi : b_lo + (b_hi - b_lo) * k / (kCand - 1));
-    };
-    // whether each of this wave's kCandPerWave budgets fits the target; the
-    // wave counts them in one pass and reduces them together, so that the
-    // shuffle latencies overlap.  Per-lane counts saturate at 2^24 (far
-    // above any target), which keeps the lane sums inside int32.
-    int bud[kCandPerWave], cnt[kCandPerWave];
-#pragma unroll
-    for (int k = 0; k < kCandPerWave; ++k) {
-      bud[k] = cand(w * kCandPerWave + k);
-      cnt[k] = 0;
-    }
-    for (int e = lane; e < nqb; e += kWave) {
+  //    kCand budgets spread over the window are counted at once, and the
+  //    smallest that fits the target is taken (the top one when none does,
+  //    which can only happen through the cap)
+  const int k = tid % kCand, sl = tid / kCand;
+  const int bud = static_cast<int>(k == kCand - 1 ? b_hi : b_lo + (b_hi - b_lo) * k / (kCand - 1));
+  {
+    const int L4 = chunk_steps(bud, 4), L6 = chunk_steps(bud, 6), L10 = chunk_steps(bud, 10);
+    int cnt = 0;
+    for (int e = sl; e < nqb; e += kCandSlices) {
       const int v = s.qbn[e];
       const int steps = v & kStepMask, wt = v >> kWShift;
-#pragma unroll
-      for (int k = 0; k < kCandPerWave; ++k) {
-        const int L = chunk_steps(bud[k], wt);
-        cnt[k] = min(cnt[k] + (steps + L - 1) / L, 1 << 24);
-      }
+      const int L = wt == 4 ? L4 : (wt == 6 ? L6 : L10);
+      cnt = min(cnt + (steps + L - 1) / L, 1 << 24);   // far above any target; sums stay in int32
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-      for (int k = 0; k < kCandPerWave; ++k) cnt[k] += __shfl_xor(cnt[k], o, kWave);
-    if (lane == 0) {
-#pragma unroll
-      for (int k = 0; k < kCandPerWave; ++k) {
-        const int kk = w * kCandPerWave + k;
-        s.cnt[kk] = (kk == kCand - 1 || static_cast<int64_t>(cnt[k]) * a.H <= target) ? 1 : 0;
-      }
-    }
-    __syncthreads();
-    int j = kCand - 1;
-    for (int k = kCand - 1; k >= 0; --k)
-      if (s.cnt[k]) j = k;
-    budget = cand(j);
-  }
-
-  // 4. chunks per entry, then first item of each entry
-  __syncthreads();                           // every wave is done counting
-  for (int e = tid; e < nqb; e += kPrepThreads) {
-    const int v = s.qbn[e];
-    const int L = chunk_steps(budget, v >> kWShift);
-    const int nch = ((v & kStepMask) + L - 1) / L;
-    s.qbn[e] = nch;
-    s.qbf[e] = nch * a.H;
+    cnt += __shfl_xor(cnt, 16, kWave);
+    cnt += __shfl_xor(cnt, 32, kWave);
+    if (lane < kCand) s.cnt[w][lane] = cnt;
   }
   __syncthreads();
-  const int64_t n_items = block_scan(s.qbf, nqb, s);
+
+  // 4. chunks per entry and first item of each entry (wave 0)
+  if (w == 0) {
+    int j = kCand - 1;
+    if (lane < kCand) {
+      int64_t c = 0;
+      for (int i = 0; i < kPrepWaves; ++i) c += s.cnt[i][lane];
+      if (c * H <= target) j = lane;
+    }
+    const uint64_t fits = __ballot(j == lane && lane < kCand);
+    const int jj = fits ? __builtin_ctzll(fits) : kCand - 1;
+    const int budget = __shfl(bud, jj, kWave);       // lanes 0..15 hold the candidates in order
+    int64_t n_items = 0;
+    for (int e0 = 0; e0 < nqb; e0 += kWave) {
+      const int e = e0 + lane;
+      int nch = 0;
+      if (e < nqb) {
+        const int v = s.qbn[e];
+        const int L = chunk_steps(budget, v >> kWShift);
+        nch = ((v & kStepMask) + L - 1) / L;
+        s.qbn[e] = nch;
+      }
+      int64_t tot;
+      const int64_t ex = n_items + wave_excl_scan(static_cast<int64_t>(nch) * H, lane, &tot);
+      if (e < nqb) s.qbf[e] = static_cast<int32_t>(min<int64_t>(ex, a.item_cap));
+      n_items += tot;
+    }
+    if (lane == 0) {
+      s.budget = budget;
+      s.n_items = static_cast<int32_t>(min<int64_t>(n_items, static_cast<int64_t>(a.item_cap) + 1));
+    }
+  }
+  __syncthreads();
+  const int n_items = s.n_items;
   if (n_items > a.item_cap) {
     if (tid == 0) {
       hdr->wl_status = HSTU_DEV_CAPACITY;
@@ -356,7 +396,7 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
   }
 
   // 5. the work list (one thread per item) and the per-entry tables used by
-  //    the norm / output kernel
+  //    the norm kernel
   for (int e = tid; e < nqb; e += kPrepThreads) {
     const int u = s.qbu[e], qb = e - s.qbb[u];
     a.ws.qb_first[e] = s.qbf[e];
@@ -364,13 +404,14 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
     a.ws.qb_row0[e] = s.off[u] + qb * kQB;
     a.ws.qb_rows[e] = min(kQB, s.off[u + 1] - s.off[u] - qb * kQB);
   }
-  for (int i = tid; i < n_items; i += kPrepThreads) {
-    int lo = 0, hi = nqb - 1;                // last entry whose first item <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s.qbf[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo, u = s.qbu[e], qb = e - s.qbb[u], nch = s.qbn[e];
+  // thread t writes the contiguous items [t*m, (t+1)*m): one binary search
+  // for the entry of its first item, then a walk over the entries
+  const int m = (n_items + kPrepThreads - 1) / kPrepThreads;
+  const int i_beg = min(n_items, tid * m), i_end = min(n_items, i_beg + m);
+  int e = i_beg < i_end ? entry_user(s.qbf, nqb, i_beg) : 0;   // last entry whose first item <= i
+  for (int i = i_beg; i < i_end; ++i) {
+    while (e + 1 < nqb && s.qbf[e + 1] <= i) ++e;
+    const int u = s.qbu[e], qb = e - s.qbb[u], nch = s.qbn[e];
     const int r = i - s.qbf[e], h = r / nch, kc = r - h * nch;
     const int n = s.off[u + 1] - s.off[u];
     const int c = s.hist[u];
@@ -388,9 +429,9 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
 
   if (tid == 0) {
     hdr->wl_status = 0;
-    hdr->n_items = static_cast<int32_t>(n_items);
+    hdr->n_items = n_items;
     hdr->n_qb = nqb;
-    hdr->item_budget = budget;
+    hdr->item_budget = s.budget;
     hdr->counter = 0;
   }
 }

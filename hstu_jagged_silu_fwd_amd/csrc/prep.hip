@@ -30,13 +30,15 @@ constexpr int kStepKeys = 32;   // attention key step
 constexpr int kMinSteps = 4;    // shortest chunk: a step for each of up to four phases
 constexpr int kCapSteps = kMaxChunkKeys / kStepKeys;
 // Cost of one 32-key step by the entry's query groups G, in units of about a
-// tenth of a microsecond: the attention workgroup splits the steps of a
-// q-block with G <= 4 over four phases, with G <= 8 over two, and multiplies
-// every step with all its waves otherwise, so the time per step is a step
-// function of G (measured on MI355X: about 0.85, 1.3 and 2.1 us).
-__device__ __forceinline__ int step_weight(int groups) { return groups <= 4 ? 4 : (groups <= 8 ? 6 : 10); }
-constexpr int kMinWeight = 4;
-constexpr int kMaxWeight = 10;
+// tenth of a microsecond (measured per step on MI355X: about 0.6 us up to
+// two groups, 0.7 up to four, 0.87 up to eight -- the attention workgroup
+// splits those steps over four or two phases -- and 1.5 to 1.8 us beyond,
+// where every wave multiplies every step).
+__device__ __forceinline__ int step_weight(int groups) {
+  return groups <= 2 ? 6 : (groups <= 4 ? 7 : (groups <= 8 ? 9 : (groups <= 12 ? 15 : 18)));
+}
+constexpr int kMinWeight = 6;
+constexpr int kMaxWeight = 18;
 constexpr int kWShift = 25;     // entry word: steps (bits 0..24) | weight << 25
 constexpr int kStepMask = (1 << kWShift) - 1;
 constexpr int kRowsPerThread = 4;
@@ -337,12 +339,11 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
   const int k = tid % kCand, sl = tid / kCand;
   const int bud = static_cast<int>(k == kCand - 1 ? b_hi : b_lo + (b_hi - b_lo) * k / (kCand - 1));
   {
-    const int L4 = chunk_steps(bud, 4), L6 = chunk_steps(bud, 6), L10 = chunk_steps(bud, 10);
     int cnt = 0;
     for (int e = sl; e < nqb; e += kCandSlices) {
       const int v = s.qbn[e];
       const int steps = v & kStepMask, wt = v >> kWShift;
-      const int L = wt == 4 ? L4 : (wt == 6 ? L6 : L10);
+      const int L = chunk_steps(bud, wt);
       cnt = min(cnt + (steps + L - 1) / L, 1 << 24);   // far above any target; sums stay in int32
     }
     cnt += __shfl_xor(cnt, 16, kWave);

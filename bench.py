@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-events", action="store_true", help="skip the per-kernel event pass (no roofline or stage split)")
+    ap.add_argument("--kvcache", action="store_true",
+                    help="measure the KV cache manager (plan on the host, page tables on the device) "
+                         "on a serving stream instead of the layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -281,8 +284,75 @@ def cpu_baseline(wl, B, R, min_seconds=10.0):
                        f"all {wl.layers} layers, every key), fp64 numpy, {dt:.1f} s")
 
 
+# ---------------------------------------------------------------------------
+# KV cache manager measurement: a stream of batches of 64 users drawn with
+# Zipf(1.2) popularity from 4096 users, U{1..512} new tokens each, over the
+# 8-layer serving pool (2^17 pages of 32 tokens, 1040 pages per user row,
+# 1024 cached users at most).  Misses resend the whole sequence, as in the
+# serving workload; a sequence restarts once it would pass 4096 tokens, so
+# that any batch fits the pool.  Timed: the host plan (lookup, eviction,
+# allocation) and the device page-table build of every batch.
+# ---------------------------------------------------------------------------
+def kvcache_bench(args):
+    import numpy as np
+    import torch
+    from hstu_jagged_silu_fwd_amd.kvcache import KVCache
+    L, P, ps, maxP, users, pop, B, cap = 8, 1 << 17, 32, 1040, 1024, 4096, 64, 4096
+    rng = np.random.default_rng(args.seed)
+    kv = KVCache(num_layers=L, num_pages=P, page_size=ps, max_pages_per_user=maxP, max_users=users)
+    length = {}
+    def batch():
+        ids = []
+        while len(ids) < B:
+            u = int(min(rng.zipf(1.2), pop))
+            if u not in ids:
+                ids.append(u)
+        cached = kv.lookup(ids)
+        n = []
+        for u, c in zip(ids, cached.tolist()):
+            k = int(rng.integers(1, 513))
+            full = length.get(u, 0) + k
+            if full > cap:                            # restart an over-long user
+                kv.evict(u)
+                full, c = k, -1
+            length[u] = full
+            n.append(k if c >= 0 else full)
+        return ids, n
+    for _ in range(args.warmup * 20):
+        ids, n = batch()
+        kv.build_tables(kv.plan(ids, n))
+    torch.cuda.synchronize()
+    nb = args.steps * 5
+    host, dev, hits, upd, ev = 0.0, 0.0, 0, 0, 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(nb):
+        ids, n = batch()
+        t0 = time.perf_counter()
+        p = kv.plan(ids, n)
+        host += time.perf_counter() - t0
+        e0.record()
+        kv.build_tables(p)
+        e1.record()
+        torch.cuda.synchronize()
+        dev += e0.elapsed_time(e1) * 1e-3
+        hits += int((p.hist_len > 0).sum())
+        upd += p.updates.shape[0]
+        ev += len(p.evicted)
+    print(json.dumps({
+        "metric": "KV cache plan + page-table build per batch", "value": (host + dev) / nb * 1e6,
+        "unit": "us per batch of 64 users", "higher_is_better": False, "n_gpus": 1, "batches": nb,
+        "host_plan_us": host / nb * 1e6, "device_tables_us": dev / nb * 1e6,
+        "hit_rate": hits / (nb * B), "page_updates_per_batch": upd / nb, "evictions_per_batch": ev / nb,
+        "config": {"workload": "kvcache-serving-stream", "layers": L, "pool_pages": P, "page_size": ps,
+                   "max_pages_per_user": maxP, "max_users": users, "population": pop, "batch": B,
+                   "popularity": "zipf(1.2)", "new": "U{1..512}", "max_tokens": cap}}), flush=True)
+
+
 def main():
     args = parse()
+    if args.kvcache:
+        kvcache_bench(args)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return

@@ -42,8 +42,11 @@ class HSTUStack:
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         self._ws = None
 
-    def desc(self, total_new: int) -> _lib.LayerDesc:
-        return _lib.make_desc(total_new=total_new, **self.common)
+    def desc(self, total_new: int, num_users: Optional[int] = None) -> _lib.LayerDesc:
+        kw = dict(self.common)
+        if num_users is not None:
+            kw["num_users"] = num_users
+        return _lib.make_desc(total_new=total_new, **kw)
 
     def _dev(self, a, dtype):
         t = torch.as_tensor(a)
@@ -76,18 +79,28 @@ class HSTUStack:
 
     def layer(self, l: int, x: torch.Tensor, new_offsets: torch.Tensor, hist_len: torch.Tensor,
               y: torch.Tensor, workspace: Optional[torch.Tensor] = None, timestamps=None,
-              ts_offsets=None, stream=None, stage_events=None) -> None:
+              ts_offsets=None, stream=None, stage_events=None, page_table=None) -> None:
+        """Layer l over a batch; page_table [B, max_pages] overrides the layer's
+        own table (the batch size is then taken from new_offsets)."""
         T = int(x.shape[0])
-        ws = self.workspace(T) if workspace is None else workspace
         L = self.layers[l]
-        _lib.layer_fwd(self.desc(T), x, new_offsets, hist_len, L["page_table"], self.k_pool,
+        nu = None if page_table is None else int(new_offsets.shape[0]) - 1
+        desc = self.desc(T, nu)
+        ws = self.workspace(T) if workspace is None else workspace
+        if nu is not None and workspace is None:
+            need = _lib.workspace_size(desc)
+            if ws.numel() < need:
+                self._ws = ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        _lib.layer_fwd(desc, x, new_offsets, hist_len, L["page_table"] if page_table is None else page_table, self.k_pool,
                        self.v_pool, L["w1t"], L["w2t"], L["pos_bias"], y, ws,
                        ts_bias=L["ts_bias"], timestamps=timestamps, ts_offsets=ts_offsets,
                        stream=stream, stage_events=stage_events)
 
     def forward(self, x, new_offsets, hist_len, timestamps=None, ts_offsets=None,
-                stream=None, return_all: bool = False):
-        """Run every layer; returns the last layer's output (or all outputs)."""
+                stream=None, return_all: bool = False, page_tables=None):
+        """Run every layer; returns the last layer's output (or all outputs).
+        page_tables: optional per-layer [B, max_pages] tables (e.g. a KV cache
+        plan's, from KVCache.build_tables) instead of the layers' own."""
         x = self._dev(x, self.tdtype)
         off = self._dev(new_offsets, torch.int32)
         hl = self._dev(hist_len, torch.int32)
@@ -96,7 +109,8 @@ class HSTUStack:
         outs = []
         for l in range(len(self.layers)):
             y = torch.empty_like(x)
-            self.layer(l, x, off, hl, y, timestamps=ts, ts_offsets=tso, stream=stream)
+            self.layer(l, x, off, hl, y, timestamps=ts, ts_offsets=tso, stream=stream,
+                       page_table=None if page_tables is None else page_tables[l])
             outs.append(y)
             x = y
         return outs if return_all else outs[-1]

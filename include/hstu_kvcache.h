@@ -1,0 +1,139 @@
+/*
+ * hstu_kvcache.h -- C ABI of the paged KV cache manager of libhstu: lookup,
+ * allocation and least-recently-used eviction of users' pages in the paged
+ * GPU KV pool that the layer (include/hstu.h) reads and appends to, plus a
+ * device builder of the per-layer page tables of a batch.
+ *
+ * Source: NVIDIA technical blog "Deploying an HSTU generative recommender
+ * with NVIDIA Dynamo-Triton", section "Why serving large sequential
+ * recommenders is hard": the GPU cache is a paged KV data table supporting
+ * lookup, allocation, append and eviction, and when GPU cache space runs
+ * short, old users are evicted under an LRU-like policy.  The exact policy
+ * below (whole users evicted, least recently planned first, never a user of
+ * the batch being planned, all-or-nothing plans, last-in-first-out page
+ * reuse) is this library's reading of that passage.
+ *
+ * Model.  The cache serves L layers that share one pool of P pages of
+ * page_size token slots (every layer of a user holds the same number of
+ * pages, in pages distinct from every other (user, layer)).  A user is a
+ * 64-bit id; a cached user occupies one of max_users slots and has c cached
+ * tokens, held in ceil(c / page_size) pages per layer.
+ *
+ * hstu_kvcache_plan(batch of B distinct users, n_new[b] new tokens each):
+ *   1. lookup: a cached user is a hit with hist_len = c, any other user a
+ *      miss with hist_len = 0 (its whole sequence is then sent as new rows);
+ *   2. every user needs ceil((hist_len + n_new) / page_size) pages per layer;
+ *      a miss also needs a slot.  If the free pages and slots, plus those of
+ *      every cached user outside the batch, cannot cover the batch, the plan
+ *      fails with HSTU_KV_FULL and changes nothing;
+ *   3. while pages or slots are short, the least recently used cached user
+ *      outside the batch is evicted: its pages (layer by layer, page index
+ *      by page index) go onto the free-page stack and its slot onto the
+ *      free-slot stack;
+ *   4. users are served in batch order: a miss pops a slot; the missing pages
+ *      of layer 0, then layer 1, ... are popped off the free-page stack
+ *      (initially pages 0, 1, 2, ... come off first); each assignment is
+ *      reported as an update record {slot, layer, page index, page id};
+ *   5. the batch's users become the most recently used, in batch order (the
+ *      last one most recent), and each user's cached length becomes
+ *      hist_len + n_new (the layer forward appends those tokens).
+ * A user whose tokens would exceed max_pages_per_user * page_size makes the
+ * plan fail with HSTU_KV_TOO_LONG, changing nothing.
+ *
+ * The page directory is a device int32 array [max_users][L][max_pages] that
+ * the caller allocates (hstu_kvcache_directory_elems) and keeps: row (slot,
+ * layer) lists the slot's page ids in position order.  hstu_kv_tables_build
+ * applies a plan's update records to it and gathers the batch's page tables
+ * [L][B][max_pages] for hstu_layer_fwd (entries past a user's pages are
+ * whatever the directory holds; the layer only reads positions in use).
+ *
+ * Conventions: the manager is host-only (no HIP calls); its handle is owned
+ * by the caller and is not thread-safe.  Pointers passed to the manager are
+ * HOST pointers; pointers passed to hstu_kv_tables_build are DEVICE pointers
+ * and its work is enqueued on hip_stream.  Errors return a nonzero status
+ * and leave the cache unchanged.
+ */
+#ifndef HSTU_KVCACHE_H_
+#define HSTU_KVCACHE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_KV_OK = 0,
+  HSTU_KV_INVALID_ARG = -1,   /* null pointer, bad size, duplicate user in a batch */
+  HSTU_KV_FULL = -10,         /* the batch needs more pages or slots than can be freed */
+  HSTU_KV_TOO_LONG = -11,     /* a user's tokens exceed max_pages_per_user * page_size */
+  HSTU_KV_CAPACITY = -12,     /* an output array is too small */
+  HSTU_KV_HIP = -13           /* a HIP launch failed (hstu_kv_tables_build) */
+} hstu_kv_status;
+
+typedef struct hstu_kvcache hstu_kvcache;
+
+/* One page assignment made by a plan. */
+typedef struct {
+  int32_t slot, layer, page_index, page_id;
+} hstu_kv_update;
+
+/* A cache over num_pages pages of page_size tokens for num_layers layers,
+ * up to max_users cached users of at most max_pages_per_user pages per
+ * layer.  Returns NULL on invalid sizes (any < 1, page_size not a power of
+ * two, num_pages >= 2^31) or allocation failure. */
+hstu_kvcache* hstu_kvcache_create(int32_t num_layers, int64_t num_pages, int32_t page_size,
+                                  int32_t max_pages_per_user, int32_t max_users);
+void hstu_kvcache_destroy(hstu_kvcache* cache);
+
+/* Elements of the device page directory: max_users * num_layers * max_pages. */
+int64_t hstu_kvcache_directory_elems(const hstu_kvcache* cache);
+
+/* Plans one batch (steps 1-5 above).
+ *   user_ids[B], n_new[B] (n_new >= 0)                       in
+ *   hist_len[B]  cached tokens reused per user (0 = miss)    out
+ *   slots[B]     directory slot per user                     out
+ *   updates[update_cap], *n_updates  page assignments        out
+ *   evicted[evicted_cap], *n_evicted user ids evicted        out (may be NULL
+ *                                    when evicted_cap == 0; evictions are then
+ *                                    still made, only not reported)
+ * update_cap must be at least num_layers * sum_b ceil((hist_len + n_new) /
+ * page_size) (num_layers * B * max_pages_per_user always suffices), else
+ * HSTU_KV_CAPACITY and no change; evicted ids past evicted_cap are dropped
+ * from the report. */
+hstu_kv_status hstu_kvcache_plan(hstu_kvcache* cache, int32_t B, const int64_t* user_ids,
+                                 const int32_t* n_new, int32_t* hist_len, int32_t* slots,
+                                 hstu_kv_update* updates, int32_t update_cap, int32_t* n_updates,
+                                 int64_t* evicted, int32_t evicted_cap, int32_t* n_evicted);
+
+/* Cached tokens of each user (-1 when not cached); changes nothing, not even
+ * the recency order. */
+hstu_kv_status hstu_kvcache_lookup(const hstu_kvcache* cache, int32_t B, const int64_t* user_ids,
+                                   int32_t* cached_len);
+
+/* Evicts one user explicitly (its pages and slot are freed, pushed as in
+ * step 3).  *found = 1 when the user was cached, else 0. */
+hstu_kv_status hstu_kvcache_evict(hstu_kvcache* cache, int64_t user_id, int32_t* found);
+
+/* Free pages and cached users. */
+hstu_kv_status hstu_kvcache_stats(const hstu_kvcache* cache, int64_t* free_pages,
+                                  int32_t* cached_users);
+
+/* Applies update records to the device page directory and gathers the page
+ * tables of a planned batch:
+ *   directory  [max_users][num_layers][max_pages] int32 (device, in/out)
+ *   updates    [n_updates] hstu_kv_update (device)
+ *   slots      [B] int32 (device)
+ *   tables     [num_layers][B][max_pages] int32 (device, out)
+ * Two kernels on hip_stream (the scatter, then the gather).  Update records
+ * and slots must come from plans of a cache with these sizes. */
+hstu_kv_status hstu_kv_tables_build(int32_t* directory, int32_t num_layers, int32_t max_users,
+                                    int32_t max_pages, const hstu_kv_update* updates,
+                                    int32_t n_updates, const int32_t* slots, int32_t B,
+                                    int32_t* tables, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSTU_KVCACHE_H_ */

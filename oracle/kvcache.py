@@ -1,0 +1,136 @@
+"""Reference model of the paged KV cache manager.  TEST INFRASTRUCTURE.
+
+The NVIDIA blog "Deploying an HSTU generative recommender with NVIDIA
+Dynamo-Triton" (section "Why serving large sequential recommenders is hard")
+says the GPU KV cache is a paged data table supporting lookup, allocation,
+append and eviction, and that when GPU cache space runs short old users are
+evicted under an LRU-like policy.  The pages give no further rule; the rule
+modelled here is the one the library header states:
+
+  * a plan takes a batch of distinct users with n_new tokens each; a cached
+    user is a hit (history length = its cached tokens), any other a miss
+    (history 0);
+  * a user holds ceil(tokens / page_size) pages in every layer;
+  * if the batch cannot fit even after freeing everything held by users
+    outside it, the plan fails and changes nothing;
+  * otherwise, while pages or slots are short, the cached user outside the
+    batch whose last plan is oldest is evicted: its pages go onto the
+    free-page stack layer by layer and index by index, its slot onto the
+    free-slot stack;
+  * users are served in batch order: a miss takes the top free slot; missing
+    pages are taken off the top of the free-page stack, layer 0 first, and
+    each assignment is reported as (slot, layer, page index, page id);
+  * every batch user's last-use time becomes the clock value of its place in
+    the batch (the last one most recent), and its cached length history +
+    n_new.
+
+This model keeps a last-use time per user and evicts by minimum time; the
+library keeps a linked recency list.  The two agree exactly on every
+output, which the tests check on random traces.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Sequence, Tuple
+
+
+class CacheFull(Exception):
+    pass
+
+
+class TooLong(Exception):
+    pass
+
+
+@dataclass
+class _User:
+    slot: int
+    length: int
+    pages: List[List[int]]      # per layer, page ids in position order
+    last_use: int
+
+
+@dataclass
+class RefKVCache:
+    num_layers: int
+    num_pages: int
+    page_size: int
+    max_pages_per_user: int
+    max_users: int
+    users: Dict[int, _User] = field(default_factory=dict)
+    free_pages: List[int] = field(default_factory=list)    # top = end of the list
+    free_slots: List[int] = field(default_factory=list)
+    clock: int = 0
+
+    def __post_init__(self):
+        self.free_pages = list(range(self.num_pages - 1, -1, -1))
+        self.free_slots = list(range(self.max_users - 1, -1, -1))
+
+    def _pages_for(self, tokens: int) -> int:
+        return -(-tokens // self.page_size)
+
+    def lookup(self, ids: Sequence[int]) -> List[int]:
+        return [self.users[i].length if i in self.users else -1 for i in ids]
+
+    def _evict(self, uid: int) -> None:
+        u = self.users.pop(uid)
+        for layer_pages in u.pages:
+            for p in layer_pages:
+                self.free_pages.append(p)
+        self.free_slots.append(u.slot)
+
+    def evict(self, uid: int) -> bool:
+        if uid not in self.users:
+            return False
+        self._evict(uid)
+        return True
+
+    def plan(self, ids: Sequence[int], n_new: Sequence[int]):
+        """Returns (hist_len, slots, updates, evicted) or raises ValueError,
+        CacheFull or TooLong (state unchanged)."""
+        ids, n_new = list(ids), list(n_new)
+        if len(set(ids)) != len(ids) or any(n < 0 for n in n_new):
+            raise ValueError("duplicate user or negative count")
+        hist = [self.users[i].length if i in self.users else 0 for i in ids]
+        need = []
+        for i, h, n in zip(ids, hist, n_new):
+            if h + n > self.max_pages_per_user * self.page_size:
+                raise TooLong(i)
+            held = len(self.users[i].pages[0]) if i in self.users else 0
+            need.append(self._pages_for(h + n) - held)
+        need_pages = self.num_layers * sum(need)
+        misses = sum(1 for i in ids if i not in self.users)
+        outside = [i for i in self.users if i not in set(ids)]
+        can_free = sum(self.num_layers * len(self.users[i].pages[0]) for i in outside)
+        if len(self.free_pages) + can_free < need_pages or len(self.free_slots) + len(outside) < misses:
+            raise CacheFull()
+        evicted = []
+        while len(self.free_pages) < need_pages or len(self.free_slots) < misses:
+            victim = min(outside, key=lambda i: self.users[i].last_use)
+            outside.remove(victim)
+            self._evict(victim)
+            evicted.append(victim)
+        slots, updates = [], []
+        for i, h, n, k in zip(ids, hist, n_new, need):
+            if i not in self.users:
+                self.users[i] = _User(self.free_slots.pop(), 0,
+                                      [[] for _ in range(self.num_layers)], 0)
+            u = self.users[i]
+            for layer in range(self.num_layers):
+                for _ in range(k):
+                    p = self.free_pages.pop()
+                    updates.append((u.slot, layer, len(u.pages[layer]), p))
+                    u.pages[layer].append(p)
+            u.length = h + n
+            slots.append(u.slot)
+        for i in ids:
+            self.clock += 1
+            self.users[i].last_use = self.clock
+        return hist, slots, updates, evicted
+
+    def page_table(self, uid: int, layer: int) -> List[int]:
+        return list(self.users[uid].pages[layer])
+
+    def owned_pages(self) -> List[Tuple[int, int, int]]:
+        """(page, user, layer) for every held page."""
+        return [(p, uid, l) for uid, u in self.users.items() for l, ps in enumerate(u.pages) for p in ps]

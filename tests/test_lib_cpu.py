@@ -26,6 +26,22 @@ def test_exports_every_header_function():
         assert hasattr(lib, n), n
 
 
+def test_exports_every_kvcache_header_function():
+    """include/hstu_kvcache.h: every declared function is exported."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(_lib.HEADER_PATH), "hstu_kvcache.h")
+    src = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    names = re.findall(r"^\s*(?:hstu_kv_status|hstu_kvcache\*|void|int64_t)\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    assert set(names) == {"hstu_kvcache_create", "hstu_kvcache_destroy", "hstu_kvcache_directory_elems",
+                          "hstu_kvcache_plan", "hstu_kvcache_lookup", "hstu_kvcache_evict",
+                          "hstu_kvcache_stats", "hstu_kv_tables_build"}
+    lib = hs.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
 def test_desc_struct_layout():
     # int32 x6, int64, int32 x5, float x2, int32 -> 64 bytes with the int64 aligned at 24.
     assert ctypes.sizeof(_lib.LayerDesc) == 64

@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--kvcache", action="store_true",
                     help="measure the KV cache manager (plan on the host, page tables on the device) "
                          "on a serving stream instead of the layer")
+    ap.add_argument("--kvhost", action="store_true",
+                    help="measure the host tier: page-copy bandwidth and a user's onboard time "
+                         "against recomputing its history")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -348,8 +351,88 @@ def kvcache_bench(args):
                    "popularity": "zipf(1.2)", "new": "U{1..512}", "max_tokens": cap}}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Host tier measurement on the 3-layer bf16 batch-8 shapes (hidden 512, 4
+# heads of 128, 32-token pages; a page of one layer is 32 KiB of K and 32
+# KiB of V): bandwidth of the page-copy kernel offloading and onboarding
+# 4096 pages, and, for one user with a 4096-token history, the onboard of
+# its 3 x 128 pages against recomputing the history through the 3 layers
+# (the layer call with no cache on 4096 new rows).
+# ---------------------------------------------------------------------------
+def kvhost_bench(args):
+    import numpy as np
+    import torch
+    from hstu_jagged_silu_fwd_amd.kvcache import KVCache, Plan
+    from hstu_jagged_silu_fwd_amd.stack import HSTUStack
+    from workloads import B8_KV_HIT, make_workload
+    H, d, ps, L, npg = 4, 128, 32, 3, 4096
+    P = 2 * npg
+    kv = KVCache(num_layers=L, num_pages=P, page_size=ps, max_pages_per_user=160, max_users=4, host_pages=npg)
+    kp = torch.zeros((P, H, ps, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((P, H, d, ps), dtype=torch.bfloat16, device="cuda")
+    page_bytes = 2 * H * ps * d * 2
+    empty = (np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros((0, 4), np.int32), [])
+    def run(copies):
+        kv.copy_pages(Plan(*empty, copies), kp, vp)
+    off = np.array([[0, i, i, 0] for i in range(npg)], np.int32)
+    on = np.array([[1, npg + i, i, 0] for i in range(npg)], np.int32)
+    for _ in range(3):
+        run(off); run(on)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_off = t_on = 0.0
+    reps = 10
+    for _ in range(reps):
+        e[0].record(); run(off); e[1].record(); run(on); e[2].record()
+        torch.cuda.synchronize()
+        t_off += e[0].elapsed_time(e[1]); t_on += e[1].elapsed_time(e[2])
+    t_off, t_on = t_off / reps * 1e-3, t_on / reps * 1e-3
+    # one user: onboard 3 x 128 pages vs recompute 4096 tokens through 3 layers
+    upages = (4096 // ps) * L
+    on_user = on[:upages]
+    for _ in range(3):
+        run(on_user)
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(reps):
+        run(on_user)
+    e[1].record()
+    torch.cuda.synchronize()
+    t_user = e[0].elapsed_time(e[1]) / reps * 1e-3
+    wl = make_workload(B8_KV_HIT, seed=0, B=1, hist=("const", 0), new=("const", 4096))
+    st = HSTUStack(num_users=1, num_heads=H, head_dim=d, page_size=ps, num_pool_pages=P, max_pages_per_user=160,
+                   pos_buckets=wl.pos_buckets, pos_mbits=wl.pos_mbits, attn_scale=wl.attn_scale, num_layers=L)
+    for l in range(L):
+        li = wl.layer(l)
+        table = np.concatenate([np.arange(128 * l, 128 * (l + 1)), np.zeros(32)]).astype(np.int32)[None, :]
+        st.set_layer(l, w1t=li.w1t, w2t=li.w2t, pos_bias=li.pos_bias, page_table=table)
+    x = torch.from_numpy(wl.x0).to("cuda", torch.bfloat16)
+    off_u = np.array([0, 4096], np.int32)
+    for _ in range(3):
+        st.forward(x, off_u, np.zeros(1, np.int32))
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(reps):
+        st.forward(x, off_u, np.zeros(1, np.int32))
+    e[1].record()
+    torch.cuda.synchronize()
+    t_rec = e[0].elapsed_time(e[1]) / reps * 1e-3
+    gb = npg * page_bytes / 1e9
+    print(json.dumps({
+        "metric": "host-tier page copies: offload / onboard bandwidth; onboard vs recompute of one user",
+        "value": gb / t_on, "unit": "GB/s onboard (host -> HBM)", "higher_is_better": True, "n_gpus": 1,
+        "offload_GBs": gb / t_off, "onboard_GBs": gb / t_on, "pages": npg, "page_bytes": page_bytes,
+        "user_onboard_us": t_user * 1e6, "user_recompute_us": t_rec * 1e6,
+        "recompute_over_onboard": t_rec / t_user,
+        "config": {"workload": "kvhost-3layer-bf16-hist4096", "layers": L, "hidden": H * d, "heads": H,
+                   "head_dim": d, "page_size": ps, "user_tokens": 4096, "user_pages": upages}}), flush=True)
+
+
 def main():
     args = parse()
+    if args.kvhost:
+        kvhost_bench(args)
+        return
     if args.kvcache:
         kvcache_bench(args)
         return

@@ -1,6 +1,8 @@
 """Binding of the paged KV cache manager (include/hstu_kvcache.h): lookup,
-page allocation and LRU eviction on the host, page-table building on the
-device.  Argument marshalling only: every decision is made by libhstu.
+page allocation and LRU eviction on the host (with an optional pinned host
+tier that evicted users are offloaded to and onboarded back from), page-table
+building and page copies on the device.  Argument marshalling only: every
+decision is made by libhstu.
 """
 from __future__ import annotations
 
@@ -38,22 +40,25 @@ def _lib_kv() -> ctypes.CDLL:
     if _bound is lib:
         return lib
     lib.hstu_kvcache_create.restype = P
-    lib.hstu_kvcache_create.argtypes = [I32, I64, I32, I32, I32]
+    lib.hstu_kvcache_create.argtypes = [I32, I64, I32, I32, I32, I64]
     lib.hstu_kvcache_destroy.restype = None
     lib.hstu_kvcache_destroy.argtypes = [P]
     lib.hstu_kvcache_directory_elems.restype = I64
     lib.hstu_kvcache_directory_elems.argtypes = [P]
     lib.hstu_kvcache_plan.restype = I32
     lib.hstu_kvcache_plan.argtypes = [P, I32, P, P, P, P, P, I32, ctypes.POINTER(I32), P, I32,
-                                      ctypes.POINTER(I32)]
+                                      ctypes.POINTER(I32), P, I32, ctypes.POINTER(I32)]
     lib.hstu_kvcache_lookup.restype = I32
-    lib.hstu_kvcache_lookup.argtypes = [P, I32, P, P]
+    lib.hstu_kvcache_lookup.argtypes = [P, I32, P, P, P]
     lib.hstu_kvcache_evict.restype = I32
     lib.hstu_kvcache_evict.argtypes = [P, I64, ctypes.POINTER(I32)]
     lib.hstu_kvcache_stats.restype = I32
-    lib.hstu_kvcache_stats.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(I32)]
+    lib.hstu_kvcache_stats.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I64),
+                                       ctypes.POINTER(I32)]
     lib.hstu_kv_tables_build.restype = I32
     lib.hstu_kv_tables_build.argtypes = [P, I32, I32, I32, P, I32, P, I32, P, P]
+    lib.hstu_kv_copy_pages.restype = I32
+    lib.hstu_kv_copy_pages.argtypes = [P, P, P, P, I64, I64, I64, I64, P, I32, I32, P]
     _bound = lib
     return lib
 
@@ -67,24 +72,33 @@ class Plan:
     hist_len: np.ndarray      # [B] int32: cached tokens reused (0 = miss)
     slots: np.ndarray         # [B] int32: directory slots
     updates: np.ndarray       # [n, 4] int32: (slot, layer, page index, page id)
-    evicted: List[int]        # user ids evicted by this plan
+    evicted: List[int]        # user ids evicted from the GPU by this plan
+    copies: np.ndarray        # [m, 4] int32: (onboard, gpu page, host page, 0), offloads first
+
+    @property
+    def n_offload(self) -> int:
+        return int(np.count_nonzero(self.copies[:, 0] == 0)) if self.copies.size else 0
 
 
 class KVCache:
     """Host cache manager over a pool of num_pages pages of page_size tokens
-    shared by num_layers layers, plus the device page directory."""
+    shared by num_layers layers (and, with host_pages > 0, a host tier of that
+    many pages), plus the device page directory."""
 
     def __init__(self, *, num_layers: int, num_pages: int, page_size: int, max_pages_per_user: int,
-                 max_users: int):
+                 max_users: int, host_pages: int = 0):
         self.lib = _lib_kv()
         self.L, self.P, self.ps = num_layers, num_pages, page_size
-        self.maxP, self.max_users = max_pages_per_user, max_users
-        h = self.lib.hstu_kvcache_create(num_layers, num_pages, page_size, max_pages_per_user, max_users)
+        self.maxP, self.max_users, self.PH = max_pages_per_user, max_users, host_pages
+        h = self.lib.hstu_kvcache_create(num_layers, num_pages, page_size, max_pages_per_user, max_users,
+                                         host_pages)
         if not h:
             raise KVCacheError("hstu_kvcache_create", -1)
         self.h = P(h)
         self._dir = None
         self._pinned = None       # reused pinned host staging buffer for updates and slots
+        self._cpinned = None      # the same for page copies
+        self.host_k = self.host_v = None
 
     def close(self) -> None:
         if self.h:
@@ -97,13 +111,16 @@ class KVCache:
         except Exception:
             pass
 
-    def lookup(self, user_ids: Sequence[int]) -> np.ndarray:
+    def lookup(self, user_ids: Sequence[int], with_tier: bool = False):
+        """Cached tokens per user (-1: not cached); with_tier also returns the
+        tier per user (0 none, 1 GPU, 2 host)."""
         ids = np.ascontiguousarray(user_ids, dtype=np.int64)
         out = np.empty(ids.shape[0], dtype=np.int32)
-        rc = self.lib.hstu_kvcache_lookup(self.h, ids.shape[0], _np_ptr(ids), _np_ptr(out))
+        tier = np.empty(ids.shape[0], dtype=np.int32)
+        rc = self.lib.hstu_kvcache_lookup(self.h, ids.shape[0], _np_ptr(ids), _np_ptr(out), _np_ptr(tier))
         if rc != 0:
             raise KVCacheError("hstu_kvcache_lookup", rc)
-        return out
+        return (out, tier) if with_tier else out
 
     def plan(self, user_ids: Sequence[int], n_new: Sequence[int]) -> Plan:
         ids = np.ascontiguousarray(user_ids, dtype=np.int64)
@@ -115,15 +132,18 @@ class KVCache:
         cap = int(self.L * np.sum((cached + np.maximum(n, 0) + self.ps - 1) // self.ps))
         upd = np.empty((max(cap, 1), 4), dtype=np.int32)
         ev = np.empty(max(self.max_users, 1), dtype=np.int64)
+        ccap = 2 * self.P if self.PH > 0 else 0
+        cps = np.empty((max(ccap, 1), 4), dtype=np.int32)
         hist = np.empty(B, dtype=np.int32)
         slots = np.empty(B, dtype=np.int32)
-        nu, ne = I32(0), I32(0)
+        nu, ne, nc = I32(0), I32(0), I32(0)
         rc = self.lib.hstu_kvcache_plan(self.h, B, _np_ptr(ids), _np_ptr(n), _np_ptr(hist), _np_ptr(slots),
                                         upd.ctypes.data_as(P), cap, ctypes.byref(nu), ev.ctypes.data_as(P),
-                                        ev.shape[0], ctypes.byref(ne))
+                                        ev.shape[0], ctypes.byref(ne), cps.ctypes.data_as(P), ccap,
+                                        ctypes.byref(nc))
         if rc != 0:
             raise KVCacheError("hstu_kvcache_plan", rc)
-        return Plan(hist, slots, upd[:nu.value].copy(), ev[:ne.value].tolist())
+        return Plan(hist, slots, upd[:nu.value].copy(), ev[:ne.value].tolist(), cps[:nc.value].copy())
 
     def evict(self, user_id: int) -> bool:
         found = I32(0)
@@ -132,12 +152,51 @@ class KVCache:
             raise KVCacheError("hstu_kvcache_evict", rc)
         return bool(found.value)
 
-    def stats(self):
-        fp, cu = I64(0), I32(0)
-        rc = self.lib.hstu_kvcache_stats(self.h, ctypes.byref(fp), ctypes.byref(cu))
+    def stats(self, host: bool = False):
+        """(free GPU pages, GPU-cached users), plus (free host pages, host users)
+        when host is set."""
+        fp, cu, fh, hu = I64(0), I32(0), I64(0), I32(0)
+        rc = self.lib.hstu_kvcache_stats(self.h, ctypes.byref(fp), ctypes.byref(cu), ctypes.byref(fh),
+                                         ctypes.byref(hu))
         if rc != 0:
             raise KVCacheError("hstu_kvcache_stats", rc)
-        return fp.value, cu.value
+        return (fp.value, cu.value, fh.value, hu.value) if host else (fp.value, cu.value)
+
+    def host_tier(self, page_shape_k, page_shape_v, dtype):
+        """The pinned host tier arrays [host_pages, *page_shape] (allocated on
+        first use)."""
+        import torch
+        if self.host_k is None:
+            self.host_k = torch.empty((self.PH, *page_shape_k), dtype=dtype, pin_memory=True)
+            self.host_v = torch.empty((self.PH, *page_shape_v), dtype=dtype, pin_memory=True)
+        return self.host_k, self.host_v
+
+    def copy_pages(self, plan: Plan, k_pool, v_pool, stream=None) -> None:
+        """Runs the plan's offloads, then its onboards, between the device pools
+        and the pinned host tier (call before the batch's layers)."""
+        import torch
+        m = plan.copies.shape[0]
+        if m == 0:
+            return
+        hk, hv = self.host_tier(tuple(k_pool.shape[1:]), tuple(v_pool.shape[1:]), k_pool.dtype)
+        need = 4 * m
+        if self._cpinned is None or self._cpinned.numel() < need:
+            self._cpinned = torch.empty(max(need, 1024) * 2, dtype=torch.int32, pin_memory=True)
+            self._cstaged = None
+        if getattr(self, "_cstaged", None) is not None:
+            self._cstaged.synchronize()
+        host = self._cpinned[:need]
+        host.numpy()[:] = plan.copies.reshape(-1)
+        dev = host.to(device=k_pool.device, non_blocking=True)
+        self._cstaged = torch.cuda.Event()
+        self._cstaged.record()
+        pbk = k_pool[0].numel() * k_pool.element_size()
+        pbv = v_pool[0].numel() * v_pool.element_size()
+        rc = self.lib.hstu_kv_copy_pages(P(k_pool.data_ptr()), P(v_pool.data_ptr()), P(hk.data_ptr()),
+                                         P(hv.data_ptr()), pbk, pbv, int(k_pool.shape[0]), self.PH,
+                                         P(dev.data_ptr()), plan.n_offload, m, _lib._stream(stream))
+        if rc != 0:
+            raise KVCacheError("hstu_kv_copy_pages", rc)
 
     def directory(self, device="cuda"):
         """The device page directory [max_users, L, max_pages] (allocated on

@@ -17,6 +17,7 @@ from hstu_jagged_silu_fwd_amd.kvcache import KVCache, KVCacheError
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRACE = json.load(open(os.path.join(HERE, "golden", "kvcache_trace.json")))
+HOST_TRACE = json.load(open(os.path.join(HERE, "golden", "kvcache_host_trace.json")))
 ERR = {"full": -10, "too_long": -11, "invalid": -1}
 
 
@@ -60,6 +61,38 @@ def test_library_follows_the_hand_worked_trace():
     assert kv.stats() == (fin["free_pages"], fin["cached_users"])
 
 
+def test_host_tier_reference_model_follows_the_hand_worked_trace():
+    ref = RefKVCache(**HOST_TRACE["config"])
+    for st in HOST_TRACE["steps"]:
+        hist, slots, updates, evicted = ref.plan(st["ids"], st["n_new"])
+        assert hist == st["hist"] and slots == st["slots"], st["why"]
+        assert [list(u) for u in updates] == st["updates"], st["why"]
+        assert [list(c) for c in ref.last_copies] == st["copies"], st["why"]
+        assert evicted == st["evicted"], st["why"]
+    fin = HOST_TRACE["final"]
+    ids = [int(k) for k in fin["lookup"]]
+    assert ref.lookup(ids) == list(fin["lookup"].values())
+    assert ref.tier(ids) == list(fin["tier"].values())
+    assert (len(ref.free_pages), len(ref.users), len(ref.host_free), len(ref.host)) == \
+        (fin["free_pages"], fin["cached_users"], fin["free_host_pages"], fin["host_users"])
+
+
+def test_host_tier_library_follows_the_hand_worked_trace():
+    kv = KVCache(**HOST_TRACE["config"])
+    for st in HOST_TRACE["steps"]:
+        p = kv.plan(st["ids"], st["n_new"])
+        assert p.hist_len.tolist() == st["hist"] and p.slots.tolist() == st["slots"], st["why"]
+        assert p.updates.tolist() == st["updates"], st["why"]
+        assert p.copies[:, :3].tolist() == st["copies"], st["why"]
+        assert p.evicted == st["evicted"], st["why"]
+    fin = HOST_TRACE["final"]
+    ids = [int(k) for k in fin["lookup"]]
+    lens, tiers = kv.lookup(ids, with_tier=True)
+    assert lens.tolist() == list(fin["lookup"].values()) and tiers.tolist() == list(fin["tier"].values())
+    assert kv.stats(host=True) == (fin["free_pages"], fin["cached_users"], fin["free_host_pages"],
+                                   fin["host_users"])
+
+
 def random_trace(rng, n_batches, max_b, n_ids, max_new):
     for _ in range(n_batches):
         B = int(rng.integers(0, max_b + 1))
@@ -68,12 +101,15 @@ def random_trace(rng, n_batches, max_b, n_ids, max_new):
         yield ids.tolist(), n.tolist()
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2, 3])
-def test_library_matches_reference_model_on_random_traces(seed):
+@pytest.mark.parametrize("seed,host", [(0, False), (1, False), (2, False), (3, False),
+                                       (10, True), (11, True), (12, True), (13, True)])
+def test_library_matches_reference_model_on_random_traces(seed, host):
     rng = np.random.default_rng(seed)
     cfg = dict(num_layers=int(rng.integers(1, 4)), num_pages=int(rng.integers(20, 200)),
                page_size=int(2 ** rng.integers(2, 6)), max_pages_per_user=int(rng.integers(2, 12)),
                max_users=int(rng.integers(2, 16)))
+    if host:
+        cfg["host_pages"] = int(rng.integers(4, 300))
     ref, kv = RefKVCache(**cfg), KVCache(**cfg)
     outcomes = {"ok": 0, "full": 0, "too_long": 0}
     for ids, n in random_trace(rng, 300, 6, 24, 3 * cfg["page_size"]):
@@ -92,9 +128,11 @@ def test_library_matches_reference_model_on_random_traces(seed):
         assert got.slots.tolist() == want[1]
         assert [tuple(u) for u in got.updates.tolist()] == [tuple(u) for u in want[2]]
         assert got.evicted == want[3]
-        assert kv.stats() == (len(ref.free_pages), len(ref.users))
+        assert [tuple(c) for c in got.copies[:, :3].tolist()] == [tuple(c) for c in ref.last_copies]
+        assert kv.stats(host=True) == (len(ref.free_pages), len(ref.users), len(ref.host_free), len(ref.host))
         probe = list(range(3, 24 * 7919, 7919 * 3))
-        assert kv.lookup(probe).tolist() == ref.lookup(probe)
+        lens, tiers = kv.lookup(probe, with_tier=True)
+        assert lens.tolist() == ref.lookup(probe) and tiers.tolist() == ref.tier(probe)
     assert outcomes["ok"] > 50
 
 
@@ -135,6 +173,42 @@ def test_invariants_on_random_traces(seed):
             assert free_before + freed < need or slots_before + len(evicted) - 1 < misses
         else:
             assert free_before >= need and slots_before >= misses
+
+
+@pytest.mark.parametrize("seed", [7, 8])
+def test_host_tier_invariants_on_random_traces(seed):
+    """Host pages are held by at most one (user, layer) and never lost; no
+    user is in both tiers; an offloaded user's host pages receive exactly its
+    GPU pages; an onboarded user's first pages come from exactly its host
+    pages, in position order; a host hit keeps its history."""
+    rng = np.random.default_rng(seed)
+    cfg = dict(num_layers=2, num_pages=48, page_size=8, max_pages_per_user=5, max_users=5, host_pages=30)
+    ref = RefKVCache(**cfg)
+    for ids, n in random_trace(rng, 400, 4, 14, 20):
+        gpu_before = {uid: [list(p) for p in u.pages] for uid, u in ref.users.items()}
+        host_before = {uid: ([list(p) for p in e.pages], e.length) for uid, e in ref.host.items()}
+        try:
+            hist, slots, updates, evicted = ref.plan(ids, n)
+        except (CacheFull, TooLong):
+            continue
+        assert not (set(ref.users) & set(ref.host))
+        hp = [p for e in ref.host.values() for lp in e.pages for p in lp]
+        assert len(hp) == len(set(hp)) and sorted(hp + ref.host_free) == list(range(cfg["host_pages"]))
+        offl = [c for c in ref.last_copies if c[0] == 0]
+        onb = [c for c in ref.last_copies if c[0] == 1]
+        assert ref.last_copies == offl + onb
+        for uid in evicted:
+            if uid in ref.host and uid not in host_before:
+                got = {(g, h) for _, g, h in offl if h in {p for lp in ref.host[uid].pages for p in lp}}
+                want = {(g, h) for gl, hl in zip(gpu_before[uid], ref.host[uid].pages) for g, h in zip(gl, hl)}
+                assert got == want
+        for b, uid in enumerate(ids):
+            if uid in host_before and uid not in gpu_before:
+                assert hist[b] == host_before[uid][1]
+                u = ref.users[uid]
+                want = [(1, u.pages[l][i], host_before[uid][0][l][i])
+                        for l in range(cfg["num_layers"]) for i in range(len(host_before[uid][0][l]))]
+                assert sorted(c for c in onb if c in set(want)) == sorted(want)
 
 
 def test_lookup_does_not_touch_recency():

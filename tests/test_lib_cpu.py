@@ -36,7 +36,7 @@ def test_exports_every_kvcache_header_function():
                        src, flags=re.M)
     assert set(names) == {"hstu_kvcache_create", "hstu_kvcache_destroy", "hstu_kvcache_directory_elems",
                           "hstu_kvcache_plan", "hstu_kvcache_lookup", "hstu_kvcache_evict",
-                          "hstu_kvcache_stats", "hstu_kv_tables_build"}
+                          "hstu_kvcache_stats", "hstu_kv_tables_build", "hstu_kv_copy_pages"}
     lib = hs.load()
     for n in names:
         assert hasattr(lib, n), n

@@ -29,5 +29,7 @@ Modules:
   layer    -- jagged layer / stack (numpy fp64) and a padded-dense variant
   brute    -- scalar pure-Python brute force for tiny shapes
   paging   -- pool layout: append (scatter) and gather through a page table
+  kvcache  -- reference model of the cache manager (LRU, host tier, trim)
+  preprocess -- token rows: embeddings, interleave, context, positions
 """
-from . import buckets, layer, brute, paging  # noqa: F401
+from . import buckets, layer, brute, paging, preprocess  # noqa: F401

@@ -22,8 +22,10 @@ def _silu(z: float) -> float:
 
 def layer_brute(x, new_len, hist_len, hist_k, hist_v, w1, w2, pos_bias,
                 pos_mbits, attn_scale, eps, H, timestamps=None, ts_bias=None,
-                ts_mbits=0):
+                ts_mbits=0, num_candidates=None):
     """Arguments as oracle.layer.layer_forward (nested lists or arrays).
+    With num_candidates, row t of user u is a candidate when t >= n - m_u;
+    a candidate skips the keys of every other candidate.
     Returns y as a list of rows (Python floats)."""
     T = len(x)
     D = len(w1)
@@ -45,11 +47,14 @@ def layer_brute(x, new_len, hist_len, hist_k, hist_v, w1, w2, pos_bias,
         c, n = int(hist_len[u]), int(new_len[u])
         keys = [[float(v) for v in hist_k[u][j]] for j in range(c)] + [Kblk[r0 + t] for t in range(n)]
         vals = [[float(v) for v in hist_v[u][j]] for j in range(c)] + [Vblk[r0 + t] for t in range(n)]
+        m_u = 0 if num_candidates is None else int(num_candidates[u])
         for t in range(n):
             p = c + t
             o = [0.0] * D
             for h in range(H):
                 for j in range(p + 1):
+                    if t >= n - m_u and j >= c + n - m_u and j != p:
+                        continue                    # another candidate's key
                     s = 0.0
                     for e in range(h * d, (h + 1) * d):
                         s += Qblk[r0 + t][e] * keys[j][e]

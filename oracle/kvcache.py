@@ -39,6 +39,11 @@ section, with onboard and offload):
     page -> host page); it becomes the newest host entry;
   * every offload is listed before every onboard.
 
+Trim (candidate tokens scored once are not history): a GPU-cached user's
+cached length shrinks by a given count; the pages past ceil(new length /
+page_size) go onto the free-page stack layer by layer and index by index
+(as in an eviction); recency is unchanged.
+
 This model keeps last-use / entry times and picks victims by minimum time;
 the library keeps linked recency lists.  The two agree exactly on every
 output, which the tests check on random traces.
@@ -191,6 +196,23 @@ class RefKVCache:
             self.users[i].last_use = self.clock
         self.last_copies = offloads + onboards
         return hist, slots, updates, evicted
+
+    def trim(self, ids: Sequence[int], drop: Sequence[int]) -> None:
+        """Shortens each user's cached length by drop tokens (all users must
+        be GPU-cached, distinct, with drop in [0, length]; else ValueError and
+        no change)."""
+        ids, drop = list(ids), list(drop)
+        if len(set(ids)) != len(ids) or any(i not in self.users for i in ids) or \
+                any(k < 0 or k > self.users[i].length for i, k in zip(ids, drop)):
+            raise ValueError("bad trim")
+        for i, k in zip(ids, drop):
+            u = self.users[i]
+            u.length -= k
+            keep = self._pages_for(u.length)
+            for layer_pages in u.pages:
+                for p in layer_pages[keep:]:
+                    self.free_pages.append(p)
+                del layer_pages[keep:]
 
     def page_table(self, uid: int, layer: int) -> List[int]:
         return list(self.users[uid].pages[layer])

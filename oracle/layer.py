@@ -24,6 +24,15 @@ Definition (per layer, all arithmetic in float64 on the exact input values):
  5. Y = (Nrm * U) W2: elementwise gating before the output projection
     (same sections).
  6. In a stack, X_{l+1} = Y_l (no residual: reading).
+ 7. Candidates (optional): the last m_u new rows of user u are candidate
+    items to be scored.  A candidate at position p attends to every key
+    before the first candidate, cs = c + n - m_u, and to itself, not to the
+    other candidates; rows before cs keep the plain causal mask.  (The pages
+    list candidate items among the sequence's tokens, NVIDIA blog "Why use
+    HSTU for generative recommendation", and give the workload's candidate
+    count, section "Benchmark setup", but state no mask for them: this
+    rule, that each candidate is scored as if it alone followed the
+    history, is a reading.)
 """
 from __future__ import annotations
 
@@ -57,10 +66,12 @@ def attention_user(q_rows: np.ndarray, t_rows: np.ndarray, k_all: np.ndarray,
                    pos_mbits: int, attn_scale: float,
                    ts: Optional[np.ndarray] = None,
                    ts_bias: Optional[np.ndarray] = None, ts_mbits: int = 0,
-                   q_block: int = 512) -> np.ndarray:
+                   q_block: int = 512, cand_start: Optional[int] = None) -> np.ndarray:
     """Step 3 for one user.  q_rows [m, D] are the queries of new rows with
     in-user indices t_rows [m]; k_all / v_all [c+n, D] hold history then new
-    keys/values in position order.  Returns the attention output [m, D]."""
+    keys/values in position order; cand_start is the position of the first
+    candidate (step 7; None = no candidates).  Returns the attention output
+    [m, D]."""
     m, D = q_rows.shape
     d = D // H
     out = np.zeros((m, D), dtype=np.float64)
@@ -73,6 +84,8 @@ def attention_user(q_rows: np.ndarray, t_rows: np.ndarray, k_all: np.ndarray,
         j = np.arange(L, dtype=np.int64)
         delta = p[:, None] - j[None, :]
         keep = delta >= 0                                           # causal, inclusive
+        if cand_start is not None:                                  # step 7
+            keep &= (j[None, :] < cand_start) | (delta == 0)
         bias = pb[bucket_np(delta, pos_mbits, pb.shape[0])]
         if tb is not None:
             tsd = np.asarray(ts, np.int64)
@@ -89,7 +102,7 @@ def attention_user(q_rows: np.ndarray, t_rows: np.ndarray, k_all: np.ndarray,
 def layer_forward(x, new_len, hist_len, hist_k, hist_v, w1, w2, pos_bias,
                   pos_mbits, attn_scale, eps, H, timestamps=None, ts_bias=None,
                   ts_mbits=0, rows: Optional[Sequence[int]] = None,
-                  q_block: int = 512) -> dict:
+                  q_block: int = 512, num_candidates=None) -> dict:
     """One layer over a jagged batch.
 
     x [T, D] holds the new rows of all users back to back (user u owns rows
@@ -98,6 +111,8 @@ def layer_forward(x, new_len, hist_len, hist_k, hist_v, w1, w2, pos_bias,
     position order.  timestamps: per user int64 [hist_len[u] + new_len[u]]
     (or None).  rows: optional subset of global row indices whose attention
     and output are computed (all K/V are still computed); None = all rows.
+    num_candidates: per user count of trailing candidate rows (step 7), or
+    None for none.
 
     Returns float64 arrays: u, v, q, k [T, D]; rows [m]; o, nrm, g, y [m, D]
     (o already includes attn_scale)."""
@@ -121,10 +136,15 @@ def layer_forward(x, new_len, hist_len, hist_k, hist_v, w1, w2, pos_bias,
         k_all = np.vstack([hk, K[r0:r1]])
         v_all = np.vstack([hv, V[r0:r1]])
         ridx = sel[mask]
+        cs = None
+        if num_candidates is not None:
+            m_u = int(num_candidates[u])
+            assert 0 <= m_u <= r1 - r0
+            cs = c + (r1 - r0) - m_u
         o[mask] = attention_user(
             Q[ridx], ridx - r0, k_all, v_all, c, H, pos_bias, pos_mbits,
             attn_scale, None if timestamps is None else timestamps[u],
-            ts_bias, ts_mbits, q_block)
+            ts_bias, ts_mbits, q_block, cs)
     nrm = layer_norm_rows(o, eps)
     g = nrm * U[sel]
     y = g @ np.asarray(w2, np.float64)
@@ -133,10 +153,13 @@ def layer_forward(x, new_len, hist_len, hist_k, hist_v, w1, w2, pos_bias,
 
 def layer_forward_padded(x, new_len, hist_len, hist_k, hist_v, w1, w2,
                          pos_bias, pos_mbits, attn_scale, eps, H,
-                         timestamps=None, ts_bias=None, ts_mbits=0) -> np.ndarray:
+                         timestamps=None, ts_bias=None, ts_mbits=0,
+                         num_candidates=None) -> np.ndarray:
     """Same layer computed on a per-user padded dense batch [B, Lmax, D] with
     explicit validity masks (an independent formulation used to pin the
-    jagged indexing).  Returns y [T, D] in jagged row order."""
+    jagged indexing).  Candidates (step 7) are a per-position flag: a key
+    flagged as a candidate is seen only by its own row.  Returns y [T, D] in
+    jagged row order."""
     x = np.asarray(x, np.float64)
     T, D = x.shape
     d = D // H
@@ -152,6 +175,7 @@ def layer_forward_padded(x, new_len, hist_len, hist_k, hist_v, w1, w2,
     Qp = np.zeros((B, Lmax, D))
     valid = np.zeros((B, Lmax), dtype=bool)
     is_new = np.zeros((B, Lmax), dtype=bool)
+    is_cand = np.zeros((B, Lmax), dtype=bool)
     tsp = np.zeros((B, Lmax), dtype=np.int64)
     for u in range(B):
         c, n, r0 = int(hist_len[u]), int(new_len[u]), int(offsets[u])
@@ -162,6 +186,8 @@ def layer_forward_padded(x, new_len, hist_len, hist_k, hist_v, w1, w2,
         Qp[u, c:c + n] = Q[r0:r0 + n]
         valid[u, :c + n] = True
         is_new[u, c:c + n] = True
+        if num_candidates is not None and int(num_candidates[u]) > 0:
+            is_cand[u, c + n - int(num_candidates[u]):c + n] = True
         if timestamps is not None:
             tsp[u, :c + n] = timestamps[u]
     pos = np.arange(Lmax)
@@ -174,6 +200,7 @@ def layer_forward_padded(x, new_len, hist_len, hist_k, hist_v, w1, w2,
             dts = tsp[u][:, None] - tsp[u][None, :]
             bu = bias + np.asarray(ts_bias, np.float64)[bucket_np(dts, ts_mbits, len(ts_bias))]
         m = (delta >= 0) & valid[u][None, :] & is_new[u][:, None]
+        m &= ~is_cand[u][None, :] | (delta == 0)
         for h in range(H):
             cols = slice(h * d, (h + 1) * d)
             s = Qp[u][:, cols] @ Kp[u][:, cols].T + bu
@@ -187,7 +214,8 @@ def layer_forward_padded(x, new_len, hist_len, hist_k, hist_v, w1, w2,
 
 
 def stack_forward(x0, new_len, hist_len, layers: List[dict], attn_scale, eps,
-                  H, pos_mbits, timestamps=None, ts_mbits=0) -> List[np.ndarray]:
+                  H, pos_mbits, timestamps=None, ts_mbits=0,
+                  num_candidates=None) -> List[np.ndarray]:
     """A stack of layers, X_{l+1} = Y_l.  layers[l] holds w1, w2, pos_bias,
     ts_bias, hist_k, hist_v.  Returns [Y_0, ..., Y_{L-1}] (float64)."""
     xs = np.asarray(x0, np.float64)
@@ -196,7 +224,7 @@ def stack_forward(x0, new_len, hist_len, layers: List[dict], attn_scale, eps,
         r = layer_forward(xs, new_len, hist_len, li["hist_k"], li["hist_v"],
                           li["w1"], li["w2"], li["pos_bias"], pos_mbits,
                           attn_scale, eps, H, timestamps, li.get("ts_bias"),
-                          ts_mbits)
+                          ts_mbits, num_candidates=num_candidates)
         ys.append(r["y"])
         xs = r["y"]
     return ys

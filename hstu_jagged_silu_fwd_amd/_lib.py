@@ -71,6 +71,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_layer_fwd.restype = I32
     lib.hstu_layer_fwd_timed.argtypes = layer_args + [P]
     lib.hstu_layer_fwd_timed.restype = I32
+    lib.hstu_layer_fwd_cand.argtypes = [dp, P, P, P, P] + layer_args[4:] + [P]
+    lib.hstu_layer_fwd_cand.restype = I32
+    lib.hstu_preprocess.argtypes = [ctypes.POINTER(PrepDesc)] + [P] * 17
+    lib.hstu_preprocess.restype = I32
     lib.kv_pages_append.argtypes = [dp, P, P, P, P, P, P, P, P, P]
     lib.kv_pages_append.restype = I32
     lib.hstu_read_device_status.argtypes = [P, ctypes.POINTER(I32), P]
@@ -96,6 +100,19 @@ def loaded_hip_runtimes() -> Sequence[str]:
             if "libamdhip64" in line:
                 paths.add(line.split()[-1])
     return sorted(paths)
+
+
+class PrepDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_users", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("total_new", ctypes.c_int32),
+        ("item_rows", ctypes.c_int64),
+        ("action_rows", ctypes.c_int64),
+        ("ctx_rows", ctypes.c_int64),
+        ("max_positions", ctypes.c_int32),
+    ]
 
 
 def header_functions(path: str = HEADER_PATH) -> Sequence[str]:
@@ -164,10 +181,12 @@ def workspace_size(desc: LayerDesc) -> int:
 
 def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_pool,
               w1t, w2t, pos_bias, y, workspace, ts_bias=None, timestamps=None,
-              ts_offsets=None, stream=None, stage_events=None) -> None:
+              ts_offsets=None, stream=None, stage_events=None, num_candidates=None) -> None:
     """Enqueue one layer (see include/hstu.h).  `workspace` is a uint8 device
     tensor of at least workspace_size(desc) bytes; `stage_events` optionally
-    a sequence of 2*NUM_STAGES raw hipEvent_t handles."""
+    a sequence of 2*NUM_STAGES raw hipEvent_t handles; `num_candidates` an
+    int32 device tensor [B] of trailing candidate rows per user
+    (hstu_layer_fwd_cand)."""
     import torch
     lib = load()
     dt = _tdtype(desc)
@@ -190,13 +209,49 @@ def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_p
         ctypes.c_size_t(workspace.numel() * workspace.element_size()),
         _stream(stream),
     ]
+    arr = None
     if stage_events is not None:
         arr = (ctypes.c_void_p * (2 * NUM_STAGES))(*[ctypes.c_void_p(e) for e in stage_events])
+    if num_candidates is not None:
+        nc = _ptr(num_candidates, "num_candidates", torch.int32)
+        rc = lib.hstu_layer_fwd_cand(*args[:4], nc, *args[4:], arr)
+    elif arr is not None:
         rc = lib.hstu_layer_fwd_timed(*args, arr)
     else:
         rc = lib.hstu_layer_fwd(*args)
     if rc != 0:
         raise HSTUError(rc, "hstu_layer_fwd")
+
+
+def preprocess(*, hist_len, ctx_offsets, ctx_ids, hist_offsets, item_ids, action_ids, cand_offsets,
+               cand_ids, item_emb, action_emb, ctx_emb, pos_emb, x, new_offsets, num_candidates,
+               device_status, stream=None) -> None:
+    """Enqueue hstu_preprocess (include/hstu.h): token ids -> x [T, D] plus the
+    layer's new_offsets and num_candidates.  Tables and x share one dtype;
+    action_ids / action_emb None = no action tokens."""
+    import torch
+    dt = x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    T, D = int(x.shape[0]), int(x.shape[1])
+    desc = PrepDesc(num_users=int(hist_len.shape[0]), hidden=D,
+                    dtype=HSTU_BF16 if dt == torch.bfloat16 else HSTU_F32, total_new=T,
+                    item_rows=int(item_emb.shape[0]),
+                    action_rows=0 if action_emb is None else int(action_emb.shape[0]),
+                    ctx_rows=int(ctx_emb.shape[0]), max_positions=int(pos_emb.shape[0]))
+    i64 = torch.int64
+    rc = load().hstu_preprocess(
+        ctypes.byref(desc), _ptr(hist_len, "hist_len", torch.int32),
+        _ptr(ctx_offsets, "ctx_offsets", torch.int32), _ptr(ctx_ids, "ctx_ids", i64),
+        _ptr(hist_offsets, "hist_offsets", torch.int32), _ptr(item_ids, "item_ids", i64),
+        _ptr(action_ids, "action_ids", i64, allow_none=True),
+        _ptr(cand_offsets, "cand_offsets", torch.int32), _ptr(cand_ids, "cand_ids", i64),
+        _ptr(item_emb, "item_emb", dt), _ptr(action_emb, "action_emb", dt, allow_none=True),
+        _ptr(ctx_emb, "ctx_emb", dt), _ptr(pos_emb, "pos_emb", dt), _ptr(x, "x", dt),
+        _ptr(new_offsets, "new_offsets", torch.int32), _ptr(num_candidates, "num_candidates", torch.int32),
+        _ptr(device_status, "device_status", torch.int32), _stream(stream))
+    if rc != 0:
+        raise HSTUError(rc, "hstu_preprocess")
 
 
 def kv_pages_append(desc: LayerDesc, k_new, v_new, new_offsets, hist_len, page_table,

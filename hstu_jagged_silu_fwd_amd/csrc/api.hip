@@ -103,7 +103,7 @@ hstu_status check_layer(const hstu_layer_desc* d) {
 }
 
 hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
-                       const int32_t* hist_len, const int32_t* page_table, void* k_pool, void* v_pool,
+                       const int32_t* hist_len, const int32_t* ncand, const int32_t* page_table, void* k_pool, void* v_pool,
                        const void* w1t, const void* w2t, const float* pos_bias, const float* ts_bias,
                        const int64_t* timestamps, const int32_t* ts_offsets, void* y, void* workspace,
                        size_t workspace_bytes, void* hip_stream, void* const* ev) {
@@ -138,13 +138,13 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
     return k;
   };
   hipError_t e;
-  e = launch_prep(d, new_offsets, hist_len, page_table, ts_off, ws, L.nqb_cap, L.item_cap, grid, st,
+  e = launch_prep(d, new_offsets, hist_len, ncand, page_table, ts_off, ws, L.nqb_cap, L.item_cap, grid, st,
                   kev(HSTU_STAGE_PREP));
   if (e != hipSuccess) return HSTU_ERR_HIP;
   if (!any_rows) return HSTU_OK;
   e = launch_gemm_qkv(d, x, w1t, k_pool, v_pool, ws, st, kev(HSTU_STAGE_PROJ));
   if (e != hipSuccess) return HSTU_ERR_HIP;
-  e = launch_attn(d, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ws,
+  e = launch_attn(d, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ncand, ws,
                   grid < L.item_cap ? grid : L.item_cap, st, kev(HSTU_STAGE_ATTN));
   if (e != hipSuccess) return HSTU_ERR_HIP;
   e = launch_norm_gate(d, ws, L.nqb_cap, st, kev(HSTU_STAGE_NORM));
@@ -171,8 +171,8 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const int
                            const void* w1t, const void* w2t, const float* pos_bias, const float* ts_bias,
                            const int64_t* timestamps, const int32_t* ts_offsets, void* y, void* workspace,
                            size_t workspace_bytes, void* hip_stream) {
-  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1t, w2t, pos_bias, ts_bias,
-                    timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, nullptr);
+  return layer_impl(desc, x, new_offsets, hist_len, nullptr, page_table, k_pool, v_pool, w1t, w2t, pos_bias,
+                    ts_bias, timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, nullptr);
 }
 
 hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
@@ -181,8 +181,21 @@ hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x, con
                                  const float* ts_bias, const int64_t* timestamps, const int32_t* ts_offsets,
                                  void* y, void* workspace, size_t workspace_bytes, void* hip_stream,
                                  void* const* stage_events) {
-  return layer_impl(desc, x, new_offsets, hist_len, page_table, k_pool, v_pool, w1t, w2t, pos_bias, ts_bias,
-                    timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, stage_events);
+  return layer_impl(desc, x, new_offsets, hist_len, nullptr, page_table, k_pool, v_pool, w1t, w2t, pos_bias,
+                    ts_bias, timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, stage_events);
+}
+
+hstu_status hstu_layer_fwd_cand(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
+                                const int32_t* hist_len, const int32_t* num_candidates,
+                                const int32_t* page_table, void* k_pool, void* v_pool, const void* w1t,
+                                const void* w2t, const float* pos_bias, const float* ts_bias,
+                                const int64_t* timestamps, const int32_t* ts_offsets, void* y,
+                                void* workspace, size_t workspace_bytes, void* hip_stream,
+                                void* const* stage_events) {
+  if (num_candidates == nullptr) return HSTU_ERR_INVALID_ARG;
+  return layer_impl(desc, x, new_offsets, hist_len, num_candidates, page_table, k_pool, v_pool, w1t, w2t,
+                    pos_bias, ts_bias, timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream,
+                    stage_events);
 }
 
 hstu_status kv_pages_append(const hstu_layer_desc* desc, const void* k_new, const void* v_new,
@@ -220,6 +233,9 @@ const char* hstu_status_string(int32_t status) {
     case HSTU_DEV_CAPACITY: return "device: sequence longer than its page-table row";
     case HSTU_DEV_BAD_PAGE: return "device: page id outside the pool";
     case HSTU_DEV_BAD_TS: return "device: ts_offsets do not match sequence lengths";
+    case HSTU_DEV_BAD_CANDIDATES: return "device: a candidate count outside [0, new rows]";
+    case HSTU_DEV_BAD_TOKEN: return "device: a token id outside its embedding table";
+    case HSTU_DEV_BAD_POSITION: return "device: a position outside the position table";
     default: return "unknown status";
   }
 }

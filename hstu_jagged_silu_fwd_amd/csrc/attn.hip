@@ -22,7 +22,8 @@
 // Per step and wave:
 //   S^T[32 keys x 16 queries] = K * Q^T     (2 MFMA blocks over d; the
 //                                           accumulators start at the bias)
-//   A = SiLU(S) on the fp32 scores; masked only on diagonal steps
+//   A = SiLU(S) on the fp32 scores; masked only on diagonal steps and on
+//                                           steps that reach the candidates
 //   O^T[d x 16]             += V^T * A
 // K rows feeding S^T block b are read in the permuted order row m -> key
 // 8*(m/4) + 4*b + m%4, so the S^T accumulator of a lane holds 8 consecutive
@@ -47,6 +48,11 @@
 // there) touches at most two buckets and takes a compare/select between two
 // values; any other step takes the generic per-element bucket path.  Timestamps, when present, travel with
 // their keys through the ring; each lane keeps its query's in a register.
+//
+// Candidates: when the call gives per-user candidate counts m_u, a query at
+// or past the first candidate position cs = c + n - m_u sees only the keys
+// before cs and itself (a key at or past cs is kept only on the diagonal).
+// Rows before cs see nothing past cs anyway, so one mask covers every row.
 //
 // Partial outputs (fp32) go to the workspace; the chunks of a row are added
 // by the norm kernel (no softmax, so partial sums over key ranges simply
@@ -76,6 +82,7 @@ struct AttnArgs {
   const float* ts_bias;
   const int64_t* ts;
   const int32_t* ts_off;
+  const int32_t* ncand;      // per-user candidate counts, or null
   WsHeader* hdr;
   const AttnItem* items;
   float* part;
@@ -208,6 +215,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     const int n = __builtin_amdgcn_readfirstlane(item.b.z);
     const int c = __builtin_amdgcn_readfirstlane(item.b.w);
     const int len = c + n;
+    // first candidate position (none: past every key)
+    const int cs = a.ncand != nullptr ? len - a.ncand[u] : 0x7fffffff;
     const int nq = min(kQB, n - q0);
     const int ngroups = (nq + 15) >> 4;
     // Phases: the waves form P phases of WP = kWaves/P waves (columns);
@@ -412,9 +421,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       for (int i = 0; i < NG; ++i) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) av[i][e] *= st[i][e >> 2][e & 3];
-        if (dmn[i] < 0) {                            // causal mask on the diagonal
+        if (dmn[i] < 0 && kb + kStepKeys <= cs) {    // causal mask on the diagonal
 #pragma unroll
           for (int e = 0; e < 8; ++e) av[i][e] = dl0[i] - e >= 0 ? av[i][e] : 0.0f;
+        } else if (kb + kStepKeys > cs) {            // keys at or past the candidates
+          const int ce = cs - (kb + 8 * g);          // element e's key is past cs when e >= ce
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int de = dl0[i] - e;
+            av[i][e] = (de >= 0 && (e < ce || de == 0)) ? av[i][e] : 0.0f;
+          }
         }
         set_frag(af[i], av[i]);
       }
@@ -521,7 +537,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
 template <typename T, int HD>
 hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                   const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,
-                  const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
+                  const int32_t* ncand, const WsPtrs& ws, int grid, hipStream_t stream,
+                  const KernelEvents& ev) {
   AttnArgs<T> a;
   a.pt = pt;
   a.k_pool = static_cast<const T*>(k_pool);
@@ -531,6 +548,7 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.ts_bias = ts_bias;
   a.ts = ts;
   a.ts_off = ts_off;
+  a.ncand = ncand;
   a.hdr = ws.hdr;
   a.items = ws.items;
   a.part = ws.part;
@@ -548,11 +566,11 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
 template <typename T>
 hipError_t attn_dt(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                    const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,
-                   const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
+                   const int32_t* nc, const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
   switch (d.head_dim) {
-    case 32: return attn_t<T, 32>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
-    case 64: return attn_t<T, 64>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
-    default: return attn_t<T, 128>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
+    case 32: return attn_t<T, 32>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, nc, ws, grid, stream, ev);
+    case 64: return attn_t<T, 64>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, nc, ws, grid, stream, ev);
+    default: return attn_t<T, 128>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, nc, ws, grid, stream, ev);
   }
 }
 
@@ -560,11 +578,11 @@ hipError_t attn_dt(const hstu_layer_desc& d, const int32_t* pt, const void* k_po
 
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,
-                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream,
-                       const KernelEvents& ev) {
+                       const int32_t* ts_off, const int32_t* ncand, const WsPtrs& ws, int grid,
+                       hipStream_t stream, const KernelEvents& ev) {
   if (d.dtype == HSTU_BF16)
-    return attn_dt<bf16>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
-  return attn_dt<float>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ws, grid, stream, ev);
+    return attn_dt<bf16>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ncand, ws, grid, stream, ev);
+  return attn_dt<float>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ncand, ws, grid, stream, ev);
 }
 
 }  // namespace hstu

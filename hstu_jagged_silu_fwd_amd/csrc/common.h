@@ -267,15 +267,15 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 // Host launchers (one per kernel family), all enqueue on `stream`.
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
-                       const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
+                       const int32_t* ncand, const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream,
                        const KernelEvents& ev = {});
 hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
                            void* v_pool, const WsPtrs& ws, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
                        const float* pos_bias, const float* ts_bias, const int64_t* ts,
-                       const int32_t* ts_off, const WsPtrs& ws, int grid, hipStream_t stream,
-                       const KernelEvents& ev = {});
+                       const int32_t* ts_off, const int32_t* ncand, const WsPtrs& ws, int grid,
+                       hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
                            int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_norm_gate(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,

@@ -410,6 +410,31 @@ hstu_kv_status hstu_kvcache_evict(hstu_kvcache* c, int64_t user_id, int32_t* fou
   return HSTU_KV_OK;
 }
 
+hstu_kv_status hstu_kvcache_trim(hstu_kvcache* c, int32_t B, const int64_t* user_ids,
+                                 const int32_t* n_drop) {
+  if (c == nullptr || B < 0 || (B > 0 && (user_ids == nullptr || n_drop == nullptr)))
+    return HSTU_KV_INVALID_ARG;
+  // every check first, so that a rejected call changes nothing
+  std::unordered_set<int64_t> seen;
+  for (int32_t b = 0; b < B; ++b) {
+    const auto it = c->index.find(user_ids[b]);
+    if (it == c->index.end() || !seen.insert(user_ids[b]).second) return HSTU_KV_INVALID_ARG;
+    if (n_drop[b] < 0 || n_drop[b] > c->slot_len[it->second]) return HSTU_KV_INVALID_ARG;
+  }
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t s = c->index.find(user_ids[b])->second;
+    c->slot_len[s] -= n_drop[b];
+    const int32_t keep = pages_for(c->slot_len[s], c->ps);
+    for (int32_t l = 0; l < c->L; ++l) {
+      const int32_t* r = c->row(s, l);
+      for (int32_t i = keep; i < c->slot_npages[s]; ++i) c->free_pages.push_back(r[i]);
+    }
+    c->held -= static_cast<int64_t>(c->L) * (c->slot_npages[s] - keep);
+    c->slot_npages[s] = keep;
+  }
+  return HSTU_KV_OK;
+}
+
 hstu_kv_status hstu_kvcache_stats(const hstu_kvcache* c, int64_t* free_pages, int32_t* cached_users,
                                   int64_t* free_host_pages, int32_t* host_users) {
   if (c == nullptr || free_pages == nullptr || cached_users == nullptr) return HSTU_KV_INVALID_ARG;

@@ -47,6 +47,7 @@ constexpr int kRowsPerWg = kPrepThreads * kRowsPerThread;
 struct PrepArgs {
   const int32_t* new_off;
   const int32_t* hist;
+  const int32_t* ncand;
   const int32_t* pt;
   const int32_t* ts_off;
   WsPtrs ws;
@@ -186,7 +187,7 @@ __device__ void validate(const PrepArgs& a, PrepShared& s) {
   const int B = a.B;
   if (w == 0) {
     int err = check_offsets(a, s, lane);
-    bool cap = false, bad_ts = false;
+    bool cap = false, bad_ts = false, bad_cand = false;
     int carry = 0;
     for (int u0 = 0; u0 < B; u0 += kWave) {
       const int u = u0 + lane;
@@ -195,6 +196,7 @@ __device__ void validate(const PrepArgs& a, PrepShared& s) {
         const int n = s.off[u + 1] - s.off[u];
         const int64_t len = static_cast<int64_t>(s.hist[u]) + n;
         cap |= len > static_cast<int64_t>(a.maxP) * a.ps;
+        if (a.ncand != nullptr) bad_cand |= a.ncand[u] < 0 || a.ncand[u] > n;
         if (a.ts_off != nullptr)
           bad_ts |= (u == 0 && a.ts_off[0] != 0) ||
                     static_cast<int64_t>(a.ts_off[u + 1]) - a.ts_off[u] != len;
@@ -209,6 +211,7 @@ __device__ void validate(const PrepArgs& a, PrepShared& s) {
     }
     if (err == 0 && __any(cap)) err = HSTU_DEV_CAPACITY;
     if (err == 0 && __any(bad_ts)) err = HSTU_DEV_BAD_TS;
+    if (err == 0 && __any(bad_cand)) err = HSTU_DEV_BAD_CANDIDATES;
     if (lane == 0) {
       s.pgp[B] = carry;
       s.err = err;
@@ -440,12 +443,13 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
 }  // namespace
 
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
-                       const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
+                       const int32_t* ncand, const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream,
                        const KernelEvents& ev) {
   PrepArgs a;
   a.new_off = new_off;
   a.hist = hist;
+  a.ncand = ncand;
   a.pt = pt;
   a.ts_off = ts_off;
   a.ws = ws;

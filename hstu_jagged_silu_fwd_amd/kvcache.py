@@ -52,6 +52,8 @@ def _lib_kv() -> ctypes.CDLL:
     lib.hstu_kvcache_lookup.argtypes = [P, I32, P, P, P]
     lib.hstu_kvcache_evict.restype = I32
     lib.hstu_kvcache_evict.argtypes = [P, I64, ctypes.POINTER(I32)]
+    lib.hstu_kvcache_trim.restype = I32
+    lib.hstu_kvcache_trim.argtypes = [P, I32, P, P]
     lib.hstu_kvcache_stats.restype = I32
     lib.hstu_kvcache_stats.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I64),
                                        ctypes.POINTER(I32)]
@@ -151,6 +153,17 @@ class KVCache:
         if rc != 0:
             raise KVCacheError("hstu_kvcache_evict", rc)
         return bool(found.value)
+
+    def trim(self, user_ids: Sequence[int], n_drop: Sequence[int]) -> None:
+        """Shortens each user's cached length by n_drop tokens (candidates
+        scored once are not kept as history); all or nothing."""
+        ids = np.ascontiguousarray(user_ids, dtype=np.int64)
+        k = np.ascontiguousarray(n_drop, dtype=np.int32)
+        if ids.shape != k.shape or ids.ndim != 1:
+            raise KVCacheError("trim", -1)
+        rc = self.lib.hstu_kvcache_trim(self.h, ids.shape[0], _np_ptr(ids), _np_ptr(k))
+        if rc != 0:
+            raise KVCacheError("hstu_kvcache_trim", rc)
 
     def stats(self, host: bool = False):
         """(free GPU pages, GPU-cached users), plus (free host pages, host users)

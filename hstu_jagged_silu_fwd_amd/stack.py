@@ -79,9 +79,11 @@ class HSTUStack:
 
     def layer(self, l: int, x: torch.Tensor, new_offsets: torch.Tensor, hist_len: torch.Tensor,
               y: torch.Tensor, workspace: Optional[torch.Tensor] = None, timestamps=None,
-              ts_offsets=None, stream=None, stage_events=None, page_table=None) -> None:
+              ts_offsets=None, stream=None, stage_events=None, page_table=None,
+              num_candidates=None) -> None:
         """Layer l over a batch; page_table [B, max_pages] overrides the layer's
-        own table (the batch size is then taken from new_offsets)."""
+        own table (the batch size is then taken from new_offsets);
+        num_candidates [B] int32 marks each user's trailing candidate rows."""
         T = int(x.shape[0])
         L = self.layers[l]
         nu = None if page_table is None else int(new_offsets.shape[0]) - 1
@@ -94,10 +96,10 @@ class HSTUStack:
         _lib.layer_fwd(desc, x, new_offsets, hist_len, L["page_table"] if page_table is None else page_table, self.k_pool,
                        self.v_pool, L["w1t"], L["w2t"], L["pos_bias"], y, ws,
                        ts_bias=L["ts_bias"], timestamps=timestamps, ts_offsets=ts_offsets,
-                       stream=stream, stage_events=stage_events)
+                       stream=stream, stage_events=stage_events, num_candidates=num_candidates)
 
     def forward(self, x, new_offsets, hist_len, timestamps=None, ts_offsets=None,
-                stream=None, return_all: bool = False, page_tables=None):
+                stream=None, return_all: bool = False, page_tables=None, num_candidates=None):
         """Run every layer; returns the last layer's output (or all outputs).
         page_tables: optional per-layer [B, max_pages] tables (e.g. a KV cache
         plan's, from KVCache.build_tables) instead of the layers' own."""
@@ -106,11 +108,12 @@ class HSTUStack:
         hl = self._dev(hist_len, torch.int32)
         ts = None if timestamps is None else self._dev(timestamps, torch.int64)
         tso = None if ts_offsets is None else self._dev(ts_offsets, torch.int32)
+        nc = None if num_candidates is None else self._dev(num_candidates, torch.int32)
         outs = []
         for l in range(len(self.layers)):
             y = torch.empty_like(x)
             self.layer(l, x, off, hl, y, timestamps=ts, ts_offsets=tso, stream=stream,
-                       page_table=None if page_tables is None else page_tables[l])
+                       page_table=None if page_tables is None else page_tables[l], num_candidates=nc)
             outs.append(y)
             x = y
         return outs if return_all else outs[-1]

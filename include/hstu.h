@@ -86,7 +86,10 @@ typedef enum {
   HSTU_DEV_BAD_HIST = 2,       /* hist_len[u] < 0 */
   HSTU_DEV_CAPACITY = 3,       /* hist_len[u] + n_u > max_pages_per_user * page_size */
   HSTU_DEV_BAD_PAGE = 4,       /* a needed page id outside [0, num_pool_pages) */
-  HSTU_DEV_BAD_TS = 5          /* ts_offsets[u+1]-ts_offsets[u] != hist_len[u]+n_u */
+  HSTU_DEV_BAD_TS = 5,         /* ts_offsets[u+1]-ts_offsets[u] != hist_len[u]+n_u */
+  HSTU_DEV_BAD_CANDIDATES = 6, /* num_candidates[u] outside [0, n_u] */
+  HSTU_DEV_BAD_TOKEN = 7,      /* hstu_preprocess: a token id outside its table */
+  HSTU_DEV_BAD_POSITION = 8    /* hstu_preprocess: hist_len[u] + rows of u > max_positions */
 } hstu_device_code;
 
 typedef struct {
@@ -167,6 +170,83 @@ hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x,
                                  const int32_t* ts_offsets, void* y, void* workspace,
                                  size_t workspace_bytes, void* hip_stream,
                                  void* const* stage_events);
+
+/* hstu_layer_fwd with candidate rows, and optional stage events as in
+ * hstu_layer_fwd_timed (stage_events may be NULL).  num_candidates [B] int32
+ * (device, required): the last num_candidates[u] new rows of user u are
+ * candidate items to be scored (NVIDIA blog above, sections "Why use HSTU
+ * for generative recommendation", where candidates are tokens of the
+ * sequence, and "Benchmark setup", up to 100 candidates per request).  With
+ * cs = hist_len[u] + n_u - num_candidates[u], a row at position p >= cs
+ * attends to the keys j < cs and to j = p only: each candidate is scored as
+ * if it alone followed the history and the other new rows (the pages give
+ * no mask for candidates; this is the library's reading).  Rows before cs
+ * are unchanged.  Candidates' K and V are appended like every new row; a
+ * cache that should not keep them as history drops them afterwards
+ * (hstu_kvcache_trim).  A count outside [0, n_u] is HSTU_DEV_BAD_CANDIDATES
+ * on the status word.  The workspace size is that of hstu_layer_fwd. */
+hstu_status hstu_layer_fwd_cand(const hstu_layer_desc* desc, const void* x,
+                                const int32_t* new_offsets, const int32_t* hist_len,
+                                const int32_t* num_candidates, const int32_t* page_table,
+                                void* k_pool, void* v_pool, const void* w1t, const void* w2t,
+                                const float* pos_bias, const float* ts_bias,
+                                const int64_t* timestamps, const int32_t* ts_offsets, void* y,
+                                void* workspace, size_t workspace_bytes, void* hip_stream,
+                                void* const* stage_events);
+
+/* Input preprocessing: the layer's input rows built from categorical tokens
+ * (NVIDIA blog above, section "Why use HSTU for generative recommendation":
+ * embedding lookup, interleave of item and action embeddings when action
+ * tokens are present, context appended, positional encoding; section
+ * "Benchmark setup": 6 context features, history of item/action pairs, up to
+ * 100 candidates).  Readings: every token is one row; user u's new rows are
+ * its context tokens, then its history entries (each pair as the item's row
+ * then the action's row; without action tokens, one item row per entry),
+ * then its candidate items; row t sits at position hist_len[u] + t and
+ *     x = table[id] + pos_emb[position]
+ * added in fp32 and rounded once to dtype (tables: ctx_emb for context,
+ * item_emb for items and candidates, action_emb for actions). */
+typedef struct {
+  int32_t num_users;           /* B >= 0 (at most 4096) */
+  int32_t hidden;              /* D, a multiple of 64, at most 2048 */
+  int32_t dtype;               /* hstu_dtype of every table and of x */
+  int32_t total_new;           /* T: rows of x; must equal the rows the tokens make */
+  int64_t item_rows;           /* rows of item_emb (>= 1) */
+  int64_t action_rows;         /* rows of action_emb; 0 = no action tokens */
+  int64_t ctx_rows;            /* rows of ctx_emb (>= 1) */
+  int32_t max_positions;       /* rows of pos_emb (>= 1) */
+} hstu_prep_desc;
+
+/* Builds x [T, D] and the layer's row metadata from a jagged token batch.
+ *   hist_len      [B]   int32  cached tokens per user (first position)
+ *   ctx_offsets   [B+1] int32, ctx_ids [ctx_offsets[B]] int64    context ids
+ *   hist_offsets  [B+1] int32, item_ids / action_ids [hist_offsets[B]] int64
+ *                               history entries (action_ids NULL when
+ *                               action_rows == 0)
+ *   cand_offsets  [B+1] int32, cand_ids [cand_offsets[B]] int64  candidates
+ *   item_emb [item_rows, D], action_emb [action_rows, D] (or NULL),
+ *   ctx_emb [ctx_rows, D], pos_emb [max_positions, D]          dtype
+ *   x              [T, D] dtype   out
+ *   new_offsets    [B+1] int32    out: prefix sums of each user's rows
+ *   num_candidates [B]   int32    out: candidate rows per user (for
+ *                                 hstu_layer_fwd_cand)
+ *   device_status  one device int32: receives 0 or a hstu_device_code
+ * Device pointers, caller-owned.  Two kernels on hip_stream: a one-workgroup
+ * scan that checks the offsets (each [0] == 0, non-decreasing: else
+ * HSTU_DEV_BAD_OFFSETS, as is a row total != T), the histories
+ * (HSTU_DEV_BAD_HIST) and the positions (HSTU_DEV_BAD_POSITION) and writes
+ * new_offsets and num_candidates; then the row builder, which writes nothing
+ * after a nonzero status.  A token id outside its table sets
+ * HSTU_DEV_BAD_TOKEN while the rows are being built: x is then unspecified.
+ * T == 0 with B == 0 is a valid no-op. */
+hstu_status hstu_preprocess(const hstu_prep_desc* desc, const int32_t* hist_len,
+                            const int32_t* ctx_offsets, const int64_t* ctx_ids,
+                            const int32_t* hist_offsets, const int64_t* item_ids,
+                            const int64_t* action_ids, const int32_t* cand_offsets,
+                            const int64_t* cand_ids, const void* item_emb,
+                            const void* action_emb, const void* ctx_emb, const void* pos_emb,
+                            void* x, int32_t* new_offsets, int32_t* num_candidates,
+                            int32_t* device_status, void* hip_stream);
 
 /* Append new rows' K and V into the pools (the paged KV table's append, NVIDIA
  * blog above, same section).  k_new, v_new [T, D] dtype, rows laid out as x in

@@ -154,6 +154,21 @@ hstu_kv_status hstu_kvcache_lookup(const hstu_kvcache* cache, int32_t B, const i
  * user was cached, else 0. */
 hstu_kv_status hstu_kvcache_evict(hstu_kvcache* cache, int64_t user_id, int32_t* found);
 
+/* Shortens the cached length of each of B distinct GPU-cached users by
+ * n_drop[b] tokens (0 <= n_drop[b] <= its cached length), e.g. the candidate
+ * rows a layer call scored and appended but that are not history (the
+ * candidates of a ranking request, NVIDIA blog above, sections "Why use
+ * HSTU for generative recommendation" and "Benchmark setup"; which tokens
+ * stay cached is this library's reading).  Pages past ceil(new length /
+ * page_size) of every layer go onto the free-page stack layer by layer,
+ * page index by page index; slots and recency are unchanged.  The device
+ * directory keeps its stale entries past the new length: a later plan that
+ * grows the user rewrites them.  Any invalid entry (unknown or host-cached
+ * user, duplicate, count out of range) fails the whole call with
+ * HSTU_KV_INVALID_ARG and no change.  Host pointers. */
+hstu_kv_status hstu_kvcache_trim(hstu_kvcache* cache, int32_t B, const int64_t* user_ids,
+                                 const int32_t* n_drop);
+
 /* Free GPU pages and GPU-cached users, free host pages and host-cached
  * users (the host pointers may be NULL). */
 hstu_kv_status hstu_kvcache_stats(const hstu_kvcache* cache, int64_t* free_pages,

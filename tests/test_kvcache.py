@@ -242,3 +242,93 @@ def test_bad_arguments_rejected():
         kv.plan([1], [-1])
     assert ei.value.code == -1
     assert kv.stats() == (4, 0)
+
+
+# ---- trim: candidates scored once are dropped from the cached history ----
+
+TRIM_CFG = dict(num_layers=2, num_pages=8, page_size=2, max_pages_per_user=4, max_users=2)
+
+
+def _trim_trace(cache):
+    """Worked by hand from the rule (free pages start as a stack that pops
+    0, 1, 2, ...):
+      plan A(+5): 3 pages per layer: layer 0 takes 0, 1, 2, layer 1 takes
+        3, 4, 5; slot 0;
+      trim A by 2: length 3 keeps ceil(3/2) = 2 pages per layer; page index 2
+        of layer 0 (page 2), then of layer 1 (page 5) are pushed, so 5 is on
+        top, then 2;
+      plan A(+2): history 3, length 5 needs one more page per layer: layer 0
+        pops 5, layer 1 pops 2; pages 7 and 6 stay free."""
+    p1 = cache.plan([11], [5])
+    cache.trim([11], [2])
+    mid = cache.lookup([11])
+    p2 = cache.plan([11], [2])
+    return p1, mid, p2
+
+
+def _updates(p):
+    return [tuple(int(v) for v in u) for u in (p.updates.tolist() if hasattr(p, "updates") else p[2])]
+
+
+def test_trim_hand_worked_trace_model_and_library():
+    want1 = [(0, 0, 0, 0), (0, 0, 1, 1), (0, 0, 2, 2), (0, 1, 0, 3), (0, 1, 1, 4), (0, 1, 2, 5)]
+    want2 = [(0, 0, 2, 5), (0, 1, 2, 2)]
+    ref = RefKVCache(**TRIM_CFG)
+    h1 = ref.plan([11], [5])
+    ref.trim([11], [2])
+    assert ref.lookup([11]) == [3]
+    h2 = ref.plan([11], [2])
+    assert [tuple(u) for u in h1[2]] == want1 and [tuple(u) for u in h2[2]] == want2
+    assert h2[0] == [3] and sorted(ref.free_pages) == [6, 7]
+    kv = KVCache(**TRIM_CFG)
+    p1, mid, p2 = _trim_trace(kv)
+    assert _updates(p1) == want1 and mid.tolist() == [3]
+    assert _updates(p2) == want2 and p2.hist_len.tolist() == [3]
+    assert kv.stats() == (2, 1)
+
+
+def test_trim_rejects_bad_arguments_and_changes_nothing():
+    kv = KVCache(**TRIM_CFG)
+    kv.plan([11, 12], [3, 2])
+    before = (kv.stats(), kv.lookup([11, 12]).tolist())
+    for ids, k in [([13], [0]), ([11, 11], [1, 1]), ([11], [4]), ([11], [-1]), ([11, 13], [1, 0])]:
+        with pytest.raises(KVCacheError) as ei:
+            kv.trim(ids, k)
+        assert ei.value.code == -1
+        assert (kv.stats(), kv.lookup([11, 12]).tolist()) == before
+    kv.trim([11, 12], [3, 0])                  # to zero length: the user stays, pageless
+    assert kv.lookup([11, 12]).tolist() == [0, 2] and kv.stats() == (8 - 2, 2)
+
+
+@pytest.mark.parametrize("seed,host", [(20, False), (21, False), (22, True), (23, True)])
+def test_library_matches_reference_model_with_trims(seed, host):
+    """Random plans, each followed by a trim of a random part of what it
+    added (as a serving step drops its candidates), library against model."""
+    rng = np.random.default_rng(seed)
+    cfg = dict(num_layers=int(rng.integers(1, 4)), num_pages=int(rng.integers(20, 120)),
+               page_size=int(2 ** rng.integers(2, 5)), max_pages_per_user=int(rng.integers(2, 10)),
+               max_users=int(rng.integers(2, 10)))
+    if host:
+        cfg["host_pages"] = int(rng.integers(4, 200))
+    ref, kv = RefKVCache(**cfg), KVCache(**cfg)
+    ok = 0
+    for ids, n in random_trace(rng, 250, 5, 20, 3 * cfg["page_size"]):
+        try:
+            want = ref.plan(ids, n)
+        except (CacheFull, TooLong):
+            with pytest.raises(KVCacheError):
+                kv.plan(ids, n)
+            continue
+        got = kv.plan(ids, n)
+        assert _updates(got) == [tuple(u) for u in want[2]] and got.evicted == want[3]
+        drop = [int(rng.integers(0, k + 1)) for k in n]
+        ref.trim(ids, drop)
+        kv.trim(ids, drop)
+        ok += 1
+        assert kv.stats(host=True) == (len(ref.free_pages), len(ref.users), len(ref.host_free), len(ref.host))
+        assert kv.lookup(ids).tolist() == ref.lookup(ids)
+        owned = ref.owned_pages()
+        assert sorted([p for p, _, _ in owned] + ref.free_pages) == list(range(cfg["num_pages"]))
+        for u in ref.users.values():
+            assert all(len(lp) == -(-u.length // cfg["page_size"]) for lp in u.pages)
+    assert ok > 50

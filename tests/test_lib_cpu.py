@@ -21,7 +21,8 @@ def test_exports_every_header_function():
     lib = hs.load()
     names = list(hs.header_functions())
     assert set(names) == {"hstu_layer_workspace_size", "hstu_layer_fwd", "hstu_layer_fwd_timed",
-                          "kv_pages_append", "hstu_read_device_status", "hstu_status_string"}
+                          "hstu_layer_fwd_cand", "hstu_preprocess", "kv_pages_append",
+                          "hstu_read_device_status", "hstu_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -36,7 +37,8 @@ def test_exports_every_kvcache_header_function():
                        src, flags=re.M)
     assert set(names) == {"hstu_kvcache_create", "hstu_kvcache_destroy", "hstu_kvcache_directory_elems",
                           "hstu_kvcache_plan", "hstu_kvcache_lookup", "hstu_kvcache_evict",
-                          "hstu_kvcache_stats", "hstu_kv_tables_build", "hstu_kv_copy_pages"}
+                          "hstu_kvcache_stats", "hstu_kvcache_trim", "hstu_kv_tables_build",
+                          "hstu_kv_copy_pages"}
     lib = hs.load()
     for n in names:
         assert hasattr(lib, n), n
@@ -93,3 +95,26 @@ def test_single_hip_runtime_in_process():
     hs.load()
     rts = _lib.loaded_hip_runtimes()
     assert len(rts) == 1, rts
+
+
+def test_candidate_and_preprocess_host_checks():
+    """Host-checkable errors of the candidate layer call and of the
+    preprocessing return before anything is enqueued (no GPU needed)."""
+    import ctypes
+    lib = hs.load()
+    d = desc()
+    # num_candidates is required (desc, x, offsets, hist, num_candidates, then
+    # the 11 pointers page_table .. workspace, bytes, stream, events)
+    assert lib.hstu_layer_fwd_cand(ctypes.byref(d), None, None, None, None, *([None] * 11), 0, None, None) == -1
+    P = _lib.PrepDesc
+    args = [None] * 17
+    assert lib.hstu_preprocess(None, *args) == -1
+    good = dict(num_users=2, hidden=512, dtype=1, total_new=10, item_rows=100, action_rows=4,
+                ctx_rows=8, max_positions=8320)
+    for over, code in [(dict(hidden=96), -2), (dict(hidden=4096), -2), (dict(dtype=7), -2),
+                       (dict(num_users=5000), -2), (dict(item_rows=0), -1), (dict(ctx_rows=0), -1),
+                       (dict(action_rows=-1), -1), (dict(max_positions=0), -1), (dict(total_new=-1), -1),
+                       ({}, -1)]:          # {}: valid sizes, null pointers
+        kw = dict(good)
+        kw.update(over)
+        assert lib.hstu_preprocess(ctypes.byref(P(**kw)), *args) == code, over

@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--kvhost", action="store_true",
                     help="measure the host tier: page-copy bandwidth and a user's onboard time "
                          "against recomputing its history")
+    ap.add_argument("--rank", action="store_true",
+                    help="ranking requests shaped like the pages' workload (8,198 cached context+history "
+                         "tokens, 100 candidates, batch 8, 3 and 8 layers): tokens -> preprocessing -> "
+                         "layers with candidates, cached vs full recompute")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -428,8 +432,141 @@ def kvhost_bench(args):
                    "head_dim": d, "page_size": ps, "user_tokens": 4096, "user_pages": upages}}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Ranking requests on the pages' workload shape (hidden 512, 4 heads, bf16;
+# per user 6 context tokens and 4,096 item/action pairs = 8,198 history
+# tokens, plus 100 candidates: 8,298 tokens, position table of the aligned
+# 8,320): batch 8, 3 and 8 layers.  Synthetic stand-in for the pages'
+# KuaiRand-1K inputs: item ids uniform over a 100,000-row table, 8 action
+# types, context ids over a 1,000-row table.  Two request kinds:
+#   hit:       the history is cached; a request sends the 100 candidates of
+#              each user (800 rows): preprocessing, then the layers with
+#              every new row a candidate;
+#   recompute: nothing cached; a request sends all 8,298 tokens of each user
+#              (66,384 rows) with the last 100 as candidates.
+# Latency per logical request = time of one batch / 8.
+# ---------------------------------------------------------------------------
+def rank_bench(args):
+    import torch
+    from hstu_jagged_silu_fwd_amd import _lib
+    from hstu_jagged_silu_fwd_amd.stack import HSTUStack
+    from workloads.gen import BIAS_STD, W_STD, round_bf16
+    B, D, H, d, ps = 8, 512, 4, 128, 32
+    n_ctx, pairs, m, max_pos = 6, 4096, 100, 8320
+    hist = n_ctx + 2 * pairs
+    maxP = max_pos // ps
+    n_items, n_actions, n_ctxv = 100_000, 8, 1000
+    rng = np.random.default_rng(args.seed)
+    dev = "cuda"
+    bf = torch.bfloat16
+    tab = lambda n, sd: torch.from_numpy(round_bf16(rng.normal(0, sd, size=(n, D)).astype(np.float32))).to(dev, bf)
+    item_emb, action_emb, ctx_emb, pos_emb = tab(n_items, 0.8), tab(n_actions, 0.8), tab(n_ctxv, 0.8), tab(max_pos, 0.6)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device=dev)
+    i64 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int64, device=dev)
+
+    def request(hit):
+        ctx = np.zeros(1, np.int64) if hit else rng.integers(0, n_ctxv, B * n_ctx)   # (one unused id when none)
+        k = 0 if hit else pairs
+        r = dict(hist_len=i32([hist if hit else 0] * B),
+                 ctx_offsets=i32(np.arange(B + 1) * (0 if hit else n_ctx)), ctx_ids=i64(ctx),
+                 hist_offsets=i32(np.arange(B + 1) * k),
+                 item_ids=i64(rng.integers(0, n_items, max(B * k, 1))),
+                 action_ids=i64(rng.integers(0, n_actions, max(B * k, 1))),
+                 cand_offsets=i32(np.arange(B + 1) * m), cand_ids=i64(rng.integers(0, n_items, B * m)))
+        T = B * (m if hit else hist + m)
+        r.update(item_emb=item_emb, action_emb=action_emb, ctx_emb=ctx_emb, pos_emb=pos_emb,
+                 x=torch.empty((T, D), dtype=bf, device=dev),
+                 new_offsets=torch.empty(B + 1, dtype=torch.int32, device=dev),
+                 num_candidates=torch.empty(B, dtype=torch.int32, device=dev),
+                 device_status=torch.zeros(1, dtype=torch.int32, device=dev))
+        return r, T
+
+    out_all = {}
+    for L in (3, 8):
+        P = L * B * maxP
+        st = HSTUStack(num_users=B, num_heads=H, head_dim=d, page_size=ps, num_pool_pages=P, max_pages_per_user=maxP,
+                       pos_buckets=128, pos_mbits=3, attn_scale=1.0 / max_pos, norm_eps=EPS, dtype="bf16",
+                       num_layers=L)
+        perm = rng.permutation(P).astype(np.int32)
+        for l in range(L):
+            st.set_layer(l, w1t=round_bf16(rng.normal(0, W_STD, size=(4 * D, D)).astype(np.float32)),
+                         w2t=round_bf16(rng.normal(0, W_STD, size=(D, D)).astype(np.float32)),
+                         pos_bias=rng.normal(0, BIAS_STD, size=128).astype(np.float32),
+                         page_table=perm[l * B * maxP:(l + 1) * B * maxP].reshape(B, maxP))
+        res = {}
+        # recompute first: it also fills the pool with every user's history
+        lib = _lib.load()
+        for kind, steps in (("recompute", max(3, args.steps // 6)), ("hit", args.steps)):
+            req, T = request(kind == "hit")
+            # argument lists built once (the timed loop only calls the library)
+            pdesc = _lib.PrepDesc(num_users=B, hidden=D, dtype=_lib.HSTU_BF16, total_new=T, item_rows=n_items,
+                                  action_rows=n_actions, ctx_rows=n_ctxv, max_positions=max_pos)
+            ptr = lambda k: ctypes.c_void_p(req[k].data_ptr())
+            stream = torch.cuda.current_stream().cuda_stream
+            pargs = [ctypes.byref(pdesc)] + [ptr(k) for k in (
+                "hist_len", "ctx_offsets", "ctx_ids", "hist_offsets", "item_ids", "action_ids", "cand_offsets",
+                "cand_ids", "item_emb", "action_emb", "ctx_emb", "pos_emb", "x", "new_offsets", "num_candidates",
+                "device_status")] + [ctypes.c_void_p(stream)]
+            ldesc = st.desc(T)
+            ws = st.workspace(T)
+            ys = [torch.empty((T, D), dtype=bf, device=dev) for _ in range(2)]
+            largs = []
+            for l in range(L):
+                Ll = st.layers[l]
+                xin = req["x"] if l == 0 else ys[(l - 1) % 2]
+                largs.append([ctypes.byref(ldesc), ctypes.c_void_p(xin.data_ptr()), ptr("new_offsets"),
+                              ptr("hist_len"), ptr("num_candidates"), ctypes.c_void_p(Ll["page_table"].data_ptr()),
+                              ctypes.c_void_p(st.k_pool.data_ptr()), ctypes.c_void_p(st.v_pool.data_ptr()),
+                              ctypes.c_void_p(Ll["w1t"].data_ptr()), ctypes.c_void_p(Ll["w2t"].data_ptr()),
+                              ctypes.c_void_p(Ll["pos_bias"].data_ptr()), None, None, None,
+                              ctypes.c_void_p(ys[l % 2].data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                              ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream), None])
+
+            def run():
+                rc = lib.hstu_preprocess(*pargs)
+                for a in largs:
+                    rc |= lib.hstu_layer_fwd_cand(*a)
+                if rc != 0:
+                    raise RuntimeError(f"ranking request failed: {rc}")
+            for _ in range(args.warmup):
+                run()
+            torch.cuda.synchronize()
+            assert int(req["device_status"].item()) == 0 and st.read_status(ws) == 0
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                run()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / steps
+            # the preprocessing alone (two kernels), event-bracketed
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                lib.hstu_preprocess(*pargs)
+            e1.record()
+            torch.cuda.synchronize()
+            prep_us = 1e3 * e0.elapsed_time(e1) / steps
+            prep_bytes = T * 3 * D * 2 + T * 8           # two table rows read, one row written; the id
+            res[kind] = dict(rows=T, ms_per_batch=1e3 * wall, ms_per_request=1e3 * wall / B,
+                             tokens_per_s=T / wall, preprocess_us=prep_us,
+                             preprocess_gbs=prep_bytes / (prep_us * 1e-6) / 1e9)
+        res["recompute_over_hit"] = res["recompute"]["ms_per_batch"] / res["hit"]["ms_per_batch"]
+        out_all[f"{L}layer"] = res
+        del st
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "ranking request latency, pages-shaped workload (cached history vs full recompute)",
+        "unit": "ms per logical request", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
+        "data": "synthetic", "steps_hit": args.steps, "results": out_all,
+        "config": {"workload": "rank-bf16-b8-ctx6-hist8192-cand100", "batch": B, "hidden": D, "heads": H,
+                   "history_tokens": hist, "candidates": m, "context_tokens": n_ctx, "item_action_pairs": pairs,
+                   "position_table": max_pos, "page_size": ps, "item_table_rows": n_items}}), flush=True)
+
+
 def main():
     args = parse()
+    if args.rank:
+        rank_bench(args)
+        return
     if args.kvhost:
         kvhost_bench(args)
         return

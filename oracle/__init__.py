@@ -31,5 +31,6 @@ Modules:
   paging   -- pool layout: append (scatter) and gather through a page table
   kvcache  -- reference model of the cache manager (LRU, host tier, trim)
   preprocess -- token rows: embeddings, interleave, context, positions
+  beam     -- Semantic-ID beam-decode attention over a shared context KV
 """
-from . import buckets, layer, brute, paging, preprocess  # noqa: F401
+from . import buckets, layer, brute, paging, preprocess, beam  # noqa: F401

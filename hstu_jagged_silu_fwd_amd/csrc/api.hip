@@ -236,6 +236,8 @@ const char* hstu_status_string(int32_t status) {
     case HSTU_DEV_BAD_CANDIDATES: return "device: a candidate count outside [0, new rows]";
     case HSTU_DEV_BAD_TOKEN: return "device: a token id outside its embedding table";
     case HSTU_DEV_BAD_POSITION: return "device: a position outside the position table";
+    case HSTU_DEV_BAD_CTX_LEN: return "device: a context length outside [0, max_ctx]";
+    case HSTU_DEV_BAD_PATH: return "device: a beam path slot outside [0, beam width)";
     default: return "unknown status";
   }
 }

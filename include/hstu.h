@@ -89,7 +89,9 @@ typedef enum {
   HSTU_DEV_BAD_TS = 5,         /* ts_offsets[u+1]-ts_offsets[u] != hist_len[u]+n_u */
   HSTU_DEV_BAD_CANDIDATES = 6, /* num_candidates[u] outside [0, n_u] */
   HSTU_DEV_BAD_TOKEN = 7,      /* hstu_preprocess: a token id outside its table */
-  HSTU_DEV_BAD_POSITION = 8    /* hstu_preprocess: hist_len[u] + rows of u > max_positions */
+  HSTU_DEV_BAD_POSITION = 8,   /* hstu_preprocess: hist_len[u] + rows of u > max_positions */
+  HSTU_DEV_BAD_CTX_LEN = 9,    /* hstu_beam_decode_attn: ctx_len[r] outside [0, max_ctx] */
+  HSTU_DEV_BAD_PATH = 10       /* hstu_beam_decode_attn: a path slot outside [0, W) */
 } hstu_device_code;
 
 typedef struct {

@@ -118,3 +118,30 @@ def test_candidate_and_preprocess_host_checks():
         kw = dict(good)
         kw.update(over)
         assert lib.hstu_preprocess(ctypes.byref(P(**kw)), *args) == code, over
+
+
+def test_beam_header_exports_and_host_checks():
+    """include/hstu_beam.h: every declared function is exported, and bad
+    descriptors are rejected on the host (no GPU needed)."""
+    import os
+    import re
+    from hstu_jagged_silu_fwd_amd import beam as hb
+    path = os.path.join(os.path.dirname(_lib.HEADER_PATH), "hstu_beam.h")
+    src = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    names = re.findall(r"^\s*hstu_status\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, flags=re.M)
+    assert set(names) == {"hstu_beam_workspace_size", "hstu_beam_decode_attn"}
+    lib = hb._lib_beam()
+    for n in names:
+        assert hasattr(lib, n)
+    good = dict(num_requests=4, beam_width=256, num_q_heads=16, num_kv_heads=8, head_dim=128, max_ctx=1024,
+                step=2, max_steps=3, scale=128 ** -0.5, dtype=1)
+    n = ctypes.c_size_t(0)
+    assert lib.hstu_beam_workspace_size(ctypes.byref(hb.BeamDesc(**good)), ctypes.byref(n)) == 0 and n.value > 0
+    for over, code in [(dict(head_dim=32), -2), (dict(dtype=5), -2), (dict(max_ctx=1000), -1),
+                       (dict(num_q_heads=12, num_kv_heads=8), -1), (dict(step=3), -1), (dict(beam_width=0), -1),
+                       (dict(scale=0.0), -1), (dict(num_requests=-1), -1)]:
+        kw = dict(good)
+        kw.update(over)
+        assert lib.hstu_beam_workspace_size(ctypes.byref(hb.BeamDesc(**kw)), ctypes.byref(n)) == code, over
+    # valid sizes, null pointers
+    assert lib.hstu_beam_decode_attn(ctypes.byref(hb.BeamDesc(**good)), *([None] * 9), 0, None) == -1

@@ -58,6 +58,9 @@ def parse():
                     help="ranking requests shaped like the pages' workload (8,198 cached context+history "
                          "tokens, 100 candidates, batch 8, 3 and 8 layers): tokens -> preprocessing -> "
                          "layers with candidates, cached vs full recompute")
+    ap.add_argument("--beam", action="store_true",
+                    help="Semantic-ID beam-decode attention over a shared context KV (4 requests, beam 256, "
+                         "16 query / 8 KV heads of 128, bf16; contexts 1,000 and 5,000; steps 0-2)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -562,8 +565,75 @@ def rank_bench(args):
                    "position_table": max_pos, "page_size": ps, "item_table_rows": n_items}}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Beam-decode attention of Semantic-ID GR on the pages' request shapes
+# (offline: 4 requests, context 1,000, beam 256, 3 decoded tokens; online:
+# context 5,000, concurrency 4).  The decoder's attention shape (16 query
+# heads, 8 KV heads, head dim 128, bf16) is that of a Qwen3-1.7B-class model,
+# which the pages name without giving its shape.  One call = one decode step
+# of one layer for every beam of every request.
+# ---------------------------------------------------------------------------
+def beam_bench(args):
+    import torch
+    from hstu_jagged_silu_fwd_amd import _lib
+    from hstu_jagged_silu_fwd_amd import beam as hb
+    R, W, Hq, Hkv, d, S = 4, 256, 16, 8, 128, 3
+    rng = torch.Generator(device="cuda").manual_seed(args.seed)
+    bf = torch.bfloat16
+    lib = hb._lib_beam()
+    res = {}
+    for ctx in (1000, 5000):
+        Cmax = (ctx + 31) // 32 * 32
+        rnd = lambda *shape: torch.randn(*shape, generator=rng, device="cuda", dtype=torch.float32).to(bf)
+        q = rnd(R, W, Hq, d)
+        ck, cvt = rnd(R, Hkv, Cmax, d), rnd(R, Hkv, d, Cmax)
+        bk, bv = rnd(R, S, W, Hkv, d), rnd(R, S, W, Hkv, d)
+        ctx_len = torch.full((R,), ctx, dtype=torch.int32, device="cuda")
+        path = torch.randint(0, W, (R, W, S), generator=rng, device="cuda", dtype=torch.int32)
+        out = torch.empty_like(q)
+        per = {}
+        for t in range(S):
+            desc = hb.make_desc(q, ck, bk, t, d ** -0.5)
+            ws = torch.empty(hb.workspace_size(desc), dtype=torch.uint8, device="cuda")
+            pth = path[:, :, :t].contiguous() if t else None
+            argv = [ctypes.byref(desc)] + [ctypes.c_void_p(x.data_ptr()) if x is not None else None
+                                           for x in (q, ck, cvt, ctx_len, bk, bv, pth, out, ws)] + \
+                   [ctypes.c_size_t(ws.numel()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)]
+            for _ in range(args.warmup):
+                lib.hstu_beam_decode_attn(*argv)
+            torch.cuda.synchronize()
+            assert int(ws[:4].view(torch.int32).item()) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                rc = lib.hstu_beam_decode_attn(*argv)
+            e1.record()
+            torch.cuda.synchronize()
+            assert rc == 0
+            us = 1e3 * e0.elapsed_time(e1) / args.steps
+            keys = ctx + t + 1
+            flops = 4.0 * R * W * Hq * keys * d
+            byts = 2.0 * (2 * R * Hkv * ctx * d + 2 * R * W * Hq * d + 2 * R * (t + 1) * W * Hkv * d)
+            per[f"step{t}"] = dict(us=us, tflops=flops / us / 1e6, mfma_frac=flops / us / 1e6 / BF16_PEAK_TFLOPS,
+                                   gbs=byts / us / 1e3, hbm_frac=byts / us / 1e3 / HBM_PEAK_GBS,
+                                   algorithmic_bytes=byts, flops=flops)
+        res[f"ctx{ctx}"] = per
+        del q, ck, cvt, bk, bv, out
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "Semantic-ID beam-decode attention per decode step and layer", "unit": "us",
+        "higher_is_better": False, "n_gpus": 1, "dtype": "bf16", "data": "synthetic", "steps": args.steps,
+        "results": res,
+        "config": {"workload": "sid-beam-decode-r4-w256-hq16-hkv8-d128", "requests": R, "beam_width": W,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "contexts": [1000, 5000], "decode_steps": S,
+                   "timing": "event-bracketed back-to-back calls (split kernel + combine kernel)"}}), flush=True)
+
+
 def main():
     args = parse()
+    if args.beam:
+        beam_bench(args)
+        return
     if args.rank:
         rank_bench(args)
         return

@@ -130,7 +130,7 @@ struct StepGeo {
   static_assert(NST * STAGE >= (PMAX - 1) * (kWaves / PMAX) * kGpw * 16 * HD * 4, "reduction fits the ring");
 };
 
-template <typename T, int HD>
+template <typename T, int HD, bool CAND>
 __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   using G = StepGeo<T, HD>;
   constexpr int CE = G::CE, KCH = G::KCH, VCH = G::VCH, NST = G::NST, IPW = G::IPW;
@@ -215,8 +215,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     const int n = __builtin_amdgcn_readfirstlane(item.b.z);
     const int c = __builtin_amdgcn_readfirstlane(item.b.w);
     const int len = c + n;
-    // first candidate position (none: past every key)
-    const int cs = a.ncand != nullptr ? len - a.ncand[u] : 0x7fffffff;
+    // first candidate position (the instance without candidates has none)
+    const int cs = CAND ? len - a.ncand[u] : 0x7fffffff;
     const int nq = min(kQB, n - q0);
     const int ngroups = (nq + 15) >> 4;
     // Phases: the waves form P phases of WP = kWaves/P waves (columns);
@@ -421,16 +421,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       for (int i = 0; i < NG; ++i) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) av[i][e] *= st[i][e >> 2][e & 3];
-        if (dmn[i] < 0 && kb + kStepKeys <= cs) {    // causal mask on the diagonal
-#pragma unroll
-          for (int e = 0; e < 8; ++e) av[i][e] = dl0[i] - e >= 0 ? av[i][e] : 0.0f;
-        } else if (kb + kStepKeys > cs) {            // keys at or past the candidates
+        if (CAND && kb + kStepKeys > cs) {           // keys at or past the candidates
           const int ce = cs - (kb + 8 * g);          // element e's key is past cs when e >= ce
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int de = dl0[i] - e;
             av[i][e] = (de >= 0 && (e < ce || de == 0)) ? av[i][e] : 0.0f;
           }
+        } else if (dmn[i] < 0) {                     // causal mask on the diagonal
+#pragma unroll
+          for (int e = 0; e < 8; ++e) av[i][e] = dl0[i] - e >= 0 ? av[i][e] : 0.0f;
         }
         set_frag(af[i], av[i]);
       }
@@ -560,7 +560,8 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.mbits = d.pos_mbits;
   a.ntsb = d.ts_buckets;
   a.tsmbits = d.ts_mbits;
-  return launch_kernel(attn_kernel<T, HD>, dim3(grid), dim3(64 * kWaves), stream, ev, a);
+  if (ncand != nullptr) return launch_kernel(attn_kernel<T, HD, true>, dim3(grid), dim3(64 * kWaves), stream, ev, a);
+  return launch_kernel(attn_kernel<T, HD, false>, dim3(grid), dim3(64 * kWaves), stream, ev, a);
 }
 
 template <typename T>

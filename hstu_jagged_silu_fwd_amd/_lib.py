@@ -73,6 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_layer_fwd_timed.restype = I32
     lib.hstu_layer_fwd_cand.argtypes = [dp, P, P, P, P] + layer_args[4:] + [P]
     lib.hstu_layer_fwd_cand.restype = I32
+    lib.hstu_stack_workspace_size.argtypes = [dp, I32, ctypes.POINTER(SZ)]
+    lib.hstu_stack_workspace_size.restype = I32
+    lib.hstu_stack_fwd.argtypes = [dp, I32] + [P] * 15 + [SZ, P]
+    lib.hstu_stack_fwd.restype = I32
     lib.hstu_preprocess.argtypes = [ctypes.POINTER(PrepDesc)] + [P] * 17
     lib.hstu_preprocess.restype = I32
     lib.kv_pages_append.argtypes = [dp, P, P, P, P, P, P, P, P, P]
@@ -221,6 +225,40 @@ def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_p
         rc = lib.hstu_layer_fwd(*args)
     if rc != 0:
         raise HSTUError(rc, "hstu_layer_fwd")
+
+
+def stack_workspace_size(desc: LayerDesc, num_layers: int) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().hstu_stack_workspace_size(ctypes.byref(desc), int(num_layers), ctypes.byref(n))
+    if rc != 0:
+        raise HSTUError(rc, "hstu_stack_workspace_size")
+    return int(n.value)
+
+
+def stack_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_tables, k_pools, v_pools, w1t, w2t, pos_bias,
+              ys, workspace, ts_bias=None, timestamps=None, ts_offsets=None, num_candidates=None,
+              stream=None) -> None:
+    """Enqueue hstu_stack_fwd (include/hstu.h): per-layer arguments are
+    sequences of device tensors, one per layer; ys[l] receives layer l."""
+    import torch
+    dt = _tdtype(desc)
+    nl = len(w1t)
+    arr = lambda vals: (ctypes.c_void_p * nl)(*[ctypes.c_void_p(v) for v in vals])
+    none_rows = desc.total_new == 0
+    rc = load().hstu_stack_fwd(
+        ctypes.byref(desc), nl, _ptr(x, "x", dt, allow_none=none_rows), _ptr(new_offsets, "new_offsets", torch.int32),
+        _ptr(hist_len, "hist_len", torch.int32), _ptr(num_candidates, "num_candidates", torch.int32, allow_none=True),
+        arr([_ptr(t, "page_table", torch.int32) for t in page_tables]),
+        arr([_ptr(t, "k_pool", dt) for t in k_pools]), arr([_ptr(t, "v_pool", dt) for t in v_pools]),
+        arr([_ptr(t, "w1t", dt) for t in w1t]), arr([_ptr(t, "w2t", dt) for t in w2t]),
+        arr([_ptr(t, "pos_bias", torch.float32) for t in pos_bias]),
+        None if ts_bias is None else arr([_ptr(t, "ts_bias", torch.float32) for t in ts_bias]),
+        _ptr(timestamps, "timestamps", torch.int64, allow_none=True),
+        _ptr(ts_offsets, "ts_offsets", torch.int32, allow_none=True),
+        arr([_ptr(t, "y", dt, allow_none=none_rows) or 0 for t in ys]), _ptr(workspace, "workspace"),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
+    if rc != 0:
+        raise HSTUError(rc, "hstu_stack_fwd")
 
 
 def preprocess(*, hist_len, ctx_offsets, ctx_ids, hist_offsets, item_ids, action_ids, cand_offsets,

@@ -28,7 +28,7 @@ int attn_grid() {
   return cus * kAttnWgPerCu;
 }
 
-Layout make_layout(const hstu_layer_desc& d, int target) {
+Layout make_layout(const hstu_layer_desc& d, int target, int nl = 1) {
   Layout L{};
   const size_t T = static_cast<size_t>(d.total_new);
   const size_t B = static_cast<size_t>(d.num_users);
@@ -40,7 +40,7 @@ Layout make_layout(const hstu_layer_desc& d, int target) {
   const int64_t per_entry = 1 + (max_len + kMaxChunkKeys - 1) / kMaxChunkKeys;
   L.item_cap = static_cast<int>(d.num_heads * L.nqb_cap * per_entry + target);
   size_t off = 256;  // WsHeader
-  L.row_loc = off;  off = align256(off + 8 * T);
+  L.row_loc = off;  off = align256(off + 8 * T * static_cast<size_t>(nl));
   L.qb_first = off; off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
   L.qb_nch = off;   off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
   L.qb_row0 = off;  off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
@@ -138,7 +138,7 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
     return k;
   };
   hipError_t e;
-  e = launch_prep(d, new_offsets, hist_len, ncand, page_table, ts_off, ws, L.nqb_cap, L.item_cap, grid, st,
+  e = launch_prep(d, new_offsets, hist_len, ncand, &page_table, 1, ts_off, ws, L.nqb_cap, L.item_cap, grid, st,
                   kev(HSTU_STAGE_PREP));
   if (e != hipSuccess) return HSTU_ERR_HIP;
   if (!any_rows) return HSTU_OK;
@@ -154,9 +154,80 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
   return HSTU_OK;
 }
 
+// A stack of nl layers over one batch: the metadata is prepared and checked
+// once (every layer's page table included), then each layer runs its four
+// compute kernels; layer l reads layer l-1's output.
+hstu_status stack_impl(const hstu_layer_desc* desc, int32_t nl, const void* x, const int32_t* new_offsets,
+                       const int32_t* hist_len, const int32_t* ncand, const int32_t* const* pts,
+                       void* const* kps, void* const* vps, const void* const* w1s, const void* const* w2s,
+                       const float* const* pbs, const float* const* tsbs, const int64_t* timestamps,
+                       const int32_t* ts_offsets, void* const* ys, void* workspace, size_t workspace_bytes,
+                       void* hip_stream) {
+  hstu_status s = check_layer(desc);
+  if (s != HSTU_OK) return s;
+  if (nl < 1 || nl > kMaxStackLayers) return HSTU_ERR_INVALID_ARG;
+  const hstu_layer_desc& d = *desc;
+  const bool any_rows = d.total_new > 0;
+  const bool has_ts = d.ts_buckets > 0;
+  if (new_offsets == nullptr || hist_len == nullptr || pts == nullptr || kps == nullptr || vps == nullptr ||
+      w1s == nullptr || w2s == nullptr || pbs == nullptr || ys == nullptr || workspace == nullptr)
+    return HSTU_ERR_INVALID_ARG;
+  if (has_ts && (tsbs == nullptr || timestamps == nullptr || ts_offsets == nullptr)) return HSTU_ERR_INVALID_ARG;
+  for (int l = 0; l < nl; ++l) {
+    if (pts[l] == nullptr || kps[l] == nullptr || vps[l] == nullptr || w1s[l] == nullptr || w2s[l] == nullptr ||
+        pbs[l] == nullptr || (has_ts && tsbs[l] == nullptr))
+      return HSTU_ERR_INVALID_ARG;
+    if (any_rows && (ys[l] == nullptr || ys[l] == (l == 0 ? x : ys[l - 1]))) return HSTU_ERR_INVALID_ARG;
+  }
+  if (any_rows && x == nullptr) return HSTU_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return HSTU_ERR_INVALID_ARG;
+  const int grid = attn_grid();
+  const Layout L = make_layout(d, grid, nl);
+  if (workspace_bytes < L.total) return HSTU_ERR_WORKSPACE;
+  const WsPtrs ws = ws_ptrs(workspace, L);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const int32_t* ts_off = has_ts ? ts_offsets : nullptr;
+  const int64_t* ts = has_ts ? timestamps : nullptr;
+  hipError_t e = launch_prep(d, new_offsets, hist_len, ncand, pts, nl, ts_off, ws, L.nqb_cap, L.item_cap, grid, st);
+  if (e != hipSuccess) return HSTU_ERR_HIP;
+  if (!any_rows) return HSTU_OK;
+  for (int l = 0; l < nl; ++l) {
+    WsPtrs wl = ws;
+    wl.row_loc = ws.row_loc + static_cast<size_t>(l) * d.total_new;   // this layer's pool slots
+    e = launch_gemm_qkv(d, l == 0 ? x : ys[l - 1], w1s[l], kps[l], vps[l], wl, st);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    e = launch_attn(d, pts[l], kps[l], vps[l], pbs[l], has_ts ? tsbs[l] : nullptr, ts, ts_off, ncand, ws,
+                    grid < L.item_cap ? grid : L.item_cap, st);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    e = launch_norm_gate(d, ws, L.nqb_cap, st);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    e = launch_gemm_out(d, ws.q, w2s[l], ys[l], &ws.hdr->status, st);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+  }
+  return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+hstu_status hstu_stack_workspace_size(const hstu_layer_desc* desc, int32_t num_layers, size_t* bytes) {
+  hstu_status s = check_layer(desc);
+  if (s != HSTU_OK) return s;
+  if (bytes == nullptr || num_layers < 1 || num_layers > kMaxStackLayers) return HSTU_ERR_INVALID_ARG;
+  *bytes = make_layout(*desc, attn_grid(), num_layers).total;
+  return HSTU_OK;
+}
+
+hstu_status hstu_stack_fwd(const hstu_layer_desc* desc, int32_t num_layers, const void* x,
+                           const int32_t* new_offsets, const int32_t* hist_len, const int32_t* num_candidates,
+                           const int32_t* const* page_tables, void* const* k_pools, void* const* v_pools,
+                           const void* const* w1t, const void* const* w2t, const float* const* pos_bias,
+                           const float* const* ts_bias, const int64_t* timestamps, const int32_t* ts_offsets,
+                           void* const* y, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return stack_impl(desc, num_layers, x, new_offsets, hist_len, num_candidates, page_tables, k_pools, v_pools, w1t,
+                    w2t, pos_bias, ts_bias, timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream);
+}
 
 hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes) {
   hstu_status s = check_layer(desc);

@@ -22,6 +22,7 @@ constexpr int kMaxBuckets = 1024;
 constexpr int kMaxChunkKeys = 8192;   // attention split never exceeds this many keys
 constexpr int kMaxRows = 1 << 18;     // new rows per call
 constexpr int kMaxQBlocks = kMaxRows / kQB + kMaxUsers;
+constexpr int kMaxStackLayers = 32;   // layers of one hstu_stack_fwd call
 
 // ---------------------------------------------------------------------------
 // MFMA fragments.  A fragment holds 8 elements per lane.  For a 16x16 tile
@@ -233,7 +234,7 @@ struct AttnItem {
 
 struct WsPtrs {
   WsHeader* hdr;
-  int2* row_loc;             // [T] (pool page, slot) of each new row's K/V
+  int2* row_loc;             // [layers][T] (pool page, slot) of each new row's K/V
   int32_t* qb_first;         // [nqb_cap] first work item of a q-block entry (head 0)
   int32_t* qb_nch;           // [nqb_cap] key chunks of a q-block entry
   int32_t* qb_row0;          // [nqb_cap] first jagged row of a q-block entry
@@ -267,7 +268,8 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 // Host launchers (one per kernel family), all enqueue on `stream`.
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
-                       const int32_t* ncand, const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
+                       const int32_t* ncand, const int32_t* const* pts, int nl, const int32_t* ts_off,
+                       const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream,
                        const KernelEvents& ev = {});
 hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,

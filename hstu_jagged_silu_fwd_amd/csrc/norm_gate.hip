@@ -20,7 +20,7 @@ constexpr int kThreads = 256;
 
 template <typename T>
 struct NormArgs {
-  const WsHeader* hdr;
+  WsHeader* hdr;
   const int32_t* qb_first;          // [entries] first work item (head 0)
   const int32_t* qb_nch;            // [entries] key chunks
   const int32_t* qb_row0;           // [entries] first jagged row
@@ -71,6 +71,9 @@ __global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
   const int D = a.D;
   const int e = blockIdx.x / kBlocks, rb = blockIdx.x % kBlocks;   // q-block entry, row block in it
   const int4 hv = *reinterpret_cast<const int4*>(a.hdr);   // status, wl_status, items, entries
+  // the attention kernel of this layer is done with its work-fetch counter:
+  // reset it for the next layer of a stack (whose prep does not run again)
+  if (blockIdx.x == 0 && tid == 0) a.hdr->counter = 0;
   const int first = a.qb_first[e], nch = a.qb_nch[e], row0 = a.qb_row0[e], rows = a.qb_rows[e];
   // all five loads are issued before the exit test (no short-circuit chain
   // of dependent loads)

@@ -48,10 +48,10 @@ struct PrepArgs {
   const int32_t* new_off;
   const int32_t* hist;
   const int32_t* ncand;
-  const int32_t* pt;
+  const int32_t* pt[kMaxStackLayers];   // page table of each layer (nl of them)
   const int32_t* ts_off;
   WsPtrs ws;
-  int B, T, H, ps, maxP;
+  int B, T, H, ps, maxP, nl;
   int64_t P;
   int nqb_cap, item_cap, target_items;
 };
@@ -126,16 +126,19 @@ __device__ void map_rows(const PrepArgs& a, const PrepShared& s, int slice) {
     user[i] = r < a.T ? row_to_user(s.off, a.B, r) : 0;
     pos[i] = r < a.T ? s.hist[user[i]] + (r - s.off[user[i]]) : -1;
   }
+  for (int l = 0; l < a.nl; ++l) {                   // every layer's pages (one per call but a stack's)
+    const int32_t* pt = a.pt[l];
 #pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const bool ok = pos[i] >= 0 && pos[i] / a.ps < a.maxP;
-    pg[i] = ok ? a.pt[static_cast<size_t>(user[i]) * a.maxP + pos[i] / a.ps] : -1;
-  }
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const bool ok = pos[i] >= 0 && pos[i] / a.ps < a.maxP;
+      pg[i] = ok ? pt[static_cast<size_t>(user[i]) * a.maxP + pos[i] / a.ps] : -1;
+    }
 #pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const int r = r0 + i * kPrepThreads;
-    if (r < a.T) {
-      a.ws.row_loc[r] = make_int2(pg[i], pos[i] >= 0 ? pos[i] % a.ps : 0);
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int r = r0 + i * kPrepThreads;
+      if (r < a.T) {
+        a.ws.row_loc[static_cast<size_t>(l) * a.T + r] = make_int2(pg[i], pos[i] >= 0 ? pos[i] % a.ps : 0);
+      }
     }
   }
 }
@@ -231,19 +234,25 @@ __device__ void validate(const PrepArgs& a, PrepShared& s) {
     const int i_beg = min(total_pages, tid * m), i_end = min(total_pages, i_beg + m);
     int u = i_beg < i_end ? entry_user(s.pgp, B, i_beg) : 0;
     int u_end = s.pgp[u + 1];                        // first flat index past user u
-    for (int i0 = i_beg; i0 < i_end; i0 += kU) {
-      int32_t pg[kU];
+    const int u_first = u, u_end_first = u_end;
+    for (int l = 0; l < a.nl; ++l) {                 // every layer's table
+      const int32_t* pt = a.pt[l];
+      u = u_first;
+      u_end = u_end_first;
+      for (int i0 = i_beg; i0 < i_end; i0 += kU) {
+        int32_t pg[kU];
 #pragma unroll
-      for (int k = 0; k < kU; ++k) {
-        const int i = i0 + k;
-        pg[k] = 0;
-        if (i < i_end) {
-          while (i >= u_end) u_end = s.pgp[++u + 1];   // skips users without pages
-          pg[k] = a.pt[static_cast<size_t>(u) * a.maxP + (i - s.pgp[u])];
+        for (int k = 0; k < kU; ++k) {
+          const int i = i0 + k;
+          pg[k] = 0;
+          if (i < i_end) {
+            while (i >= u_end) u_end = s.pgp[++u + 1];   // skips users without pages
+            pg[k] = pt[static_cast<size_t>(u) * a.maxP + (i - s.pgp[u])];
+          }
         }
-      }
 #pragma unroll
-      for (int k = 0; k < kU; ++k) bad |= pg[k] < 0 || pg[k] >= a.P;
+        for (int k = 0; k < kU; ++k) bad |= pg[k] < 0 || pg[k] >= a.P;
+      }
     }
   }
   const bool wave_bad = __any(bad);
@@ -443,14 +452,16 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
 }  // namespace
 
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
-                       const int32_t* ncand, const int32_t* pt, const int32_t* ts_off, const WsPtrs& ws,
+                       const int32_t* ncand, const int32_t* const* pts, int nl, const int32_t* ts_off,
+                       const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream,
                        const KernelEvents& ev) {
   PrepArgs a;
   a.new_off = new_off;
   a.hist = hist;
   a.ncand = ncand;
-  a.pt = pt;
+  for (int l = 0; l < kMaxStackLayers; ++l) a.pt[l] = l < nl ? pts[l] : nullptr;
+  a.nl = nl;
   a.ts_off = ts_off;
   a.ws = ws;
   a.B = d.num_users;

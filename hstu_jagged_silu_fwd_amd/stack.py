@@ -41,6 +41,8 @@ class HSTUStack:
         self.layers: List[dict] = [dict() for _ in range(num_layers)]
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         self._ws = None
+        self._sws = None          # workspace of the stack calls
+        self._last_ws = None      # workspace of the last call (its status word)
 
     def desc(self, total_new: int, num_users: Optional[int] = None) -> _lib.LayerDesc:
         kw = dict(self.common)
@@ -93,6 +95,7 @@ class HSTUStack:
             need = _lib.workspace_size(desc)
             if ws.numel() < need:
                 self._ws = ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        self._last_ws = ws
         _lib.layer_fwd(desc, x, new_offsets, hist_len, L["page_table"] if page_table is None else page_table, self.k_pool,
                        self.v_pool, L["w1t"], L["w2t"], L["pos_bias"], y, ws,
                        ts_bias=L["ts_bias"], timestamps=timestamps, ts_offsets=ts_offsets,
@@ -100,23 +103,37 @@ class HSTUStack:
 
     def forward(self, x, new_offsets, hist_len, timestamps=None, ts_offsets=None,
                 stream=None, return_all: bool = False, page_tables=None, num_candidates=None):
-        """Run every layer; returns the last layer's output (or all outputs).
-        page_tables: optional per-layer [B, max_pages] tables (e.g. a KV cache
-        plan's, from KVCache.build_tables) instead of the layers' own."""
+        """Run every layer in one hstu_stack_fwd call (the batch metadata is
+        prepared once for all layers); returns the last layer's output (or
+        all outputs).  page_tables: optional per-layer [B, max_pages] tables
+        (e.g. a KV cache plan's, from KVCache.build_tables) instead of the
+        layers' own."""
         x = self._dev(x, self.tdtype)
         off = self._dev(new_offsets, torch.int32)
         hl = self._dev(hist_len, torch.int32)
         ts = None if timestamps is None else self._dev(timestamps, torch.int64)
         tso = None if ts_offsets is None else self._dev(ts_offsets, torch.int32)
         nc = None if num_candidates is None else self._dev(num_candidates, torch.int32)
-        outs = []
-        for l in range(len(self.layers)):
-            y = torch.empty_like(x)
-            self.layer(l, x, off, hl, y, timestamps=ts, ts_offsets=tso, stream=stream,
-                       page_table=None if page_tables is None else page_tables[l], num_candidates=nc)
-            outs.append(y)
-            x = y
+        T = int(x.shape[0])
+        nl = len(self.layers)
+        nu = None if page_tables is None else int(off.shape[0]) - 1
+        desc = self.desc(T, nu)
+        need = _lib.stack_workspace_size(desc, nl)
+        if self._sws is None or self._sws.numel() < need:
+            self._sws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        outs = [torch.empty_like(x) for _ in range(nl)]
+        L = self.layers
+        pts = [L[l]["page_table"] for l in range(nl)] if page_tables is None else \
+            [self._dev(page_tables[l], torch.int32) for l in range(nl)]
+        has_ts = L[0]["ts_bias"] is not None
+        _lib.stack_fwd(desc, x, off, hl, pts, [self.k_pool] * nl, [self.v_pool] * nl, [l["w1t"] for l in L],
+                       [l["w2t"] for l in L], [l["pos_bias"] for l in L], outs, self._sws,
+                       ts_bias=[l["ts_bias"] for l in L] if has_ts else None, timestamps=ts, ts_offsets=tso,
+                       num_candidates=nc, stream=stream)
+        self._last_ws = self._sws
         return outs if return_all else outs[-1]
 
     def read_status(self, workspace: Optional[torch.Tensor] = None) -> int:
-        return _lib.read_device_status(self._ws if workspace is None else workspace)
+        """Device status of the last call: the given workspace, else that of
+        the last forward (stack call) or layer call, whichever ran last."""
+        return _lib.read_device_status(self._last_ws if workspace is None else workspace)

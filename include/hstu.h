@@ -250,6 +250,33 @@ hstu_status hstu_preprocess(const hstu_prep_desc* desc, const int32_t* hist_len,
                             void* x, int32_t* new_offsets, int32_t* num_candidates,
                             int32_t* device_status, void* hip_stream);
 
+/* A stack of num_layers layers over one batch, layer l's output feeding
+ * layer l+1 (the HSTU blocks applied in sequence, NVIDIA blog above, section
+ * "Why use HSTU for generative recommendation"), in one call whose batch
+ * metadata -- validation, the attention work list, every layer's pool slots
+ * -- is prepared once for all layers instead of once per layer.  Results
+ * are those of num_layers hstu_layer_fwd_cand (num_candidates != NULL) or
+ * hstu_layer_fwd calls with the same arguments, bit for bit.
+ *   num_layers in [1, 32]
+ *   page_tables, k_pools, v_pools, w1t, w2t, pos_bias, ts_bias, y: HOST
+ *     arrays of num_layers DEVICE pointers, one per layer, each as in
+ *     hstu_layer_fwd (ts_bias may be NULL when ts_buckets == 0); y[l]
+ *     receives layer l's output [T, D] and must not alias its input (x for
+ *     layer 0, y[l-1] after), so two buffers used in turn suffice
+ *   num_candidates: as in hstu_layer_fwd_cand, or NULL
+ *   workspace: hstu_stack_workspace_size(desc, num_layers) bytes
+ * Every page table is validated before any layer runs: a data problem in
+ * any of them stops the whole stack (nothing is written). */
+hstu_status hstu_stack_workspace_size(const hstu_layer_desc* desc, int32_t num_layers, size_t* bytes);
+hstu_status hstu_stack_fwd(const hstu_layer_desc* desc, int32_t num_layers, const void* x,
+                           const int32_t* new_offsets, const int32_t* hist_len,
+                           const int32_t* num_candidates, const int32_t* const* page_tables,
+                           void* const* k_pools, void* const* v_pools, const void* const* w1t,
+                           const void* const* w2t, const float* const* pos_bias,
+                           const float* const* ts_bias, const int64_t* timestamps,
+                           const int32_t* ts_offsets, void* const* y, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
 /* Append new rows' K and V into the pools (the paged KV table's append, NVIDIA
  * blog above, same section).  k_new, v_new [T, D] dtype, rows laid out as x in
  * hstu_layer_fwd; row t of user u goes to position hist_len[u] + t.  Only

@@ -21,8 +21,9 @@ def test_exports_every_header_function():
     lib = hs.load()
     names = list(hs.header_functions())
     assert set(names) == {"hstu_layer_workspace_size", "hstu_layer_fwd", "hstu_layer_fwd_timed",
-                          "hstu_layer_fwd_cand", "hstu_preprocess", "kv_pages_append",
-                          "hstu_read_device_status", "hstu_status_string"}
+                          "hstu_layer_fwd_cand", "hstu_stack_workspace_size", "hstu_stack_fwd",
+                          "hstu_preprocess", "kv_pages_append", "hstu_read_device_status",
+                          "hstu_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -145,3 +146,19 @@ def test_beam_header_exports_and_host_checks():
         assert lib.hstu_beam_workspace_size(ctypes.byref(hb.BeamDesc(**kw)), ctypes.byref(n)) == code, over
     # valid sizes, null pointers
     assert lib.hstu_beam_decode_attn(ctypes.byref(hb.BeamDesc(**good)), *([None] * 9), 0, None) == -1
+
+
+def test_stack_host_checks():
+    """hstu_stack_fwd / hstu_stack_workspace_size reject bad layer counts and
+    missing per-layer arrays before touching the GPU."""
+    import ctypes
+    lib = hs.load()
+    d = desc()
+    n = ctypes.c_size_t(0)
+    assert lib.hstu_stack_workspace_size(ctypes.byref(d), 3, ctypes.byref(n)) == 0
+    one = ctypes.c_size_t(0)
+    assert lib.hstu_stack_workspace_size(ctypes.byref(d), 1, ctypes.byref(one)) == 0 and n.value >= one.value
+    for nl in (0, 33):
+        assert lib.hstu_stack_workspace_size(ctypes.byref(d), nl, ctypes.byref(n)) == -1
+    # desc, layers, x, offsets, hist, candidates, 9 per-layer arrays and tensors, y, ws, bytes, stream
+    assert lib.hstu_stack_fwd(ctypes.byref(d), 3, *([None] * 15), 0, None) == -1

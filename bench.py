@@ -461,6 +461,32 @@ def kvhost_bench(args):
 #              (66,384 rows) with the last 100 as candidates.
 # Latency per logical request = time of one batch / 8.
 # ---------------------------------------------------------------------------
+def rank_cpu_baseline(hist, m, D, H, L, min_seconds=10.0):
+    """The fp64 oracle on cached ranking requests of one user each (its
+    history K/V given, its m candidates computed through L layers), request
+    after request until min_seconds of CPU work are done."""
+    import threadpoolctl
+    from oracle import layer as olayer
+    rng = np.random.default_rng(1)
+    layers = [dict(w1=rng.normal(0, 0.02, (D, 4 * D)), w2=rng.normal(0, 0.02, (D, D)),
+                   pos_bias=rng.normal(0, 0.1, 128), hist_k=[rng.normal(0.05, 0.24, (hist, D))],
+                   hist_v=[rng.normal(0.05, 0.24, (hist, D))]) for _ in range(L)]
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        olayer.stack_forward(rng.normal(0, 1, (m, D)), [m], [hist], layers, 1.0 / 8320, EPS, H, 3,
+                             num_candidates=[m])
+        n += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return dict(value=1e3 * dt / n, unit="ms per logical request", cores=int(threads), kind="oracle",
+                sample=f"{n} cached ranking requests of one user ({m} candidates over {hist} cached tokens, "
+                       f"{L} layers), fp64 numpy, {dt:.1f} s")
+
+
 def rank_bench(args):
     import torch
     from hstu_jagged_silu_fwd_amd import _lib
@@ -537,16 +563,29 @@ def rank_bench(args):
                               ctypes.c_void_p(ys[l % 2].data_ptr()), ctypes.c_void_p(ws.data_ptr()),
                               ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream), None])
 
+            # the timed request: preprocessing, then the whole stack in one call
+            sws = torch.empty(max(_lib.stack_workspace_size(ldesc, L), ws.numel()), dtype=torch.uint8, device=dev)
+            P = ctypes.c_void_p
+            parr = lambda vals: (P * L)(*[P(v) for v in vals])
+            keep = [parr([st.layers[l]["page_table"].data_ptr() for l in range(L)]),
+                    parr([st.k_pool.data_ptr()] * L), parr([st.v_pool.data_ptr()] * L),
+                    parr([st.layers[l]["w1t"].data_ptr() for l in range(L)]),
+                    parr([st.layers[l]["w2t"].data_ptr() for l in range(L)]),
+                    parr([st.layers[l]["pos_bias"].data_ptr() for l in range(L)]),
+                    parr([ys[l % 2].data_ptr() for l in range(L)])]
+            sargs = [ctypes.byref(ldesc), L, ptr("x"), ptr("new_offsets"), ptr("hist_len"), ptr("num_candidates"),
+                     *keep[:6], None, None, None, keep[6], P(sws.data_ptr()), ctypes.c_size_t(sws.numel()),
+                     P(stream)]
+
             def run():
                 rc = lib.hstu_preprocess(*pargs)
-                for a in largs:
-                    rc |= lib.hstu_layer_fwd_cand(*a)
+                rc |= lib.hstu_stack_fwd(*sargs)
                 if rc != 0:
                     raise RuntimeError(f"ranking request failed: {rc}")
             for _ in range(args.warmup):
                 run()
             torch.cuda.synchronize()
-            assert int(req["device_status"].item()) == 0 and st.read_status(ws) == 0
+            assert int(req["device_status"].item()) == 0 and st.read_status(sws) == 0
             t0 = time.perf_counter()
             for _ in range(steps):
                 run()
@@ -564,10 +603,47 @@ def rank_bench(args):
             res[kind] = dict(rows=T, ms_per_batch=1e3 * wall, ms_per_request=1e3 * wall / B,
                              tokens_per_s=T / wall, preprocess_us=prep_us,
                              preprocess_gbs=prep_bytes / (prep_us * 1e-6) / 1e9)
+            if kind == "hit" and L == 3:
+                # event pass over the same calls: each layer's stage kernels
+                # bracketed by runtime-stamped events; the attention's roofline
+                hip = _lib.hip_runtime()
+                hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+                hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+                nev = 2 * _lib.NUM_STAGES
+                evs = []
+                for _ in range(steps * L):
+                    arr = (ctypes.c_void_p * nev)()
+                    for j in range(nev):
+                        e = ctypes.c_void_p()
+                        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+                        arr[j] = e
+                    evs.append(arr)
+                for st_i in range(steps):
+                    lib.hstu_preprocess(*pargs)
+                    for l, a_l in enumerate(largs):
+                        assert lib.hstu_layer_fwd_cand(*a_l[:-1], evs[st_i * L + l]) == 0
+                torch.cuda.synchronize()
+                ms = ctypes.c_float(0)
+                stage = np.zeros(_lib.NUM_STAGES)
+                for arr in evs:
+                    for k in range(_lib.NUM_STAGES):
+                        assert hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * k], arr[2 * k + 1]) == 0
+                        stage[k] += ms.value
+                stage_us = 1e3 * stage / len(evs)
+                attn_bytes = B * (hist + m) * 4 * D + T * D * 2 + T * D * 4   # K/V rows once, Q, fp32 partial out
+                attn_flops = 4 * D * B * m * (hist + 1)
+                ach = attn_bytes / (stage_us[2] * 1e-6) / 1e9
+                res["hit"]["stages_us"] = {n: float(v) for n, v in zip(_lib.STAGES, stage_us)}
+                res["hit"]["roofline"] = dict(kernel="paged_silu_attn (candidates)", bound="hbm", achieved=ach,
+                                              peak=HBM_PEAK_GBS, unit="GB/s", frac=ach / HBM_PEAK_GBS,
+                                              traffic=None, mean_us=float(stage_us[2]),
+                                              bytes_per_launch=attn_bytes,
+                                              mfma_frac=attn_flops / (stage_us[2] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS)
         res["recompute_over_hit"] = res["recompute"]["ms_per_batch"] / res["hit"]["ms_per_batch"]
         out_all[f"{L}layer"] = res
         del st
         torch.cuda.empty_cache()
+    out_all["cpu_baseline"] = None if args.no_cpu_baseline else rank_cpu_baseline(hist, m, D, H, 3)
     print(json.dumps({
         "metric": "ranking request latency, pages-shaped workload (cached history vs full recompute)",
         "unit": "ms per logical request", "higher_is_better": False, "n_gpus": 1, "dtype": "bf16",
@@ -585,6 +661,32 @@ def rank_bench(args):
 # which the pages name without giving its shape.  One call = one decode step
 # of one layer for every beam of every request.
 # ---------------------------------------------------------------------------
+def beam_cpu_baseline(ctx, R, W, Hq, Hkv, d, min_seconds=10.0):
+    """The fp64 oracle on decode step 2 for one request of 16 beams at a
+    time (a bounded sample), scaled to a whole call of R requests x W beams."""
+    import threadpoolctl
+    from oracle.beam import beam_decode_attention
+    rng = np.random.default_rng(2)
+    w = 16
+    q = rng.normal(0, 1, (1, w, Hq, d))
+    ck, cv = [rng.normal(0, 1, (ctx, Hkv, d))], [rng.normal(0, 1, (ctx, Hkv, d))]
+    bk, bv = rng.normal(0, 1, (1, 3, w, Hkv, d)), rng.normal(0, 1, (1, 3, w, Hkv, d))
+    path = rng.integers(0, w, (1, w, 2))
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        beam_decode_attention(q, ck, cv, bk, bv, path, 2, d ** -0.5)
+        n += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return dict(value=1e6 * dt / n * (R * W) / w, unit="us per decode step (all beams), scaled", cores=int(threads),
+                kind="oracle", sample=f"{n} calls of 1 request x {w} beams at context {ctx}, step 2, fp64 numpy, "
+                                      f"{dt:.1f} s, scaled by {R * W // w}")
+
+
 def beam_bench(args):
     import torch
     from hstu_jagged_silu_fwd_amd import _lib
@@ -629,6 +731,8 @@ def beam_bench(args):
             per[f"step{t}"] = dict(us=us, tflops=flops / us / 1e6, mfma_frac=flops / us / 1e6 / BF16_PEAK_TFLOPS,
                                    gbs=byts / us / 1e3, hbm_frac=byts / us / 1e3 / HBM_PEAK_GBS,
                                    algorithmic_bytes=byts, flops=flops)
+        if not args.no_cpu_baseline and ctx == 1000:
+            res["cpu_baseline"] = beam_cpu_baseline(ctx, R, W, Hq, Hkv, d)
         res[f"ctx{ctx}"] = per
         del q, ck, cvt, bk, bv, out
         torch.cuda.empty_cache()

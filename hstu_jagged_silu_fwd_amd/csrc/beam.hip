@@ -10,11 +10,13 @@
 // head) the W * G query rows form a matrix and the context keys another.
 // Kernel 1 takes one (request, KV head, 256-row query tile, context chunk)
 // per workgroup of eight waves; each wave owns two 16-row query groups.  The
-// chunk's keys are walked in 32-key steps, double-buffered through LDS (the
-// next step's loads are in registers while the current step is multiplied):
-//   S^T [32 keys x 16 queries] = K * Q^T      (MFMA, 2 blocks over d)
-//   online softmax in base 2 (a lane holds 8 consecutive keys of one query;
-//   the row maximum is reduced over the four lanes that share the query)
+// chunk's keys are walked in 64-key steps, double-buffered through LDS (the
+// next step's loads are in registers while the current step is multiplied),
+// each step multiplied as two 32-key halves:
+//   S^T [32 keys x 16 queries] = K * Q^T      (MFMA, 2 blocks over d, per half)
+//   online softmax in base 2 over the step's 64 keys (a lane holds 8
+//   consecutive keys of one query per half; the row maximum is reduced over
+//   the four lanes that share the query, once per step)
 //   O^T [d x 16] = alpha * O^T + V^T * P       (MFMA)
 // K rows feeding S^T block b are read in the order row m -> key 8*(m/4) +
 // 4*b + m%4, so a lane's score accumulators are exactly the keys of its
@@ -37,7 +39,8 @@ namespace {
 constexpr int kBWaves = 8;
 constexpr int kBThreads = 64 * kBWaves;
 constexpr int kTileRows = 32 * kBWaves;      // two 16-row groups per wave
-constexpr int kBStep = 32;                   // keys per step
+constexpr int kBStep = 64;                   // keys per step (two 32-key halves)
+constexpr int kCtxAlign = 32;                // max_ctx granularity: every 16-byte V^T load stays in the row
 constexpr int kCombineRows = 4;              // output rows (waves) per combine workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -204,64 +207,76 @@ __global__ __launch_bounds__(kBThreads) void beam_ctx_kernel(BeamArgs a) {
     if (s + 1 < nsteps) load_step(s + 1);            // in flight during the products
     const unsigned char* st = s_stage + (s & 1) * G::STAGE;
     const int kb = k_lo + kBStep * s;
-    // S^T = K * Q^T
-    Frag<T> kf[NC][2];
+    // S^T = K * Q^T for both 32-key halves of the step
+    f32x4 sc[2][2][2];                                 // [group][half][block]
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const int chunk = (cc * 32 + 8 * gq) / G::CE;
-      read_frag(kf[cc][0], st + krow0 * G::KROW, chunk, 0);
-      read_frag(kf[cc][1], st + (krow0 + 4) * G::KROW, chunk, 0);
-    }
-    f32x4 sc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      sc[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hf = 0; hf < 2; ++hf) {
+      Frag<T> kf[NC][2];
+      const unsigned char* kp = st + (32 * hf + krow0) * G::KROW;
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        sc[i][0] = mma16(kf[cc][0], qf[i][cc], sc[i][0]);
-        sc[i][1] = mma16(kf[cc][1], qf[i][cc], sc[i][1]);
+        const int chunk = (cc * 32 + 8 * gq) / G::CE;
+        read_frag(kf[cc][0], kp, chunk, 0);
+        read_frag(kf[cc][1], kp + 4 * G::KROW, chunk, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        sc[i][hf][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc[i][hf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          sc[i][hf][0] = mma16(kf[cc][0], qf[i][cc], sc[i][hf][0]);
+          sc[i][hf][1] = mma16(kf[cc][1], qf[i][cc], sc[i][hf][1]);
+        }
       }
     }
-    Frag<T> vf[NO];
-    {
-      const unsigned char* vp = st + G::KBYTES + l16 * G::VROW;
-      const int vchunk = (8 * gq) / G::CE;
-#pragma unroll
-      for (int ob = 0; ob < NO; ++ob) read_frag(vf[ob], vp + ob * 16 * G::VROW, vchunk, 0);
-    }
-    // online softmax over the step's keys kb + 8*gq + e
+    // online softmax over the step's 64 keys (half hf, element e: key
+    // kb + 32*hf + 8*gq + e); one maximum and one rescale per step
     const int nvalid = k_hi - (kb + 8 * gq);
-    Frag<T> pf[2];
+    Frag<T> pf[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      float p[8];
+      float p[2][8];
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = e < nvalid ? sc[i][e >> 2][e & 3] * a.scale2 : -INFINITY;
-        mx = fmaxf(mx, p[e]);
-      }
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[hf][e] = 32 * hf + e < nvalid ? sc[i][hf][e >> 2][e & 3] * a.scale2 : -INFINITY;
+          mx = fmaxf(mx, p[hf][e]);
+        }
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float mnew = fmaxf(m[i], mx);              // finite: every step has a valid key
       const float alpha = __builtin_amdgcn_exp2f(m[i] - mnew);
       float ps = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(p[e] - mnew);
-        ps += p[e];
-      }
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[hf][e] = __builtin_amdgcn_exp2f(p[hf][e] - mnew);
+          ps += p[hf][e];
+        }
       l[i] = l[i] * alpha + ps;
       m[i] = mnew;
 #pragma unroll
       for (int ob = 0; ob < NO; ++ob) o[i][ob] *= alpha;
-      set_frag(pf[i], p);
+      set_frag(pf[i][0], p[0]);
+      set_frag(pf[i][1], p[1]);
     }
+    // O^T += V^T * P, half by half
 #pragma unroll
-    for (int ob = 0; ob < NO; ++ob)
+    for (int hf = 0; hf < 2; ++hf) {
+      Frag<T> vf[NO];
+      const unsigned char* vp = st + G::KBYTES + l16 * G::VROW;
+      const int vchunk = (32 * hf + 8 * gq) / G::CE;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) o[i][ob] = mma16(vf[ob], pf[i], o[i][ob]);
+      for (int ob = 0; ob < NO; ++ob) read_frag(vf[ob], vp + ob * 16 * G::VROW, vchunk, 0);
+#pragma unroll
+      for (int ob = 0; ob < NO; ++ob)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o[i][ob] = mma16(vf[ob], pf[i][hf], o[i][ob]);
+    }
     if (s + 1 < nsteps) store_step((s + 1) & 1);     // the buffer step s-1 used: free since the last barrier
     __syncthreads();
   }
@@ -364,7 +379,7 @@ BeamLayout beam_layout(const hstu_beam_desc& d) {
   L.NR = d.beam_width * L.G;
   L.nqt = (L.NR + kTileRows - 1) / kTileRows;
   const int64_t tiles = static_cast<int64_t>(d.num_requests) * d.num_kv_heads * L.nqt;
-  const int max_chunks = d.max_ctx / kBStep;
+  const int max_chunks = (d.max_ctx + kBStep - 1) / kBStep;
   int64_t want = tiles > 0 ? (device_cus() + tiles - 1) / tiles : 1;
   want = want < 1 ? 1 : (want > max_chunks ? max_chunks : want);
   L.csz = static_cast<int>((d.max_ctx + want - 1) / want + kBStep - 1) / kBStep * kBStep;
@@ -385,7 +400,7 @@ hstu_status check_beam(const hstu_beam_desc* d) {
   if (d->head_dim != 64 && d->head_dim != 128) return HSTU_ERR_UNSUPPORTED;
   if (d->num_requests < 0 || d->beam_width < 1 || d->beam_width > 1024 || d->num_kv_heads < 1 ||
       d->num_q_heads < d->num_kv_heads || d->num_q_heads % d->num_kv_heads != 0 || d->num_q_heads > 256 ||
-      d->max_ctx < kBStep || d->max_ctx % kBStep != 0 || d->max_ctx > (1 << 20) || d->step < 0 ||
+      d->max_ctx < kCtxAlign || d->max_ctx % kCtxAlign != 0 || d->max_ctx > (1 << 20) || d->step < 0 ||
       d->max_steps <= d->step || !(d->scale > 0.0f))
     return HSTU_ERR_INVALID_ARG;
   return HSTU_OK;

@@ -84,3 +84,25 @@ def test_bad_page_in_last_layer_stops_the_stack():
     assert _lib.read_device_status(ws) == 4
     for y in ys:
         assert torch.all(y == 3.0)
+
+
+def test_stack_equals_layers_with_timestamps():
+    """The serving workload's timestamp bias term through the stack call."""
+    print("case stack bf16 timestamps", flush=True)
+    from workloads import B64_SERVING
+    wl = make_workload(B64_SERVING, seed=6, B=6, hist=("zipf", 1.2, 32, 3000), new=("uniform", 1, 512), layers=2,
+                       pool_pages=4096, miss_frac=0.34)
+    assert wl.timestamps is not None
+    st = stack_from_workload(wl)
+    x, off, hl = inputs(wl, st)
+    ts = torch.from_numpy(wl.ts_flat()).to(st.device)
+    tso = torch.from_numpy(wl.ts_offsets()).to(st.device)
+    ys = st.forward(x, off, hl, timestamps=ts, ts_offsets=tso, return_all=True)
+    assert st.read_status() == 0
+    xin = x
+    for l in range(2):
+        y = torch.empty_like(x)
+        st.layer(l, xin, off, hl, y, timestamps=ts, ts_offsets=tso)
+        assert st.read_status() == 0
+        assert torch.equal(ys[l], y), f"layer {l} differs"
+        xin = y

@@ -102,3 +102,25 @@ def test_device_errors_leave_output_untouched():
     assert code == 10 and torch.all(out == 5.0)
     out, code = run(c, path, 1, "f32", 0.125)
     assert code == 0 and not torch.all(out == 5.0)
+
+
+def test_beam_decode_at_the_online_size_sampled_beams():
+    """Context 5,000, beam 256, 16/8 heads of 128, bf16, step 2: every beam
+    computed on the GPU, 6 sampled beams per request against the oracle (the
+    oracle needs only their queries and paths; the BeamKV holds all slots)."""
+    print("case beam full size sampled", flush=True)
+    R, W, Hq, Hkv, d, Cmax, t = 2, 256, 16, 8, 128, 5024, 2
+    c = make(14, R, W, Hq, Hkv, d, [5000, 4321], Cmax, t + 1, "bf16")
+    path = c["rng"].integers(0, W, size=(R, W, t)).astype(np.int32)
+    out, code = run(c, path, t, "bf16", d ** -0.5)
+    assert code == 0
+    got = out.float().cpu().numpy()
+    sel = np.sort(c["rng"].choice(W, size=6, replace=False))
+    # the sampled beams' own tokens (step t) move to slots 0..5 of the oracle's
+    # copy; earlier steps keep every slot for the paths to index
+    bk, bv = c["bk"].copy(), c["bv"].copy()
+    bk[:, t, :len(sel)] = c["bk"][:, t, sel]
+    bv[:, t, :len(sel)] = c["bv"][:, t, sel]
+    sub = dict(c, q=c["q"][:, sel], bk=bk, bv=bv)
+    ref = oracle(sub, path[:, sel], t, d ** -0.5)
+    tol_check(got[:, sel], ref, "bf16", "beam full size sampled")

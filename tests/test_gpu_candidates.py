@@ -270,3 +270,22 @@ def test_serving_with_candidates_equals_recompute(dtype, seed):
     kinds = _serving_with_candidates(dtype, seed, 14)
     print(f"  {kinds}", flush=True)
     assert kinds["hit"] > 0 and kinds["miss"] > 0
+
+
+def test_candidates_at_the_pages_request_size_sampled():
+    """The pages' request shape (8 users, 8,198 cached tokens, 100 candidates
+    each, hidden 512, bf16): one layer on the GPU, sampled candidate rows of
+    every user against the oracle computed for those rows only."""
+    print("case candidates full size sampled", flush=True)
+    wl = make_workload(B8_KV_HIT, seed=9, B=8, hist=("const", 8198), new=("const", 100), layers=1,
+                       pool_pages=4096, max_pages=260)
+    st = stack_from_workload(wl)
+    m = np.full(8, 100, np.int32)
+    y, code = _run(wl, st, m)
+    assert code == 0, f"device status {code}"
+    rng = np.random.default_rng(3)
+    rows = sorted(int(u * 100 + k) for u in range(8) for k in rng.choice(100, size=3, replace=False))
+    li = wl.layer(0)
+    ref = olayer.layer_forward(wl.x0, wl.new_len, wl.hist_len, li.hist_k, li.hist_v, li.w1, li.w2, li.pos_bias,
+                               wl.pos_mbits, wl.attn_scale, EPS, wl.H, rows=rows, num_candidates=m)["y"]
+    tol_check(to_np(y)[rows], ref, "bf16", "candidates full size sampled")

@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--instances", type=int, default=6)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="time another configuration of the workload table through the same path (one instance; "
+                         "the JSON line then carries no CPU baseline)")
     ap.add_argument("--no-events", action="store_true", help="skip the per-kernel event pass (no roofline or stage split)")
     ap.add_argument("--kvcache", action="store_true",
                     help="measure the KV cache manager (plan on the host, page tables on the device) "
@@ -146,23 +149,28 @@ class Bench:
         import torch
         import hstu_jagged_silu_fwd_amd as hs
         from hstu_jagged_silu_fwd_amd import _lib
-        from workloads import make_workload
+        from workloads import CONFIGS, make_workload
 
         self.torch, self.hs, self._lib = torch, hs, _lib
         self.lib = hs.load()
         self.hip = _lib.hip_runtime()
-        self.R = args.instances
-        B = 8
-        self.wl = wl = make_workload(WORKLOAD, seed=args.seed, B=B * self.R)
+        name = args.workload
+        self.R = args.instances if name == WORKLOAD else 1
+        B = CONFIGS[name]["B"]
+        self.B = B
+        self.wl = wl = make_workload(name, seed=args.seed, B=B * self.R)
         self.L, self.D, self.H, self.d = wl.layers, wl.D, wl.H, wl.d
         dev = torch.device("cuda")
-        bf = torch.bfloat16
+        bf = torch.bfloat16 if wl.dtype == "bf16" else torch.float32      # the workload's element type
+        has_ts = wl.ts_buckets > 0
+        assert not has_ts or self.R == 1, "timestamps: one instance"
         self.k_pool = torch.empty((wl.num_pool_pages, wl.H, wl.page_size, wl.d), dtype=bf, device=dev)
         self.v_pool = torch.empty((wl.num_pool_pages, wl.H, wl.d, wl.page_size), dtype=bf, device=dev)
         common = dict(num_heads=wl.H, head_dim=wl.d, page_size=wl.page_size,
                       max_pages_per_user=wl.max_pages, num_pool_pages=wl.num_pool_pages,
                       pos_buckets=wl.pos_buckets, pos_mbits=wl.pos_mbits,
-                      attn_scale=wl.attn_scale, norm_eps=EPS, dtype="bf16")
+                      attn_scale=wl.attn_scale, norm_eps=EPS, dtype=wl.dtype,
+                      ts_buckets=wl.ts_buckets, ts_mbits=wl.ts_mbits)
         self.common = common
         status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.layers = []
@@ -171,6 +179,7 @@ class Bench:
             li = wl.layer(l)
             lay = dict(w1t=torch.from_numpy(li.w1t).to(dev, bf), w2t=torch.from_numpy(li.w2t).to(dev, bf),
                        pos_bias=torch.from_numpy(li.pos_bias).to(dev),
+                       ts_bias=torch.from_numpy(li.ts_bias).to(dev) if has_ts else None,
                        pt_all=torch.from_numpy(li.page_table).to(dev))
             # history of all users of all instances, positions 0..hist-1
             k = torch.from_numpy(np.concatenate(li.hist_k)).to(dev, bf)
@@ -198,6 +207,8 @@ class Bench:
                       x=torch.from_numpy(wl.x0[rows]).to(dev, bf),
                       ys=[torch.empty((T, self.D), dtype=bf, device=dev) for _ in range(self.L)],
                       pts=[lay["pt_all"][B * i:B * (i + 1)].contiguous() for lay in self.layers],
+                      ts=torch.from_numpy(wl.ts_flat()).to(dev) if has_ts else None,
+                      tso=torch.from_numpy(wl.ts_offsets()).to(dev) if has_ts else None,
                       desc=hs.make_desc(num_users=B, total_new=T, **common))
             ws_bytes = max(ws_bytes, hs.workspace_size(io["desc"]), _lib.stack_workspace_size(io["desc"], self.L))
             self.inst.append(io)
@@ -213,7 +224,10 @@ class Bench:
                              P(io["hist_t"].data_ptr()), P(io["pts"][l].data_ptr()),
                              P(self.k_pool.data_ptr()), P(self.v_pool.data_ptr()),
                              P(lay["w1t"].data_ptr()), P(lay["w2t"].data_ptr()),
-                             P(lay["pos_bias"].data_ptr()), None, None, None,
+                             P(lay["pos_bias"].data_ptr()),
+                             P(lay["ts_bias"].data_ptr()) if has_ts else None,
+                             P(io["ts"].data_ptr()) if has_ts else None,
+                             P(io["tso"].data_ptr()) if has_ts else None,
                              P(io["ys"][l].data_ptr()), P(self.ws.data_ptr()),
                              ctypes.c_size_t(ws_bytes), P(self.stream)))
             io["args"] = args
@@ -221,11 +235,14 @@ class Bench:
             arr = lambda ts: (P * self.L)(*[P(t.data_ptr()) for t in ts])
             io["keep"] = [arr(io["pts"]), arr([self.k_pool] * self.L), arr([self.v_pool] * self.L),
                           arr([lay["w1t"] for lay in self.layers]), arr([lay["w2t"] for lay in self.layers]),
-                          arr([lay["pos_bias"] for lay in self.layers]), arr(io["ys"])]
+                          arr([lay["pos_bias"] for lay in self.layers]), arr(io["ys"]),
+                          arr([lay["ts_bias"] for lay in self.layers]) if has_ts else None]
             k = io["keep"]
             io["stack_args"] = (ctypes.byref(io["desc"]), self.L, P(io["x"].data_ptr()), P(io["off"].data_ptr()),
-                                P(io["hist_t"].data_ptr()), None, k[0], k[1], k[2], k[3], k[4], k[5], None, None,
-                                None, k[6], P(self.ws.data_ptr()), ctypes.c_size_t(ws_bytes), P(self.stream))
+                                P(io["hist_t"].data_ptr()), None, k[0], k[1], k[2], k[3], k[4], k[5], k[7],
+                                P(io["ts"].data_ptr()) if has_ts else None,
+                                P(io["tso"].data_ptr()) if has_ts else None,
+                                k[6], P(self.ws.data_ptr()), ctypes.c_size_t(ws_bytes), P(self.stream))
         torch.cuda.synchronize()
 
     def step(self, s, events=None):
@@ -267,13 +284,14 @@ class Bench:
     def attn_work(self, io):
         """Algorithmic bytes and FLOPs of one attention launch on instance io."""
         D = self.D
+        es = 2 if self.wl.dtype == "bf16" else 4
         kv = 0
         flops = 0
         for c, n in zip(io["hist"].tolist(), io["new_len"].tolist()):
-            kv += (c + n) * 4 * D                 # K and V rows (bf16) read once
+            kv += (c + n) * 2 * D * es            # K and V rows read once
             flops += 4 * D * (n * c + n * (n + 1) // 2)
         T = io["T"]
-        return kv + T * D * 2 + T * D * 4, flops, kv
+        return kv + T * D * es + T * D * 4, flops, kv
 
 
 def cpu_baseline(wl, B, R, min_seconds=10.0):
@@ -793,12 +811,16 @@ def main():
         torch.cuda.synchronize()
     tokens = sum(b.inst[s % b.R]["T"] for s in range(args.steps))
     value = tokens / wall
-    out = dict(metric=METRIC, value=value, unit="new tokens/s", n_gpus=1, steps=args.steps,
+    from workloads import CONFIGS
+    spec = CONFIGS[b.wl.name]
+    out = dict(metric=METRIC if b.wl.name == WORKLOAD else f"HSTU stack new-tokens/sec ({b.wl.name})",
+               value=value, unit="new tokens/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=1e3 * wall / args.steps, higher_is_better=True,
-               scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-               config=dict(workload=b.wl.name, layers=b.L, batch=8, hidden=b.D, heads=b.H,
+               scaling="weak", vs_baseline=None, dtype=b.wl.dtype, data="synthetic",
+               config=dict(workload=b.wl.name, layers=b.L, batch=b.B, hidden=b.D, heads=b.H,
                            head_dim=b.d, page_size=b.wl.page_size, pool_pages=b.wl.num_pool_pages,
-                           hist="U{256..4096}", new="U{16..256}", instances=b.R,
+                           hist=str(spec["hist"]), new=str(spec["new"]), instances=b.R,
+                           timestamps=b.wl.ts_buckets > 0,
                            new_tokens_per_step=tokens / args.steps,
                            per_layer_new_tokens_per_s=value * b.L))
     if events is not None:
@@ -819,7 +841,8 @@ def main():
         achieved = attn_bytes / attn_s / 1e9
         out["roofline"] = dict(kernel="paged_silu_attn", bound="hbm", achieved=achieved,
                                peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                               traffic=load_traffic(), mean_us=1e6 * attn_s / n_launch,
+                               traffic=load_traffic() if b.wl.name == WORKLOAD else None,
+                               mean_us=1e6 * attn_s / n_launch,
                                timing="hipExtLaunchKernel start/stop events per launch, second pass of the same steps",
                                bytes_per_launch=attn_bytes / n_launch,
                                mfma_tflops=attn_flops / attn_s / 1e12,
@@ -828,8 +851,8 @@ def main():
         out["stages_note"] = ("per layer, from the layer-by-layer event pass, where prep runs in every layer; "
                               "the timed stack call runs it once per step")
         out["kernel_sum_ms_per_step"] = float(stage_ms.sum() / args.steps)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(b.wl, 8, b.R)
+    if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
+        out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
     print(json.dumps(out), flush=True)
 
 

@@ -17,7 +17,8 @@
 // `budget` units per item an entry's chunks are at most
 // clamp(budget / w, kMinSteps, kCapSteps) steps long, and the budget is the
 // smallest one found that keeps the item count within the number of resident
-// attention workgroups.  Each entry's keys are then cut into near-equal
+// attention workgroups (plus the number of entries, when those alone exceed
+// it).  Each entry's keys are then cut into near-equal
 // chunks (multiples of 32 keys).
 #include "common.h"
 
@@ -320,10 +321,18 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
     //    while no chunk sits at its cap, fewer than steps_e * w_e /
     //    (budget - w_max) + 1, so the smallest fitting budget lies in
     //    [S / target, S / (target - H * nqb) + w_max]
+    //    When the entries alone already number more than the workgroups
+    //    (H * nqb >= target), the item target becomes target + H * nqb: the
+    //    heavy entries are still cut, and the attention's dynamic fetch
+    //    spreads the items (without this, one workgroup would carry a whole
+    //    long causal q-block while the others idle).  Either way the chosen
+    //    budget keeps the item count at most that target, and target + H *
+    //    nqb is within the workspace's item capacity.
     const int64_t slack = static_cast<int64_t>(H) * nqb;
-    if (err == 0 && target > slack) {
-      b_lo = min<int64_t>(kBudgetHi, max<int64_t>(kBudgetLo, ceil_div(hs, target)));
-      b_hi = min<int64_t>(kBudgetHi, max(b_lo, ceil_div(hs, target - slack) + kMaxWeight));
+    const int64_t tgt = target > slack ? target : target + slack;
+    if (err == 0) {
+      b_lo = min<int64_t>(kBudgetHi, max<int64_t>(kBudgetLo, ceil_div(hs, tgt)));
+      b_hi = min<int64_t>(kBudgetHi, max(b_lo, ceil_div(hs, tgt - slack) + kMaxWeight));
     }
     if (lane == 0) {
       s.b_lo = static_cast<int32_t>(b_lo);
@@ -370,7 +379,8 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
     if (lane < kCand) {
       int64_t c = 0;
       for (int i = 0; i < kPrepWaves; ++i) c += s.cnt[i][lane];
-      if (c * H <= target) j = lane;
+      if (c * H <= (target > static_cast<int64_t>(H) * nqb ? target : target + static_cast<int64_t>(H) * nqb))
+        j = lane;
     }
     const uint64_t fits = __ballot(j == lane && lane < kCand);
     const int jj = fits ? __builtin_ctzll(fits) : kCand - 1;

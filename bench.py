@@ -294,6 +294,20 @@ class Bench:
         return kv + T * D * es + T * D * 4, flops, kv
 
 
+def host_info():
+    """The CPU model and the logical CPUs the host reports."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(wl, B, R, min_seconds=10.0):
     """The fp64 oracle (as it stands) on whole batches of the same workload,
     batch after batch, until at least `min_seconds` of CPU work are done."""
@@ -319,7 +333,7 @@ def cpu_baseline(wl, B, R, min_seconds=10.0):
     dt = time.perf_counter() - t0
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    return dict(value=rows / dt, unit="new tokens/s", cores=int(threads), kind="oracle",
+    return dict(value=rows / dt, unit="new tokens/s", cores=int(threads), kind="oracle", host=host_info(),
                 sample=f"{batches} batches of the same workload ({B} users each, {rows} new rows in total, "
                        f"all {wl.layers} layers, every key), fp64 numpy, {dt:.1f} s")
 
@@ -827,16 +841,23 @@ def main():
         stage_ms = np.zeros(b._lib.NUM_STAGES)
         attn_bytes = attn_flops = 0
         n_launch = 0
+        attn_each, step_each = [], []
         for s in range(args.steps):
             io = b.inst[s % b.R]
             by, fl, _ = b.attn_work(io)
+            step_sum = 0.0
             for l in range(b.L):
                 ev = events[s][l]
                 for k in range(b._lib.NUM_STAGES):
-                    stage_ms[k] += b.elapsed_ms(ev[2 * k], ev[2 * k + 1])
+                    ms = b.elapsed_ms(ev[2 * k], ev[2 * k + 1])
+                    stage_ms[k] += ms
+                    step_sum += ms
+                    if k == 2:
+                        attn_each.append(1e3 * ms)
                 attn_bytes += by
                 attn_flops += fl
                 n_launch += 1
+            step_each.append(1e3 * step_sum)
         attn_s = stage_ms[2] / 1e3
         achieved = attn_bytes / attn_s / 1e9
         out["roofline"] = dict(kernel="paged_silu_attn", bound="hbm", achieved=achieved,
@@ -851,6 +872,10 @@ def main():
         out["stages_note"] = ("per layer, from the layer-by-layer event pass, where prep runs in every layer; "
                               "the timed stack call runs it once per step")
         out["kernel_sum_ms_per_step"] = float(stage_ms.sum() / args.steps)
+        pct = lambda v: [float(np.percentile(v, q)) for q in (10, 50, 90)]
+        out["percentiles_us"] = {"attn_launch_p10_p50_p90": pct(attn_each),
+                                 "step_kernels_p10_p50_p90": pct(step_each),
+                                 "note": "event pass; steps rotate over the instances' different batches"}
     if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
     print(json.dumps(out), flush=True)

@@ -43,6 +43,7 @@
  * Host-checkable errors return a negative hstu_status and enqueue nothing; a
  * ctx_len outside [0, max_ctx] or a path entry outside [0, W) sets the status
  * word (HSTU_DEV_BAD_CTX_LEN, HSTU_DEV_BAD_PATH) and out is left unwritten.
+ * num_requests == 0 enqueues nothing (the status word is not written).
  */
 #ifndef HSTU_BEAM_H_
 #define HSTU_BEAM_H_

@@ -279,14 +279,14 @@ def preprocess(*, hist_len, ctx_offsets, ctx_ids, hist_offsets, item_ids, action
                     ctx_rows=int(ctx_emb.shape[0]), max_positions=int(pos_emb.shape[0]))
     i64 = torch.int64
     rc = load().hstu_preprocess(
-        ctypes.byref(desc), _ptr(hist_len, "hist_len", torch.int32),
+        ctypes.byref(desc), _ptr(hist_len, "hist_len", torch.int32) or None,
         _ptr(ctx_offsets, "ctx_offsets", torch.int32), _ptr(ctx_ids, "ctx_ids", i64),
         _ptr(hist_offsets, "hist_offsets", torch.int32), _ptr(item_ids, "item_ids", i64),
         _ptr(action_ids, "action_ids", i64, allow_none=True),
         _ptr(cand_offsets, "cand_offsets", torch.int32), _ptr(cand_ids, "cand_ids", i64),
         _ptr(item_emb, "item_emb", dt), _ptr(action_emb, "action_emb", dt, allow_none=True),
         _ptr(ctx_emb, "ctx_emb", dt), _ptr(pos_emb, "pos_emb", dt), _ptr(x, "x", dt),
-        _ptr(new_offsets, "new_offsets", torch.int32), _ptr(num_candidates, "num_candidates", torch.int32),
+        _ptr(new_offsets, "new_offsets", torch.int32), _ptr(num_candidates, "num_candidates", torch.int32) or None,
         _ptr(device_status, "device_status", torch.int32), _stream(stream))
     if rc != 0:
         raise HSTUError(rc, "hstu_preprocess")

@@ -192,8 +192,9 @@ extern "C" hstu_status hstu_preprocess(const hstu_prep_desc* d, const int32_t* h
       d->action_rows < 0 || d->max_positions < 1)
     return HSTU_ERR_INVALID_ARG;
   const bool acts = d->action_rows > 0;
-  if (hist_len == nullptr || ctx_offsets == nullptr || hist_offsets == nullptr || cand_offsets == nullptr ||
-      new_offsets == nullptr || num_candidates == nullptr || device_status == nullptr ||
+  const bool users = d->num_users > 0;             // [B] arrays may be NULL for an empty batch
+  if ((users && (hist_len == nullptr || num_candidates == nullptr)) || ctx_offsets == nullptr ||
+      hist_offsets == nullptr || cand_offsets == nullptr || new_offsets == nullptr || device_status == nullptr ||
       item_emb == nullptr || ctx_emb == nullptr || pos_emb == nullptr || (acts && action_emb == nullptr))
     return HSTU_ERR_INVALID_ARG;
   if (d->total_new > 0 && (x == nullptr || ctx_ids == nullptr || item_ids == nullptr || cand_ids == nullptr ||

@@ -240,7 +240,8 @@ typedef struct {
  * new_offsets and num_candidates; then the row builder, which writes nothing
  * after a nonzero status.  A token id outside its table sets
  * HSTU_DEV_BAD_TOKEN while the rows are being built: x is then unspecified.
- * T == 0 with B == 0 is a valid no-op. */
+ * T == 0 with B == 0 is a valid call (new_offsets[0] = 0, status 0); the
+ * [B] arrays may then be NULL. */
 hstu_status hstu_preprocess(const hstu_prep_desc* desc, const int32_t* hist_len,
                             const int32_t* ctx_offsets, const int64_t* ctx_ids,
                             const int32_t* hist_offsets, const int64_t* item_ids,

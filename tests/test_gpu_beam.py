@@ -51,6 +51,8 @@ CASES = [
     ("bf16", 128, 3, 40, 4, 2, [0, 37, 300], 320, 2),
     ("bf16", 64, 2, 130, 2, 1, [513, 64], 544, 1),
     ("bf16", 128, 2, 256, 16, 8, [1000, 517], 1024, 2),
+    ("f32", 64, 1, 1, 2, 2, [40], 64, 3),          # one beam, no grouping, a 4-token path
+    ("bf16", 128, 3, 3, 8, 2, [63, 64, 65], 96, 1),  # lengths around a 64-key step
 ]
 
 

@@ -289,3 +289,20 @@ def test_candidates_at_the_pages_request_size_sampled():
     ref = olayer.layer_forward(wl.x0, wl.new_len, wl.hist_len, li.hist_k, li.hist_v, li.w1, li.w2, li.pos_bias,
                                wl.pos_mbits, wl.attn_scale, EPS, wl.H, rows=rows, num_candidates=m)["y"]
     tol_check(to_np(y)[rows], ref, "bf16", "candidates full size sampled")
+
+
+def test_preprocess_empty_batch_and_empty_user():
+    print("case preprocess empty", flush=True)
+    rng = np.random.default_rng(33)
+    tab = _tables(rng, 64, "f32", max_pos=300)
+    empty = dict(hist_len=[], ctx=[], items=[], actions=[], cands=[])
+    out = _dev_prep(empty, tab, "f32", True)
+    assert int(out["device_status"].item()) == 0 and out["new_offsets"].cpu().tolist() == [0]
+    b = dict(hist_len=[3, 7, 0], ctx=[[1], [], [2, 3]], items=[[4, 5], [], [6]], actions=[[0, 1], [], [2]],
+             cands=[[7], [], []])
+    out = _dev_prep(b, tab, "f32", True)
+    assert int(out["device_status"].item()) == 0
+    x, new_len, ncand = oprep.preprocess(b["hist_len"], b["ctx"], b["items"], b["actions"], b["cands"],
+                                         tab["item_emb"], tab["action_emb"], tab["ctx_emb"], tab["pos_emb"])
+    assert np.array_equal(to_np(out["x"]), x.astype(np.float32).astype(np.float64))
+    assert out["new_offsets"].cpu().tolist() == [0, 6, 6, 10] and out["num_candidates"].cpu().tolist() == [1, 0, 0]

@@ -358,11 +358,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
           // every distance here falls into one or two adjacent buckets
           const int blo = bucket32(dmin, a.mbits, a.nb), bhi = bucket32(dmax, a.mbits, a.nb);
           const float vlo = s_pb[blo], vhi = s_pb[bhi];
-          const int bnd = blo == bhi ? 0x7fffffff : bucket_start(bhi, a.mbits);
+          if (blo == bhi) {                          // uniform: the whole step in one bucket
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < 2; ++b) st[i][b] = f32x4{vlo, vlo, vlo, vlo};
+          } else {
+            const int bnd = bucket_start(bhi, a.mbits);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[i][b][r] = (dl0[i] - 4 * b - r) >= bnd ? vhi : vlo;
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) st[i][b][r] = (dl0[i] - 4 * b - r) >= bnd ? vhi : vlo;
+          }
         } else {
 #pragma unroll
           for (int b = 0; b < 2; ++b)

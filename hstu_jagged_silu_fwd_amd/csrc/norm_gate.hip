@@ -6,9 +6,9 @@
 // Q buffer, which is dead after the attention.
 //
 // A workgroup takes 256 / TPR consecutive rows of one q-block entry (grid:
-// entry x row block), TPR threads per row (a whole wave for D = 256 or 512,
-// whose extra workgroups measured faster than 32; else 32 when D allows, 16
-// otherwise);
+// entry x row block), TPR threads per row (a whole wave for D = 256 or 512
+// and fewer than 4096 rows, whose extra workgroups measured faster than 32
+// there and slower on large batches; else 32 when D allows, 16 otherwise);
 // the row statistics are TPR-lane reductions.  The entry's table entries come in one round trip and the
 // partial sums and U in a second; the loads carry no data-dependent branches
 // (columns beyond D load a valid column and are zeroed by a select) so each
@@ -183,7 +183,9 @@ hipError_t norm_t(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipSt
 template <typename T>
 hipError_t norm_dt(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,
                    const KernelEvents& ev) {
-  if (d.hidden % 256 == 0 && d.hidden <= 512)    // a wave per row, 4 rows per workgroup
+  // a wave per row (4 rows per workgroup) for small batches, whose 32-thread
+  // grid would leave compute units idle; large batches keep 32 per row
+  if (d.hidden % 256 == 0 && d.hidden <= 512 && d.total_new < 4096)
     return norm_t<T, 64, 2>(d, ws, nqb_cap, stream, ev);
   if (d.hidden % 128 == 0) {                     // 32 threads per row, 8 rows per workgroup
     const int ng = d.hidden / 128;

@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_layer_fwd_timed.restype = I32
     lib.hstu_layer_fwd_cand.argtypes = [dp, P, P, P, P] + layer_args[4:] + [P]
     lib.hstu_layer_fwd_cand.restype = I32
+    lib.hstu_layer_fwd_noalloc.argtypes = [dp] + [P] * 15
+    lib.hstu_layer_fwd_noalloc.restype = I32
     lib.hstu_stack_workspace_size.argtypes = [dp, I32, ctypes.POINTER(SZ)]
     lib.hstu_stack_workspace_size.restype = I32
     lib.hstu_stack_fwd.argtypes = [dp, I32] + [P] * 15 + [SZ, P]
@@ -225,6 +227,33 @@ def layer_fwd(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_p
         rc = lib.hstu_layer_fwd(*args)
     if rc != 0:
         raise HSTUError(rc, "hstu_layer_fwd")
+
+
+# bytes of the library's static scratch array (HSTU_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def layer_fwd_noalloc(desc: LayerDesc, x, new_offsets, hist_len, page_table, k_pool, v_pool,
+                      w1t, w2t, pos_bias, y, device_status, ts_bias=None, timestamps=None,
+                      ts_offsets=None, stream=None) -> None:
+    """Enqueue hstu_layer_fwd_noalloc (include/hstu.h): hstu_layer_fwd with the
+    library's static scratch array as its workspace; `device_status` (int32
+    device tensor) receives the call's device code."""
+    import torch
+    dt = _tdtype(desc)
+    none_rows = desc.total_new == 0
+    rc = load().hstu_layer_fwd_noalloc(
+        ctypes.byref(desc), _ptr(x, "x", dt, allow_none=none_rows),
+        _ptr(new_offsets, "new_offsets", torch.int32), _ptr(hist_len, "hist_len", torch.int32),
+        _ptr(page_table, "page_table", torch.int32), _ptr(k_pool, "k_pool", dt), _ptr(v_pool, "v_pool", dt),
+        _ptr(w1t, "w1t", dt), _ptr(w2t, "w2t", dt), _ptr(pos_bias, "pos_bias", torch.float32),
+        _ptr(ts_bias, "ts_bias", torch.float32, allow_none=True),
+        _ptr(timestamps, "timestamps", torch.int64, allow_none=True),
+        _ptr(ts_offsets, "ts_offsets", torch.int32, allow_none=True),
+        _ptr(y, "y", dt, allow_none=none_rows), _ptr(device_status, "device_status", torch.int32),
+        _stream(stream))
+    if rc != 0:
+        raise HSTUError(rc, "hstu_layer_fwd_noalloc")
 
 
 def stack_workspace_size(desc: LayerDesc, num_layers: int) -> int:

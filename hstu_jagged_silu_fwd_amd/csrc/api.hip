@@ -3,10 +3,20 @@
 // attention -> norm * U -> G W2).
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
 using namespace hstu;
+
+// ---------------------------------------------------------------------------
+// Workspace of hstu_layer_fwd_noalloc: a file-scope device array.  Each GPU
+// holds its own copy at its own address; host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol) but
+// the address hipGetSymbolAddress returns on that device, looked up once per
+// device with the device current and kept in scratch_base_of.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[HSTU_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -207,6 +217,29 @@ hstu_status stack_impl(const hstu_layer_desc* desc, int32_t nl, const void* x, c
   return HSTU_OK;
 }
 
+// The address of `scratch` on the current device (see the top of this file).
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_base_of[kMaxDevices];
+
+hstu_status scratch_base(void** base) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HSTU_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_base_of[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return HSTU_ERR_HIP;
+    scratch_base_of[dev] = p;
+  }
+  *base = scratch_base_of[dev];
+  return HSTU_OK;
+}
+
+// Copies the call's status word (workspace header) to the caller's int.
+__global__ void copy_status_kernel(const WsHeader* hdr, int32_t* out) {
+  if (threadIdx.x == 0) *out = hdr->status;
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,6 +277,26 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x, const int
                            size_t workspace_bytes, void* hip_stream) {
   return layer_impl(desc, x, new_offsets, hist_len, nullptr, page_table, k_pool, v_pool, w1t, w2t, pos_bias,
                     ts_bias, timestamps, ts_offsets, y, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+hstu_status hstu_layer_fwd_noalloc(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
+                                   const int32_t* hist_len, const int32_t* page_table, void* k_pool,
+                                   void* v_pool, const void* w1t, const void* w2t, const float* pos_bias,
+                                   const float* ts_bias, const int64_t* timestamps, const int32_t* ts_offsets,
+                                   void* y, int32_t* device_status, void* hip_stream) {
+  hstu_status s = check_layer(desc);
+  if (s != HSTU_OK) return s;
+  if (device_status == nullptr) return HSTU_ERR_INVALID_ARG;
+  if (make_layout(*desc, attn_grid()).total > HSTU_NOALLOC_SCRATCH_BYTES) return HSTU_ERR_SCRATCH;
+  void* base = nullptr;
+  s = scratch_base(&base);
+  if (s != HSTU_OK) return s;
+  s = layer_impl(desc, x, new_offsets, hist_len, nullptr, page_table, k_pool, v_pool, w1t, w2t, pos_bias,
+                 ts_bias, timestamps, ts_offsets, y, base, HSTU_NOALLOC_SCRATCH_BYTES, hip_stream, nullptr);
+  if (s != HSTU_OK) return s;
+  copy_status_kernel<<<1, 64, 0, static_cast<hipStream_t>(hip_stream)>>>(static_cast<const WsHeader*>(base),
+                                                                        device_status);
+  return hipGetLastError() == hipSuccess ? HSTU_OK : HSTU_ERR_HIP;
 }
 
 hstu_status hstu_layer_fwd_timed(const hstu_layer_desc* desc, const void* x, const int32_t* new_offsets,
@@ -299,6 +352,7 @@ const char* hstu_status_string(int32_t status) {
     case HSTU_ERR_WORKSPACE: return "workspace too small";
     case HSTU_ERR_HIP: return "HIP runtime error";
     case HSTU_ERR_DEVICE: return "device status reports an error";
+    case HSTU_ERR_SCRATCH: return "call needs more workspace than the library's static scratch array";
     case HSTU_DEV_BAD_OFFSETS: return "device: new_offsets not a prefix sum ending at total_new";
     case HSTU_DEV_BAD_HIST: return "device: negative hist_len";
     case HSTU_DEV_CAPACITY: return "device: sequence longer than its page-table row";

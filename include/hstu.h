@@ -40,7 +40,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers unless stated, row-major,
  *     allocated and owned by the caller.  The library never allocates, frees
- *     or caches device memory and keeps no mutable global state.
+ *     or caches device memory and keeps no mutable global state, with one
+ *     exception: the static scratch array of hstu_layer_fwd_noalloc (below).
  *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream)
  *     and runs asynchronously; calls return before the GPU finishes.
  *   - Host-checkable problems (null pointer, inconsistent sizes, unsupported
@@ -71,7 +72,9 @@ typedef enum {
   HSTU_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / dtype not supported */
   HSTU_ERR_WORKSPACE = -3,     /* workspace_bytes smaller than required */
   HSTU_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed */
-  HSTU_ERR_DEVICE = -5         /* device status word holds a nonzero code */
+  HSTU_ERR_DEVICE = -5,        /* device status word holds a nonzero code */
+  HSTU_ERR_SCRATCH = -6        /* hstu_layer_fwd_noalloc: the call needs more than
+                                  HSTU_NOALLOC_SCRATCH_BYTES of workspace */
 } hstu_status;
 
 typedef enum {
@@ -195,6 +198,34 @@ hstu_status hstu_layer_fwd_cand(const hstu_layer_desc* desc, const void* x,
                                 const int64_t* timestamps, const int32_t* ts_offsets, void* y,
                                 void* workspace, size_t workspace_bytes, void* hip_stream,
                                 void* const* stage_events);
+
+/* hstu_layer_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument and no allocation of any kind.  The workspace is
+ * instead a file-scope device array of HSTU_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library; each GPU the library runs on holds its own copy from
+ * the moment the library is loaded until the process ends.  Arguments,
+ * results and errors are those of hstu_layer_fwd, plus:
+ *   device_status  one device int32 (caller-owned) that receives the call's
+ *                  hstu_device_code once its kernels have run (0 = success);
+ *                  the status word inside the scratch array is not exposed
+ *   returns HSTU_ERR_SCRATCH (enqueuing nothing) when
+ *   hstu_layer_workspace_size(desc) exceeds HSTU_NOALLOC_SCRATCH_BYTES: at
+ *   D = 512, H = 4, d = 128 in bf16 that holds batches of 8 users with up to
+ *   about 2,000 new rows and 16,384-token sequences.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (every value the kernels read is written earlier in the same call,
+ * so nothing carries over): calls that overlap in time on one GPU -- on two
+ * streams, or from two host threads without ordering -- race on it and give
+ * undefined results.  Calls ordered on one stream are safe. */
+#define HSTU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hstu_status hstu_layer_fwd_noalloc(const hstu_layer_desc* desc, const void* x,
+                                   const int32_t* new_offsets, const int32_t* hist_len,
+                                   const int32_t* page_table, void* k_pool, void* v_pool,
+                                   const void* w1t, const void* w2t, const float* pos_bias,
+                                   const float* ts_bias, const int64_t* timestamps,
+                                   const int32_t* ts_offsets, void* y, int32_t* device_status,
+                                   void* hip_stream);
 
 /* Input preprocessing: the layer's input rows built from categorical tokens
  * (NVIDIA blog above, section "Why use HSTU for generative recommendation":

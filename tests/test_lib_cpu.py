@@ -21,7 +21,8 @@ def test_exports_every_header_function():
     lib = hs.load()
     names = list(hs.header_functions())
     assert set(names) == {"hstu_layer_workspace_size", "hstu_layer_fwd", "hstu_layer_fwd_timed",
-                          "hstu_layer_fwd_cand", "hstu_stack_workspace_size", "hstu_stack_fwd",
+                          "hstu_layer_fwd_cand", "hstu_layer_fwd_noalloc", "hstu_stack_workspace_size",
+                          "hstu_stack_fwd",
                           "hstu_preprocess", "kv_pages_append", "hstu_read_device_status",
                           "hstu_status_string"}
     for n in names:
@@ -162,3 +163,20 @@ def test_stack_host_checks():
         assert lib.hstu_stack_workspace_size(ctypes.byref(d), nl, ctypes.byref(n)) == -1
     # desc, layers, x, offsets, hist, candidates, 9 per-layer arrays and tensors, y, ws, bytes, stream
     assert lib.hstu_stack_fwd(ctypes.byref(d), 3, *([None] * 15), 0, None) == -1
+
+
+def test_noalloc_host_checks():
+    """hstu_layer_fwd_noalloc: a missing status int or any null pointer is
+    rejected, and a call whose workspace would exceed the static scratch
+    array returns HSTU_ERR_SCRATCH, all before any device work."""
+    lib = hs.load()
+    d = desc()
+    assert hs.workspace_size(d) <= _lib.NOALLOC_SCRATCH_BYTES
+    # desc, 13 pointers (x .. y), device_status, stream
+    assert lib.hstu_layer_fwd_noalloc(ctypes.byref(d), *([None] * 14), None) == -1
+    big = desc(total_new=200000, num_users=4000, max_pages_per_user=1100)
+    assert hs.workspace_size(big) > _lib.NOALLOC_SCRATCH_BYTES
+    status = ctypes.c_int32(0)
+    rc = lib.hstu_layer_fwd_noalloc(ctypes.byref(big), *([None] * 13), ctypes.byref(status), None)
+    assert rc == -6
+    assert "scratch" in hs.status_string(-6)

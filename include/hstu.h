@@ -212,7 +212,8 @@ hstu_status hstu_layer_fwd_cand(const hstu_layer_desc* desc, const void* x,
  *   returns HSTU_ERR_SCRATCH (enqueuing nothing) when
  *   hstu_layer_workspace_size(desc) exceeds HSTU_NOALLOC_SCRATCH_BYTES: at
  *   D = 512, H = 4, d = 128 in bf16 that holds batches of 8 users with up to
- *   about 2,000 new rows and 16,384-token sequences.
+ *   about 4,000 new rows and 4,352-token sequences, or about 1,500 new rows
+ *   and 16,448-token sequences.
  * Every call on one GPU shares that GPU's array, which keeps the last call's
  * contents (every value the kernels read is written earlier in the same call,
  * so nothing carries over): calls that overlap in time on one GPU -- on two

@@ -25,7 +25,7 @@ constexpr int kAttnWgPerCu = 1;     // resident attention workgroups per CU
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-  size_t row_loc, qb_first, qb_nch, qb_row0, qb_rows, items, q, u, part, total;
+  size_t row_loc, qb_first, qb_nch, qb_row0, qb_rows, items, q, u, part, tables, total;
   int nqb_cap, item_cap;
 };
 
@@ -59,6 +59,7 @@ Layout make_layout(const hstu_layer_desc& d, int target, int nl = 1) {
   L.q = off;        off = align256(off + es * T * d.hidden);
   L.u = off;        off = align256(off + es * T * d.hidden);
   L.part = off;     off = align256(off + 4 * static_cast<size_t>(L.item_cap) * kQB * d.head_dim);
+  L.tables = off;   off = align256(off + 4 * static_cast<size_t>(kTabFloats) * nl);
   L.total = off;
   return L;
 }
@@ -76,6 +77,7 @@ WsPtrs ws_ptrs(void* base, const Layout& L) {
   w.q = b + L.q;
   w.u = b + L.u;
   w.part = reinterpret_cast<float*>(b + L.part);
+  w.tables = reinterpret_cast<float*>(b + L.tables);
   return w;
 }
 
@@ -148,14 +150,14 @@ hstu_status layer_impl(const hstu_layer_desc* desc, const void* x, const int32_t
     return k;
   };
   hipError_t e;
-  e = launch_prep(d, new_offsets, hist_len, ncand, &page_table, 1, ts_off, ws, L.nqb_cap, L.item_cap, grid, st,
-                  kev(HSTU_STAGE_PREP));
+  e = launch_prep(d, new_offsets, hist_len, ncand, &page_table, 1, ts_off, &pos_bias, &tsb, ws, L.nqb_cap,
+                  L.item_cap, grid, st, kev(HSTU_STAGE_PREP));
   if (e != hipSuccess) return HSTU_ERR_HIP;
   if (!any_rows) return HSTU_OK;
   e = launch_gemm_qkv(d, x, w1t, k_pool, v_pool, ws, st, kev(HSTU_STAGE_PROJ));
   if (e != hipSuccess) return HSTU_ERR_HIP;
-  e = launch_attn(d, page_table, k_pool, v_pool, pos_bias, tsb, ts, ts_off, ncand, ws,
-                  grid < L.item_cap ? grid : L.item_cap, st, kev(HSTU_STAGE_ATTN));
+  e = launch_attn(d, page_table, k_pool, v_pool, 0, ts, ts_off, ncand, ws, grid < L.item_cap ? grid : L.item_cap,
+                  st, kev(HSTU_STAGE_ATTN));
   if (e != hipSuccess) return HSTU_ERR_HIP;
   e = launch_norm_gate(d, ws, L.nqb_cap, st, kev(HSTU_STAGE_NORM));
   if (e != hipSuccess) return HSTU_ERR_HIP;
@@ -198,7 +200,8 @@ hstu_status stack_impl(const hstu_layer_desc* desc, int32_t nl, const void* x, c
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int32_t* ts_off = has_ts ? ts_offsets : nullptr;
   const int64_t* ts = has_ts ? timestamps : nullptr;
-  hipError_t e = launch_prep(d, new_offsets, hist_len, ncand, pts, nl, ts_off, ws, L.nqb_cap, L.item_cap, grid, st);
+  hipError_t e = launch_prep(d, new_offsets, hist_len, ncand, pts, nl, ts_off, pbs, has_ts ? tsbs : nullptr, ws,
+                             L.nqb_cap, L.item_cap, grid, st);
   if (e != hipSuccess) return HSTU_ERR_HIP;
   if (!any_rows) return HSTU_OK;
   for (int l = 0; l < nl; ++l) {
@@ -206,8 +209,7 @@ hstu_status stack_impl(const hstu_layer_desc* desc, int32_t nl, const void* x, c
     wl.row_loc = ws.row_loc + static_cast<size_t>(l) * d.total_new;   // this layer's pool slots
     e = launch_gemm_qkv(d, l == 0 ? x : ys[l - 1], w1s[l], kps[l], vps[l], wl, st);
     if (e != hipSuccess) return HSTU_ERR_HIP;
-    e = launch_attn(d, pts[l], kps[l], vps[l], pbs[l], has_ts ? tsbs[l] : nullptr, ts, ts_off, ncand, ws,
-                    grid < L.item_cap ? grid : L.item_cap, st);
+    e = launch_attn(d, pts[l], kps[l], vps[l], l, ts, ts_off, ncand, ws, grid < L.item_cap ? grid : L.item_cap, st);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     e = launch_norm_gate(d, ws, L.nqb_cap, st);
     if (e != hipSuccess) return HSTU_ERR_HIP;

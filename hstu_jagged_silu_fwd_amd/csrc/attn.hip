@@ -21,10 +21,12 @@
 // At the end of an item the phases' partial sums meet in LDS.
 // Per step and wave:
 //   S^T[32 keys x 16 queries] = K * Q^T     (2 MFMA blocks over d; the
-//                                           accumulators start at the bias)
-//   A = SiLU(S) on the fp32 scores; masked only on diagonal steps and on
-//                                           steps that reach the candidates
+//                                           accumulators start at the bias,
+//                                           or at a masked value, below)
+//   A = SiLU(S) on the fp32 scores          (no branches)
 //   O^T[d x 16]             += V^T * A
+// A wave with two groups runs one group's products on the matrix cores while
+// the other group's SiLU runs on the vector ALUs.
 // K rows feeding S^T block b are read in the permuted order row m -> key
 // 8*(m/4) + 4*b + m%4, so the S^T accumulator of a lane holds 8 consecutive
 // keys of one query, which is exactly its B-operand fragment for the second
@@ -40,19 +42,26 @@
 // i.e. exp2, add, reciprocal, multiply per score.  The constant -ln(2) is
 // applied with the 1/N scale by the norm kernel.
 //
-// Bias: a per-workgroup LDS table holds the scaled bias of every distance
-// below kLut, in descending order of distance: the 8 scores a lane holds per
-// group and step have 8 consecutive distances, so they read 8 consecutive
-// entries at immediate offsets from one address.  A step whose distances all
-// lie at or beyond kLut and span no more than one bucket width (2^(12-m)
-// there) touches at most two buckets and takes a compare/select between two
-// values; any other step takes the generic per-element bucket path.  Timestamps, when present, travel with
-// their keys through the ring; each lane keeps its query's in a register.
+// Bias: the layer's tables (built once per call by prep, see kTabFloats) are
+// copied into LDS by direct-to-LDS loads at the workgroup's start.  The
+// distance table holds the scaled bias of every distance below kLut, in
+// descending order of distance: the 8 scores a lane holds per group and step
+// have 8 consecutive distances, so they read 8 consecutive entries at
+// immediate offsets from one address.  A step whose distances all lie at or
+// beyond kLut and span no more than one bucket width (2^(12-m) there)
+// touches at most two buckets and takes a compare/select between two values;
+// any other step takes the generic per-element bucket path.  Timestamps
+// (an instance of the kernel of their own), when present, travel with their
+// keys through the ring; each lane keeps its query's in a register.
 //
-// Candidates: when the call gives per-user candidate counts m_u, a query at
-// or past the first candidate position cs = c + n - m_u sees only the keys
-// before cs and itself (a key at or past cs is kept only on the diagonal).
-// Rows before cs see nothing past cs anyway, so one mask covers every row.
+// Masks: a masked (query, key) pair starts its accumulator at kMasked, whose
+// SiLU is exactly 0 (see kMasked).  Negative distances (the causal mask) read
+// masked entries from the bias table's padding, so only steps that reach the
+// candidates set masks of their own.  Candidates: when the call gives
+// per-user candidate counts m_u, a query at or past the first candidate
+// position cs = c + n - m_u sees only the keys before cs and itself (a key at
+// or past cs is kept only on the diagonal).  Rows before cs see nothing past
+// cs anyway, so one mask covers every row.
 //
 // Partial outputs (fp32) go to the workspace; the chunks of a row are added
 // by the norm kernel (no softmax, so partial sums over key ranges simply
@@ -66,11 +75,8 @@
 namespace hstu {
 namespace {
 
-constexpr int kLut = 4096;
-constexpr int kLutPad = 64;        // entries past the table (negative distances: masked scores)
 constexpr int kStepKeys = 32;
 constexpr int kMaxChunkPages = kMaxChunkKeys / 16 + 1;
-constexpr float kNegLog2e = -1.4426950408889634f;
 
 template <typename T>
 struct AttnArgs {
@@ -78,8 +84,7 @@ struct AttnArgs {
   const T* k_pool;
   const T* v_pool;
   const T* q;
-  const float* pos_bias;
-  const float* ts_bias;
+  const float* tab;          // this layer's bias tables (layout at kTabFloats)
   const int64_t* ts;
   const int32_t* ts_off;
   const int32_t* ncand;      // per-user candidate counts, or null
@@ -124,51 +129,50 @@ struct StepGeo {
   static_assert(KCH >= 4 && (VCH == 4 || VCH == 8), "supported geometry");
   static_assert(NBLK * 1024 == STAGE, "whole loads per stage");
   static_assert((kStepKeys * KCH) % 64 == 0, "a load never straddles K and V^T");
-  static_assert((IPW + 1) * (NST - 2) <= 23, "wait count range");
+  static_assert((IPW + 1) * (NST - 2) <= 63, "wait count range");
   // the phase reduction reuses the ring: at most (PMAX-1) * (kWaves/PMAX)
   // waves hand over two 16 x HD fp32 tiles each
   static_assert(NST * STAGE >= (PMAX - 1) * (kWaves / PMAX) * kGpw * 16 * HD * 4, "reduction fits the ring");
 };
 
-template <typename T, int HD, bool CAND>
+template <typename T, int HD, bool CAND, bool TS>
 __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
   using G = StepGeo<T, HD>;
   constexpr int CE = G::CE, KCH = G::KCH, VCH = G::VCH, NST = G::NST, IPW = G::IPW;
   constexpr int NT = 64 * kWaves;
   constexpr int NC = HD / 32;        // 32-wide slices of the head dim (contraction of S^T)
   constexpr int NO = HD / 16;        // 16-row blocks of O^T
-  static_assert(kMaxChunkPages <= 2 * NT, "two page ids per thread");
+  constexpr int kPidPerThread = (kMaxChunkPages + NT - 1) / NT;   // page ids a thread stages
   __shared__ __attribute__((aligned(1024))) unsigned char s_ring[NST * G::STAGE];
   __shared__ __attribute__((aligned(256))) int64_t s_ts[NST][kStepKeys];
-  __shared__ float s_rlut[kLut + kLutPad];   // s_rlut[x]: bias of distance kLut - 1 - x
-  __shared__ float s_pb[kMaxBuckets];
-  __shared__ float s_tb[kMaxBuckets];
+  // bias tables (layout at kTabFloats): s_rlut[x] is the bias of distance
+  // kLut - 1 - x, s_pb / s_tb the position / timestamp buckets
+  __shared__ __attribute__((aligned(1024))) float s_tab[kTabFloats];
+  const float* s_rlut = s_tab;
+  const float* s_pb = s_tab + kTabPb;
+  const float* s_tb = s_tab + kTabTb;
   __shared__ int s_pages[kMaxChunkPages];
   __shared__ int s_next;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
-  // Status words and item count, the first item (static: workgroup i takes item i;
-  // the grid never exceeds the item capacity) and the bias tables (up to two
-  // entries of each per thread) are all loaded at once.  The tables reach LDS
-  // (and the distance table is built) inside the first item's set-up, after
-  // its page-id and query loads have gone out, so those round trips overlap.
-  static_assert(kMaxBuckets <= 2 * NT, "two bias entries per thread");
+  // Status words and item count, the first item (static: workgroup i takes
+  // item i; the grid never exceeds the item capacity) and the layer's bias
+  // tables (direct-to-LDS, 1 KiB per wave instruction) all go out at once;
+  // the tables have landed by the first item's wait for its page ids.
   const int4 hv = *reinterpret_cast<const int4*>(a.hdr);
   AttnItem item = a.items[blockIdx.x];
-  float pbv[2], tbv[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int i = tid + j * NT;
-    pbv[j] = i < a.nb ? a.pos_bias[i] : 0.f;
-    tbv[j] = i < a.ntsb ? a.ts_bias[i] : 0.f;
+  static_assert(kTabFloats % 256 == 0, "whole KiB of tables");
+  for (int j = w; j < kTabFloats / 256; j += kWaves)
+    dma_lds16(a.tab + j * 256 + lane * 4, s_tab + j * 256);
+  if ((hv.x | hv.y) != 0) {                // status words: prep rejected the call
+    wait_vm<0>();                          // (the table loads land before the workgroup ends)
+    return;
   }
-  if ((hv.x | hv.y) != 0) return;          // status words: prep rejected the call
   const int n_items = hv.z;
   const bool dynamic = n_items > static_cast<int>(gridDim.x);
-  bool tables_ready = false;
   const int ps = 1 << a.ps_shift;
-  const bool has_ts = a.ntsb > 0;
+  constexpr bool has_ts = TS;             // the timestamp term (an instance of its own)
   const int g = lane >> 4, l16 = lane & 15;
   // K row read by this lane for S^T block b is krow0 + 4*b; both rows share
   // one chunk permutation.  V^T rows 16*ob + l16 share one too.
@@ -251,8 +255,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // atomics would only queue up behind each other.)
     int nxt = 0;
     if (dynamic && tid == 0) nxt = atomicAdd(&a.hdr->counter, 1);
-    const int pid0 = tid < npg ? ptu[pg0 + tid] : 0;
-    const int pid1 = tid + NT < npg ? ptu[pg0 + tid + NT] : 0;
+    // (clamped indices: no per-lane branch, see the bias tables)
+    int pid[kPidPerThread];
+#pragma unroll
+    for (int k = 0; k < kPidPerThread; ++k) pid[k] = ptu[pg0 + min(tid + k * NT, npg - 1)];
     Frag<T> qf[kGpw][NC];
     int64_t tq[kGpw];
     const int64_t* tsu = has_ts ? a.ts + a.ts_off[u] : nullptr;
@@ -270,21 +276,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // Let these loads land before the ring starts: the compiler cannot count
     // outstanding loads across the key loop, so it would otherwise wait for
     // every in-flight stage at the first use of a query fragment.
-    if (!tables_ready) {                   // first item: bias tables into LDS meanwhile
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int i = tid + j * NT;
-        if (i < a.nb) s_pb[i] = kNegLog2e * pbv[j];
-        if (i < a.ntsb) s_tb[i] = kNegLog2e * tbv[j];
-      }
-      __syncthreads();
-      for (int i = tid; i < kLut + kLutPad; i += NT)
-        s_rlut[i] = i < kLut ? s_pb[bucket32(kLut - 1 - i, a.mbits, a.nb)] : 0.f;
-      tables_ready = true;
-    }
     wait_vm<0>();
-    if (tid < npg) s_pages[tid] = pid0;
-    if (tid + NT < npg) s_pages[tid + NT] = pid1;
+#pragma unroll
+    for (int k = 0; k < kPidPerThread; ++k)
+      if (tid + k * NT < npg) s_pages[tid + k * NT] = pid[k];
     if (tid == 0) s_next = dynamic ? static_cast<int>(gridDim.x) + nxt : n_items;
     __syncthreads();                       // pages staged; s_next published
     // the next item's descriptor, in flight during this item's key loop
@@ -296,8 +291,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     const size_t kv_head = static_cast<size_t>(h) * ps * HD;      // head block inside a page
     const size_t page_elems = static_cast<size_t>(a.H) * ps * HD;
     // Keys past the staged range (last step only) read rows of the step's
-    // own pages: in bounds; their scores are masked and their V^T columns
-    // zeroed in LDS before the products.
+    // own pages: in bounds; their K rows and V^T columns are zeroed in LDS
+    // before the products and their scores masked.
     auto issue = [&](int s) __attribute__((always_inline)) {
       const int kb = k_lo + kStepKeys * s;
       unsigned char* stg = s_ring + (s % NST) * G::STAGE;
@@ -331,132 +326,112 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
 #pragma unroll
       for (int ob = 0; ob < NO; ++ob) o[i][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- products of step s for this wave's first NG query groups ----
-    auto compute = [&](auto ngc, int s) __attribute__((always_inline)) {
-      constexpr int NG = decltype(ngc)::value;
+    // ---- the pieces of a step's products (this wave's groups) ----
+    // Accumulator start of group i at step s: the bias of every (query, key)
+    // pair, or kMasked for masked pairs.
+    auto bias_init = [&](int i, int s, f32x4 (&sv)[2]) __attribute__((always_inline)) {
       const int kb = k_lo + kStepKeys * s;
-      const unsigned char* stg = s_ring + (s % NST) * G::STAGE;
-      f32x4 st[NG][2];
-      int dl0[NG], dmn[NG];
+      // distance of element (block b, row r) is dl0 - 4*b - r
+      const int pq = c + q0 + 16 * (gi0 + i);          // first query position of the group
+      const int dl0 = pq + l16 - (kb + 8 * g);
+      const int dmin = pq - (kb + kStepKeys - 1);
+      const int dmax = pq + 15 - kb;
+      if (dmax < kLut) {
+        // element (b, r) has distance dl0 - (4b + r), entry x0 + 4b + r; a
+        // lane whose distances are all negative reads padding (masked)
+        const float* lp = s_rlut + min(kLut - 1 - dl0, kLut + kLutPad - 8);
 #pragma unroll
-      for (int i = 0; i < NG; ++i) {
-        // distance of element (block b, row r) is dl0 - 4*b - r
-        const int pq = c + q0 + 16 * (gi0 + i);        // first query position of the group
-        dl0[i] = pq + l16 - (kb + 8 * g);
-        const int dmin = pq - (kb + kStepKeys - 1);
-        const int dmax = pq + 15 - kb;
-        dmn[i] = dmin;
-        if (dmax < kLut) {
-          // element (b, r) has distance dl0 - (4b + r), entry x0 + 4b + r; a
-          // lane whose distances are all negative reads padding
-          const float* lp = s_rlut + min(kLut - 1 - dl0[i], kLut + kLutPad - 8);
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int r = 0; r < 4; ++r) sv[b][r] = lp[4 * b + r];
+      } else if (dmin >= kLut && (kLut >> a.mbits) >= dmax - dmin + 1) {
+        // every distance here falls into one or two adjacent buckets
+        const int blo = bucket32(dmin, a.mbits, a.nb), bhi = bucket32(dmax, a.mbits, a.nb);
+        const float vlo = s_pb[blo], vhi = s_pb[bhi];
+        if (blo == bhi) {                            // uniform: the whole step in one bucket
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[i][b][r] = lp[4 * b + r];
-        } else if (dmin >= kLut && (kLut >> a.mbits) >= dmax - dmin + 1) {
-          // every distance here falls into one or two adjacent buckets
-          const int blo = bucket32(dmin, a.mbits, a.nb), bhi = bucket32(dmax, a.mbits, a.nb);
-          const float vlo = s_pb[blo], vhi = s_pb[bhi];
-          if (blo == bhi) {                          // uniform: the whole step in one bucket
-#pragma unroll
-            for (int b = 0; b < 2; ++b) st[i][b] = f32x4{vlo, vlo, vlo, vlo};
-          } else {
-            const int bnd = bucket_start(bhi, a.mbits);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) st[i][b][r] = (dl0[i] - 4 * b - r) >= bnd ? vhi : vlo;
-          }
+          for (int b = 0; b < 2; ++b) sv[b] = f32x4{vlo, vlo, vlo, vlo};
         } else {
+          const int bnd = bucket_start(bhi, a.mbits);
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[i][b][r] = s_pb[bucket32(dl0[i] - 4 * b - r, a.mbits, a.nb)];
+            for (int r = 0; r < 4; ++r) sv[b][r] = (dl0 - 4 * b - r) >= bnd ? vhi : vlo;
         }
-        if (has_ts) {
-          const int64_t* tk = &s_ts[s % NST][8 * g];
+      } else {
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st[i][b][r] += s_tb[bucket64(tq[i] - tk[4 * b + r], a.tsmbits, a.ntsb)];
+          for (int r = 0; r < 4; ++r) sv[b][r] = s_pb[bucket32(dl0 - 4 * b - r, a.mbits, a.nb)];
+      }
+      if (has_ts) {
+        const int64_t* tk = &s_ts[s % NST][8 * g];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sv[b][r] += s_tb[bucket64(tq[i] - tk[4 * b + r], a.tsmbits, a.ntsb)];
+      }
+      // The causal mask is in the bias already (negative distances read the
+      // table's masked padding).  Keys at or past the candidates: element e
+      // (key kb + 8g + e) stays only if it is before cs or on the diagonal.
+      if (CAND && kb + kStepKeys > cs) {
+        const int ce = cs - (kb + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int de = dl0 - e;
+          if (!(de >= 0 && (e < ce || de == 0))) sv[e >> 2][e & 3] = kMasked;
         }
       }
-      // S^T = K * Q^T over the head dim; each K fragment feeds every group.
-      // All of the step's K fragment reads go out before the first product,
-      // so their LDS latency is paid once.
-      const unsigned char* k0p = stg + krow0 * (KCH * 16);
+    };
+    // K fragments of step s (rows read in the permuted order, see the top)
+    auto read_k = [&](int s, Frag<T> (&kf)[NC][2]) __attribute__((always_inline)) {
+      const unsigned char* k0p = s_ring + (s % NST) * G::STAGE + krow0 * (KCH * 16);
       const unsigned char* k1p = k0p + 4 * (KCH * 16);
-      Frag<T> kf[NC][2];
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
         const int chunk = (cc * 32 + 8 * g) / CE;
         read_frag(kf[cc][0], k0p, chunk, ksw);
         read_frag(kf[cc][1], k1p, chunk, ksw);
       }
+    };
+    auto read_v = [&](int s, Frag<T> (&vf)[NO]) __attribute__((always_inline)) {
+      const unsigned char* vp = s_ring + (s % NST) * G::STAGE + G::KBYTES + l16 * (VCH * 16);
+      const int vchunk = (8 * g) / CE;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
+      for (int ob = 0; ob < NO; ++ob) read_frag(vf[ob], vp + ob * 16 * (VCH * 16), vchunk, vsw);
+    };
+    // S^T of group i += K * Q^T over the head dim
+    auto s_mma = [&](int i, const Frag<T> (&kf)[NC][2], f32x4 (&sv)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-          st[i][0] = mma16(kf[cc][0], qf[i][cc], st[i][0]);
-          st[i][1] = mma16(kf[cc][1], qf[i][cc], st[i][1]);
-        }
-      // V^T fragments are read now so that their LDS latency overlaps the
-      // SiLU below.
-      Frag<T> vf[NO];
-      {
-        const unsigned char* vp = stg + G::KBYTES + l16 * (VCH * 16);
-        const int vchunk = (8 * g) / CE;
-#pragma unroll
-        for (int ob = 0; ob < NO; ++ob) read_frag(vf[ob], vp + ob * 16 * (VCH * 16), vchunk, vsw);
+      for (int cc = 0; cc < NC; ++cc) {
+        sv[0] = mma16(kf[cc][0], qf[i][cc], sv[0]);
+        sv[1] = mma16(kf[cc][1], qf[i][cc], sv[1]);
       }
-      // SiLU in independent batches (every exp2, then every reciprocal) so
-      // that no transcendental waits on the one before it
-      float av[NG][8];
+    };
+    // A = SiLU(S) in the exponent domain, no branches: every exp2, then
+    // every reciprocal, so no transcendental waits on the one before it
+    auto silu_frag = [&](const f32x4 (&sv)[2], Frag<T>& af) __attribute__((always_inline)) {
+      float av[8];
 #pragma unroll
-      for (int i = 0; i < NG; ++i)
+      for (int e = 0; e < 8; ++e) av[e] = __builtin_amdgcn_exp2f(sv[e >> 2][e & 3]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) av[i][e] = __builtin_amdgcn_exp2f(st[i][e >> 2][e & 3]);
+      for (int e = 0; e < 8; ++e) av[e] = __builtin_amdgcn_rcpf(1.0f + av[e]);
 #pragma unroll
-      for (int i = 0; i < NG; ++i)
+      for (int e = 0; e < 8; ++e) av[e] *= sv[e >> 2][e & 3];
+      set_frag(af, av);
+    };
+    // O^T of group i += V^T * A
+    auto o_mma = [&](int i, const Frag<T> (&vf)[NO], const Frag<T>& af) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) av[i][e] = __builtin_amdgcn_rcpf(1.0f + av[i][e]);
-      Frag<T> af[NG];
-#pragma unroll
-      for (int i = 0; i < NG; ++i) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[i][e] *= st[i][e >> 2][e & 3];
-        if (CAND && kb + kStepKeys > cs) {           // keys at or past the candidates
-          const int ce = cs - (kb + 8 * g);          // element e's key is past cs when e >= ce
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int de = dl0[i] - e;
-            av[i][e] = (de >= 0 && (e < ce || de == 0)) ? av[i][e] : 0.0f;
-          }
-        } else if (dmn[i] < 0) {                     // causal mask on the diagonal
-#pragma unroll
-          for (int e = 0; e < 8; ++e) av[i][e] = dl0[i] - e >= 0 ? av[i][e] : 0.0f;
-        }
-        set_frag(af[i], av[i]);
-      }
-      // O^T += V^T * A
-#pragma unroll
-      for (int ob = 0; ob < NO; ++ob)
-#pragma unroll
-        for (int i = 0; i < NG; ++i) o[i][ob] = mma16(vf[ob], af[i], o[i][ob]);
+      for (int ob = 0; ob < NO; ++ob) o[i][ob] = mma16(vf[ob], af, o[i][ob]);
     };
 
-    // ---- the key loop: one barrier per round of P steps.  Round r's steps
-    // sit in stages rP .. rP+P-1 (mod NST); the loads of round r+D are
-    // issued once round r-1's stages are free, so D rounds are in flight
-    // while one is multiplied.  (The wave's group count is fixed for the
-    // item, so each count gets a loop of its own.) ----
-    for (int s = 0; s < min(D * P, nsteps); ++s) issue(s);
     // Only the last step can reach past the staged keys.  Those keys lie
-    // beyond every query of the item, so their scores are masked; their V^T
-    // columns are zeroed in LDS (by the lanes that loaded them, once their
-    // loads have landed) so that stale pool memory cannot turn a masked
-    // product into NaN, and the products need no tail case of their own.
+    // beyond every query of the item, so their scores are masked; their K
+    // rows and V^T columns are zeroed in LDS (by the lanes that loaded them,
+    // once their loads have landed) so that stale pool memory cannot turn a
+    // masked score or product into NaN, and the products need no tail case
+    // of their own.
     const int tail_round = k_lo + kStepKeys * nsteps > kst_end ? (nsteps - 1) / P : -1;
     auto zero_tail = [&]() __attribute__((always_inline)) {
       const int kb = k_lo + kStepKeys * (nsteps - 1);
@@ -466,7 +441,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       for (int j = 0; j < IPW; ++j) {
         const int blk = w * IPW + j;
         if (blk >= G::NBLK) break;                     // uniform
-        if (blk * 64 < kStepKeys * KCH) continue;      // K rows: masked by the scores
+        if (blk * 64 < kStepKeys * KCH) {              // K rows: the lane's chunk of key q / KCH
+          if ((blk * 64 + lane) / KCH >= nvalid)
+            *reinterpret_cast<u32x4*>(stg + blk * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+          continue;
+        }
         const int qv = blk * 64 + lane - kStepKeys * KCH;
         const int e = qv / VCH, p = qv % VCH;
         const int key0 = (p ^ ((e >> G::VSH) & (VCH - 1))) * CE;   // first key of this lane's chunk
@@ -477,7 +456,64 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): the zeros are in LDS
     };
+    // loads of the steps of round rr (early waves issue theirs before the
+    // products, the others after, so the two waves of a SIMD take turns)
+    auto issue_round = [&](int rr) __attribute__((always_inline)) {
+      for (int s2 = rr * P; s2 < min((rr + 1) * P, nsteps); ++s2) issue(s2);
+    };
+    const bool early = w >= 4;
+
+    // ---- products of step s for this wave's first NG query groups ----
+    auto compute = [&](auto ngc, int s) __attribute__((always_inline)) {
+      constexpr int NG = decltype(ngc)::value;
+      f32x4 st[NG][2];
+#pragma unroll
+      for (int i = 0; i < NG; ++i) bias_init(i, s, st[i]);
+      Frag<T> kf[NC][2];
+      read_k(s, kf);
+      Frag<T> vf[NO];
+      Frag<T> af[NG];
+      if constexpr (NG == 2 && sizeof(T) == 2) {
+        // Two groups: one group's products run on the matrix cores while the
+        // other group's SiLU runs on the vector ALUs (the scheduler is told
+        // to alternate one product with a few vector instructions).
+        s_mma(0, kf, st[0]);
+        read_v(s, vf);
+        s_mma(1, kf, st[1]);
+        silu_frag(st[0], af[0]);
+#pragma unroll
+        for (int k = 0; k < 2 * NC; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        o_mma(0, vf, af[0]);
+        silu_frag(st[1], af[1]);
+#pragma unroll
+        for (int k = 0; k < NO; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 1);
+        }
+        o_mma(1, vf, af[1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) s_mma(i, kf, st[i]);
+        // V^T fragments are read now so that their LDS latency overlaps the
+        // SiLU below.
+        read_v(s, vf);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) silu_frag(st[i], af[i]);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) o_mma(i, vf, af[i]);
+      }
+    };
+
+    // ---- the key loop: one barrier per round of P steps.  Round r's steps
+    // sit in stages rP .. rP+P-1 (mod NST); the loads of round r+D are
+    // issued once round r-1's stages are free, so D rounds are in flight
+    // while one is multiplied.  (The wave's group count is fixed for the
+    // item, so each count gets a loop of its own.) ----
     auto key_loop = [&](auto ngc) __attribute__((always_inline)) {
+      for (int rr = 0; rr < min(D, nrounds); ++rr) issue_round(rr);
       for (int r = 0; r < nrounds; ++r) {
         // round r's loads have landed once only those issued after them remain
         const int later = min((r + D) * P, nsteps) - (r + 1) * P;
@@ -485,15 +521,12 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
         else wait_vm<0>();
         if (r == tail_round) zero_tail();
         bar();                             // round r visible; round r-1 no longer read
-        const bool early = w >= 4;
-        if (early)
-          for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
+        if (early) issue_round(r + D);
         if constexpr (decltype(ngc)::value > 0) {
           const int s = r * P + ph;
           if (s < nsteps) compute(ngc, s);
         }
-        if (!early)
-          for (int s2 = (r + D) * P; s2 < min((r + D + 1) * P, nsteps); ++s2) issue(s2);
+        if (!early) issue_round(r + D);
       }
     };
     if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});
@@ -538,10 +571,11 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     it = it_next;
     item = item_next;
   }
+  wait_vm<0>();                            // a workgroup without items: its table loads land first
 }
 template <typename T, int HD>
 hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
-                  const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,
+                  int layer, const int64_t* ts, const int32_t* ts_off,
                   const int32_t* ncand, const WsPtrs& ws, int grid, hipStream_t stream,
                   const KernelEvents& ev) {
   AttnArgs<T> a;
@@ -549,8 +583,7 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.k_pool = static_cast<const T*>(k_pool);
   a.v_pool = static_cast<const T*>(v_pool);
   a.q = static_cast<const T*>(ws.q);
-  a.pos_bias = pos_bias;
-  a.ts_bias = ts_bias;
+  a.tab = ws.tables + static_cast<size_t>(layer) * kTabFloats;
   a.ts = ts;
   a.ts_off = ts_off;
   a.ncand = ncand;
@@ -565,30 +598,33 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.mbits = d.pos_mbits;
   a.ntsb = d.ts_buckets;
   a.tsmbits = d.ts_mbits;
-  if (ncand != nullptr) return launch_kernel(attn_kernel<T, HD, true>, dim3(grid), dim3(64 * kWaves), stream, ev, a);
-  return launch_kernel(attn_kernel<T, HD, false>, dim3(grid), dim3(64 * kWaves), stream, ev, a);
+  const dim3 gr(grid), bl(64 * kWaves);
+  if (d.ts_buckets > 0)
+    return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, true>, gr, bl, stream, ev, a)
+                            : launch_kernel(attn_kernel<T, HD, false, true>, gr, bl, stream, ev, a);
+  return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, false>, gr, bl, stream, ev, a)
+                          : launch_kernel(attn_kernel<T, HD, false, false>, gr, bl, stream, ev, a);
 }
 
 template <typename T>
 hipError_t attn_dt(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
-                   const float* pos_bias, const float* ts_bias, const int64_t* ts, const int32_t* ts_off,
+                   int layer, const int64_t* ts, const int32_t* ts_off,
                    const int32_t* nc, const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
   switch (d.head_dim) {
-    case 32: return attn_t<T, 32>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, nc, ws, grid, stream, ev);
-    case 64: return attn_t<T, 64>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, nc, ws, grid, stream, ev);
-    default: return attn_t<T, 128>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, nc, ws, grid, stream, ev);
+    case 32: return attn_t<T, 32>(d, pt, k_pool, v_pool, layer, ts, ts_off, nc, ws, grid, stream, ev);
+    case 64: return attn_t<T, 64>(d, pt, k_pool, v_pool, layer, ts, ts_off, nc, ws, grid, stream, ev);
+    default: return attn_t<T, 128>(d, pt, k_pool, v_pool, layer, ts, ts_off, nc, ws, grid, stream, ev);
   }
 }
 
 }  // namespace
 
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
-                       const float* pos_bias, const float* ts_bias, const int64_t* ts,
-                       const int32_t* ts_off, const int32_t* ncand, const WsPtrs& ws, int grid,
-                       hipStream_t stream, const KernelEvents& ev) {
+                       int layer, const int64_t* ts, const int32_t* ts_off, const int32_t* ncand,
+                       const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev) {
   if (d.dtype == HSTU_BF16)
-    return attn_dt<bf16>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ncand, ws, grid, stream, ev);
-  return attn_dt<float>(d, pt, k_pool, v_pool, pos_bias, ts_bias, ts, ts_off, ncand, ws, grid, stream, ev);
+    return attn_dt<bf16>(d, pt, k_pool, v_pool, layer, ts, ts_off, ncand, ws, grid, stream, ev);
+  return attn_dt<float>(d, pt, k_pool, v_pool, layer, ts, ts_off, ncand, ws, grid, stream, ev);
 }
 
 }  // namespace hstu

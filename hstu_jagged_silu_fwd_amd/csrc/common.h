@@ -25,6 +25,27 @@ constexpr int kMaxQBlocks = kMaxRows / kQB + kMaxUsers;
 constexpr int kMaxStackLayers = 32;   // layers of one hstu_stack_fwd call
 
 // ---------------------------------------------------------------------------
+// Per-layer bias tables, built once per call by prep and copied into each
+// attention workgroup's LDS with direct-to-LDS loads.  All values are in the
+// attention's exponent domain (scaled by -log2(e)):
+//   [0, kLut)            bias of distance kLut - 1 - x (descending distance)
+//   [kLut, kTabPb)       kMasked (negative distances: the causal mask)
+//   [kTabPb, kTabTb)     position-bucket bias, kMaxBuckets entries
+//   [kTabTb, ...)        timestamp-bucket bias, kMaxBuckets entries
+// padded to whole KiB (kTabFloats).
+// ---------------------------------------------------------------------------
+constexpr int kLut = 4096;
+constexpr int kLutPad = 64;
+constexpr int kTabPb = kLut + kLutPad;
+constexpr int kTabTb = kTabPb + kMaxBuckets;
+constexpr int kTabFloats = (kTabTb + kMaxBuckets + 255) / 256 * 256;
+constexpr float kNegLog2e = -1.4426950408889634f;
+// Exponent-domain score of a masked (query, key) pair: S' = kMasked makes
+// 2^S' = inf, so SiLU = -ln2 * S' / (1 + 2^S') = S' * rcp(inf) = exactly 0
+// (kMasked plus any finite q.k stays finite).
+constexpr float kMasked = 1e30f;
+
+// ---------------------------------------------------------------------------
 // MFMA fragments.  A fragment holds 8 elements per lane.  For a 16x16 tile
 // product D = A*B with a 32-deep contraction, lane l supplies A[l&15][k] and
 // B[k][l&15] for the 8 contraction indices k = 8*(l>>4) + e, e = 0..7; the
@@ -243,6 +264,7 @@ struct WsPtrs {
   void* q;                   // [T, D] dtype; reused for G after attention
   void* u;                   // [T, D] dtype
   float* part;               // [item_cap, kQB, d] fp32 partial attention outputs
+  float* tables;             // [layers][kTabFloats] bias tables (see kTabFloats)
 };
 
 // Optional events that the runtime stamps at the start and the end of one
@@ -269,15 +291,14 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 // Host launchers (one per kernel family), all enqueue on `stream`.
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
                        const int32_t* ncand, const int32_t* const* pts, int nl, const int32_t* ts_off,
-                       const WsPtrs& ws,
+                       const float* const* pbs, const float* const* tbs, const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream,
                        const KernelEvents& ev = {});
 hipError_t launch_gemm_qkv(const hstu_layer_desc& d, const void* x, const void* w1t, void* k_pool,
                            void* v_pool, const WsPtrs& ws, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_attn(const hstu_layer_desc& d, const int32_t* pt, const void* k_pool, const void* v_pool,
-                       const float* pos_bias, const float* ts_bias, const int64_t* ts,
-                       const int32_t* ts_off, const int32_t* ncand, const WsPtrs& ws, int grid,
-                       hipStream_t stream, const KernelEvents& ev = {});
+                       int layer, const int64_t* ts, const int32_t* ts_off, const int32_t* ncand,
+                       const WsPtrs& ws, int grid, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_gemm_out(const hstu_layer_desc& d, const void* g, const void* w2t, void* y,
                            int32_t* status, hipStream_t stream, const KernelEvents& ev = {});
 hipError_t launch_norm_gate(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipStream_t stream,

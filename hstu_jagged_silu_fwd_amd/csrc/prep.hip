@@ -2,9 +2,9 @@
 // rows to users and pool slots, and builds the attention work list.
 // Workgroup 0 validates, workgroup 1 builds the work list at the same time
 // (each keeps the per-user and per-q-block metadata in LDS; their scans run
-// inside one wave, so the only workgroup barriers are between phases), and
-// workgroups 2.. each map a slice of kRowsPerWg new rows to (user, page,
-// slot).
+// inside one wave, so the only workgroup barriers are between phases), one
+// workgroup per layer builds that layer's bias tables for the attention, and
+// the others each map a slice of kRowsPerWg new rows to (user, page, slot).
 //
 // Work decomposition: the new rows of user u are cut into q-blocks of kQB
 // rows; q-block qb sees keys [0, hist + min(n, (qb+1)*kQB)) (causal).  The key
@@ -51,8 +51,11 @@ struct PrepArgs {
   const int32_t* ncand;
   const int32_t* pt[kMaxStackLayers];   // page table of each layer (nl of them)
   const int32_t* ts_off;
+  const float* pb[kMaxStackLayers];     // position-bucket bias of each layer
+  const float* tb[kMaxStackLayers];     // timestamp-bucket bias of each layer (null: none)
   WsPtrs ws;
   int B, T, H, ps, maxP, nl;
+  int nb, mbits, ntsb;
   int64_t P;
   int nqb_cap, item_cap, target_items;
 };
@@ -66,6 +69,8 @@ struct PrepShared {
   int32_t qbu[kMaxQBlocks];        // user of each q-block entry
   int32_t pgp[kMaxUsers + 1];      // first flat page index of each user
   int32_t cnt[kPrepWaves][16];     // per-wave item counts of the candidate budgets
+  float tpb[kMaxBuckets];          // a layer's scaled bucket tables (table workgroups)
+  float ttb[kMaxBuckets];
   int32_t bad[kPrepWaves];
   int32_t err, nqb, budget, n_items, b_lo, b_hi;
 };
@@ -165,17 +170,45 @@ __device__ int check_offsets(const PrepArgs& a, const PrepShared& s, int lane) {
 __device__ void validate(const PrepArgs& a, PrepShared& s);
 __device__ void work_list(const PrepArgs& a, PrepShared& s);
 
+// Layer l's bias tables (layout at kTabFloats), in the attention's exponent
+// domain: the bucket tables scaled by -log2(e), the distance table read from
+// them through the bucket rule, masked entries past it.
+__device__ void build_tables(const PrepArgs& a, PrepShared& s, int l) {
+  const int tid = threadIdx.x;
+  const float* pb = a.pb[l];
+  const float* tb = a.tb[l];
+  for (int i = tid; i < kMaxBuckets; i += kPrepThreads) {
+    s.tpb[i] = i < a.nb ? kNegLog2e * pb[i] : 0.f;
+    s.ttb[i] = (tb != nullptr && i < a.ntsb) ? kNegLog2e * tb[i] : 0.f;
+  }
+  __syncthreads();
+  float* out = a.ws.tables + static_cast<size_t>(l) * kTabFloats;
+  for (int i = tid; i < kTabFloats; i += kPrepThreads) {
+    float v = 0.f;
+    if (i < kLut) v = s.tpb[bucket32(kLut - 1 - i, a.mbits, a.nb)];
+    else if (i < kTabPb) v = kMasked;
+    else if (i < kTabTb) v = s.tpb[i - kTabPb];
+    else if (i < kTabTb + kMaxBuckets) v = s.ttb[i - kTabTb];
+    out[i] = v;
+  }
+}
+
 // Workgroup 0 validates the metadata (status), workgroup 1 builds the work
-// list (wl_status), workgroups 2.. map the rows.
+// list (wl_status), workgroups 2 .. 2+nl-1 build each layer's bias tables,
+// the rest map the rows.
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   __shared__ PrepShared s;
   const int tid = threadIdx.x;
   const int B = a.B;
+  if (blockIdx.x >= 2 && blockIdx.x < 2 + a.nl) {
+    build_tables(a, s, blockIdx.x - 2);
+    return;
+  }
   for (int u = tid; u <= B; u += kPrepThreads) s.off[u] = a.new_off[u];
   for (int u = tid; u < B; u += kPrepThreads) s.hist[u] = a.hist[u];
   __syncthreads();
   if (blockIdx.x >= 2) {
-    if (B > 0) map_rows(a, s, blockIdx.x - 2);   // B == 0 with rows is rejected by workgroup 0
+    if (B > 0) map_rows(a, s, blockIdx.x - 2 - a.nl);   // B == 0 with rows is rejected by workgroup 0
     return;
   }
   if (blockIdx.x == 1) work_list(a, s);
@@ -463,14 +496,21 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
 
 hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const int32_t* hist,
                        const int32_t* ncand, const int32_t* const* pts, int nl, const int32_t* ts_off,
-                       const WsPtrs& ws,
+                       const float* const* pbs, const float* const* tbs, const WsPtrs& ws,
                        int nqb_cap, int item_cap, int target_items, hipStream_t stream,
                        const KernelEvents& ev) {
   PrepArgs a;
   a.new_off = new_off;
   a.hist = hist;
   a.ncand = ncand;
-  for (int l = 0; l < kMaxStackLayers; ++l) a.pt[l] = l < nl ? pts[l] : nullptr;
+  for (int l = 0; l < kMaxStackLayers; ++l) {
+    a.pt[l] = l < nl ? pts[l] : nullptr;
+    a.pb[l] = l < nl ? pbs[l] : nullptr;
+    a.tb[l] = (l < nl && tbs != nullptr) ? tbs[l] : nullptr;
+  }
+  a.nb = d.pos_buckets;
+  a.mbits = d.pos_mbits;
+  a.ntsb = d.ts_buckets;
   a.nl = nl;
   a.ts_off = ts_off;
   a.ws = ws;
@@ -483,8 +523,8 @@ hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const i
   a.nqb_cap = nqb_cap;
   a.item_cap = item_cap;
   a.target_items = target_items;
-  return launch_kernel(prep_kernel, dim3(2 + (d.total_new + kRowsPerWg - 1) / kRowsPerWg), dim3(kPrepThreads),
-                       stream, ev, a);
+  return launch_kernel(prep_kernel, dim3(2 + nl + (d.total_new + kRowsPerWg - 1) / kRowsPerWg),
+                       dim3(kPrepThreads), stream, ev, a);
 }
 
 }  // namespace hstu

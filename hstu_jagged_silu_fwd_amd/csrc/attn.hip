@@ -9,16 +9,17 @@
 // chunk): a q-block covers all new rows of most users, so each history key is
 // read once per head and chunk.  A workgroup of eight waves takes one item at
 // a time.  The q-block's 16-row query groups are taken in adjacent pairs, one
-// pair per wave; when the block has few groups the waves also split the key
-// steps: they form P phases (P = 4, 2 or 1, as many as the waves allow) and
-// the waves of phase p multiply the steps s = p (mod P), so every wave has
-// products to do even for a single 16-row group.  The chunk's keys are walked
-// in 32-key steps.  A step's K rows [32][d] and V^T rows [d][32] are copied
-// from their pool pages into a ring of NST LDS stages with direct-to-LDS
-// loads that the waves share out; one barrier per round of P steps hands the
-// round's stages from the loads to the products, and the loads of the round D
-// rounds ahead (D = NST/P - 1) go into the stages the previous round freed.
-// At the end of an item the phases' partial sums meet in LDS.
+// pair per wave; when the block has at most eight groups the waves also split
+// the key steps: they form P = 2 phases and the waves of phase p multiply the
+// steps s = p (mod 2).  The chunk's keys are walked in 32-key steps.  A step's
+// K rows [32][d] and V^T rows [d][32] are copied from their pool pages into a
+// ring of NST LDS stages with direct-to-LDS loads that the waves share out;
+// one barrier per round (two steps per wave with one phase, one step per
+// wave with two) hands the round's stages from the loads to the products, and
+// the loads of a round two rounds behind the ring's end go into stages freed
+// two rounds earlier.  The two waves of a SIMD run their steps half a step
+// apart (see the key loop).  At the end of an item the phases' partial sums
+// meet in LDS.
 // Per step and wave:
 //   S^T[32 keys x 16 queries] = K * Q^T     (2 MFMA blocks over d; the
 //                                           accumulators start at the bias,
@@ -121,7 +122,9 @@ struct StepGeo {
   // ring: 8 stages, or as many as fit in 128 KiB (a power of two)
   static constexpr int NST_FIT = 131072 / STAGE;
   static constexpr int NST = NST_FIT >= 8 ? 8 : (NST_FIT >= 4 ? 4 : 2);
-  static constexpr int PMAX = NST / 2;                 // phases: the ring holds two rounds of PMAX steps
+  // phases: the ring holds at least three rounds of PMAX steps (see the
+  // key loop)
+  static constexpr int PMAX = NST >= 6 ? 2 : 1;
   // chunk permutation of K row `key`: (m >> KSH) with m = (key & 3) | (((key >> 3) & 3) << 2),
   // m being the lane (mod 16) that reads the row; V^T row e: (e >> VSH) & (VCH - 1)
   static constexpr int KSH = KCH >= 16 ? 0 : (KCH == 8 ? 1 : 2);
@@ -232,8 +235,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // columns below WP/2 take groups in pairs from 0, and the others take
     // the remaining groups, in pairs only as far as needed.
     const int NW = (ngroups + 1) >> 1;
-    const int P = (G::PMAX >= 4 && 4 * NW <= kWaves) ? 4 : ((G::PMAX >= 2 && 2 * NW <= kWaves) ? 2 : 1);
-    const int D = NST / P - 1;                         // rounds of loads in flight ahead
+    const int P = (G::PMAX >= 2 && 2 * NW <= kWaves) ? 2 : 1;
+    // A round is RS = P * M steps, M of them per wave (two when every wave
+    // multiplies every step, which halves the barriers), and the ring holds
+    // R of them (at least three).
+    const int M = P == 1 && NST >= 8 ? 2 : 1;
+    const int RS = P * M;
+    const int R = NST / RS;
     const int half = kWaves / (2 * P);
     const int ph = w & (P - 1), col = w / P;
     int gi0, ng_w;                                     // this wave's first group and group count
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     }
     const int kend = min(k_hi, c + q0 + nq);           // keys up to the block's last query
     const int nsteps = (kend - k_lo + kStepKeys - 1) / kStepKeys;
-    const int nrounds = (nsteps + P - 1) / P;
+    const int nrounds = (nsteps + RS - 1) / RS;
     // Let these loads land before the ring starts: the compiler cannot count
     // outstanding loads across the key loop, so it would otherwise wait for
     // every in-flight stage at the first use of a query fragment.
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // once their loads have landed) so that stale pool memory cannot turn a
     // masked score or product into NaN, and the products need no tail case
     // of their own.
-    const int tail_round = k_lo + kStepKeys * nsteps > kst_end ? (nsteps - 1) / P : -1;
+    const int tail_round = k_lo + kStepKeys * nsteps > kst_end ? (nsteps - 1) / RS : -1;
     auto zero_tail = [&]() __attribute__((always_inline)) {
       const int kb = k_lo + kStepKeys * (nsteps - 1);
       const int nvalid = kst_end - kb;                 // staged keys of the step
@@ -456,12 +464,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): the zeros are in LDS
     };
-    // loads of the steps of round rr (early waves issue theirs before the
-    // products, the others after, so the two waves of a SIMD take turns)
+    // loads of the steps of round rr (each wave its share of every stage)
     auto issue_round = [&](int rr) __attribute__((always_inline)) {
-      for (int s2 = rr * P; s2 < min((rr + 1) * P, nsteps); ++s2) issue(s2);
+      for (int s2 = rr * RS; s2 < min((rr + 1) * RS, nsteps); ++s2) issue(s2);
     };
-    const bool early = w >= 4;
 
     // ---- products of step s for this wave's first NG query groups ----
     auto compute = [&](auto ngc, int s) __attribute__((always_inline)) {
@@ -507,31 +513,100 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       }
     };
 
-    // ---- the key loop: one barrier per round of P steps.  Round r's steps
-    // sit in stages rP .. rP+P-1 (mod NST); the loads of round r+D are
-    // issued once round r-1's stages are free, so D rounds are in flight
-    // while one is multiplied.  (The wave's group count is fixed for the
-    // item, so each count gets a loop of its own.) ----
+    // ---- the key loop: one barrier per round of RS steps; at barrier k the
+    // steps of round k (stages kRS .. kRS+RS-1 mod NST) are visible.  The two
+    // waves of a SIMD take turns on its matrix core and vector ALUs: waves
+    // 0-3 multiply a step in the plain order (bias, S^T, SiLU, O^T), waves
+    // 4-7 half a step later (SiLU and O^T of their step after barrier k+1,
+    // then the bias and S^T of their next step), so while one wave's
+    // products run the other's SiLU does.  A rotated wave still reads round
+    // k-1 after barrier k, so the loads issued at barrier k (round k+R-2)
+    // go into round k-2's stages: R-2 rounds are in flight ahead. ----
     auto key_loop = [&](auto ngc) __attribute__((always_inline)) {
+      const int D = R - 2;
       for (int rr = 0; rr < min(D, nrounds); ++rr) issue_round(rr);
       for (int r = 0; r < nrounds; ++r) {
         // round r's loads have landed once only those issued after them remain
-        const int later = min((r + D) * P, nsteps) - (r + 1) * P;
+        const int later = min((r + D) * RS, nsteps) - (r + 1) * RS;
         if (later > 0) wait_vm_n(later * my_cnt);
         else wait_vm<0>();
         if (r == tail_round) zero_tail();
-        bar();                             // round r visible; round r-1 no longer read
-        if (early) issue_round(r + D);
+        bar();                             // round r visible; round r-2 no longer read
         if constexpr (decltype(ngc)::value > 0) {
-          const int s = r * P + ph;
-          if (s < nsteps) compute(ngc, s);
+          for (int j = 0; j < M; ++j) {
+            const int s = r * RS + j * P + ph;
+            if (s < nsteps) compute(ngc, s);
+          }
         }
-        if (!early) issue_round(r + D);
+        issue_round(r + D);
       }
     };
-    if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});
-    else if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
-    else key_loop(std::integral_constant<int, 0>{});
+    auto key_loop_rot = [&](auto ngc) __attribute__((always_inline)) {
+      constexpr int NG = decltype(ngc)::value;
+      const int DP = R - 1;                // one round further: this wave's issue follows a later barrier
+      for (int rr = 0; rr < min(DP, nrounds); ++rr) issue_round(rr);
+      f32x4 st[NG > 0 ? NG : 1][2];
+      {                                    // barrier 0: round 0 visible; S^T of the first step
+        const int later = min(DP * RS, nsteps) - RS;
+        if (later > 0) wait_vm_n(later * my_cnt);
+        else wait_vm<0>();
+        if (tail_round == 0) zero_tail();
+        bar();
+        if constexpr (NG > 0) {
+          const int s = min(ph, nsteps - 1);
+#pragma unroll
+          for (int i = 0; i < NG; ++i) bias_init(i, s, st[i]);
+          Frag<T> kf[NC][2];
+          read_k(s, kf);
+#pragma unroll
+          for (int i = 0; i < NG; ++i) s_mma(i, kf, st[i]);
+        }
+      }
+      for (int r = 0; r < nrounds; ++r) {
+        if (r + 1 < nrounds) {
+          // barrier r+1: round r+1's loads have landed once only those issued after them remain
+          const int later = min((r + DP) * RS, nsteps) - (r + 2) * RS;
+          if (later > 0) wait_vm_n(later * my_cnt);
+          else wait_vm<0>();
+          if (r + 1 == tail_round) zero_tail();
+          bar();
+        }
+        issue_round(r + DP);
+        if constexpr (NG > 0) {
+          for (int j = 0; j < M; ++j) {
+          const int s = r * RS + j * P + ph;
+          if (s < nsteps) {
+            // this step's SiLU and O^T, then the next step's bias and S^T
+            // (formed on this step's stage when there is none, so that the
+            // products have no branches of their own)
+            const int s1 = s + P < nsteps ? s + P : s;
+            Frag<T> vf[NO];
+            read_v(s, vf);
+            Frag<T> kf[NC][2];
+            read_k(s1, kf);
+            Frag<T> af[NG];
+#pragma unroll
+            for (int i = 0; i < NG; ++i) silu_frag(st[i], af[i]);
+#pragma unroll
+            for (int i = 0; i < NG; ++i) o_mma(i, vf, af[i]);
+#pragma unroll
+            for (int i = 0; i < NG; ++i) bias_init(i, s1, st[i]);
+#pragma unroll
+            for (int i = 0; i < NG; ++i) s_mma(i, kf, st[i]);
+          }
+          }
+        }
+      }
+    };
+    if (w < 4) {
+      if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});
+      else if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
+      else key_loop(std::integral_constant<int, 0>{});
+    } else {
+      if (ng_w == 2) key_loop_rot(std::integral_constant<int, 2>{});
+      else if (ng_w == 1) key_loop_rot(std::integral_constant<int, 1>{});
+      else key_loop_rot(std::integral_constant<int, 0>{});
+    }
 
     // ---- phases 1..P-1 hand their partial sums to phase 0 through the
     // (now idle) ring; phase 0 adds them and writes the item's rows ----

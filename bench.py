@@ -52,6 +52,8 @@ def parse():
                     help="time another configuration of the workload table through the same path (one instance; "
                          "the JSON line then carries no CPU baseline)")
     ap.add_argument("--no-events", action="store_true", help="skip the per-kernel event pass (no roofline or stage split)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline workload only: no 8-layer long-history record and no cached-vs-recompute ratios")
     ap.add_argument("--kvcache", action="store_true",
                     help="measure the KV cache manager (plan on the host, page tables on the device) "
                          "on a serving stream instead of the layer")
@@ -145,7 +147,10 @@ def load_traffic():
 
 
 class Bench:
-    def __init__(self, args):
+    def __init__(self, args, wl=None):
+        """The stack of workload args.workload (the headline workload with
+        args.instances independent batches, others with one), or of the
+        given workload `wl` (one batch of all its users)."""
         import torch
         import hstu_jagged_silu_fwd_amd as hs
         from hstu_jagged_silu_fwd_amd import _lib
@@ -154,11 +159,16 @@ class Bench:
         self.torch, self.hs, self._lib = torch, hs, _lib
         self.lib = hs.load()
         self.hip = _lib.hip_runtime()
-        name = args.workload
-        self.R = args.instances if name == WORKLOAD else 1
-        B = CONFIGS[name]["B"]
+        if wl is None:
+            name = args.workload
+            self.R = args.instances if name == WORKLOAD else 1
+            B = CONFIGS[name]["B"]
+            wl = make_workload(name, seed=args.seed, B=B * self.R)
+        else:
+            self.R = 1
+            B = wl.B
         self.B = B
-        self.wl = wl = make_workload(name, seed=args.seed, B=B * self.R)
+        self.wl = wl
         self.L, self.D, self.H, self.d = wl.layers, wl.D, wl.H, wl.d
         dev = torch.device("cuda")
         bf = torch.bfloat16 if wl.dtype == "bf16" else torch.float32      # the workload's element type
@@ -282,16 +292,21 @@ class Bench:
         return ms.value
 
     def attn_work(self, io):
-        """Algorithmic bytes and FLOPs of one attention launch on instance io."""
+        """Work of one attention launch on instance io: the algorithmic bytes
+        (every cached history key's K and V row read once, 2 * D elements per
+        key: 4 * D bytes in bf16), the broader count that also takes the new
+        rows' K/V, the queries and one fp32 output, and the FLOPs (4 * D per
+        query-key pair)."""
         D = self.D
         es = 2 if self.wl.dtype == "bf16" else 4
-        kv = 0
+        hist_kv = kv = 0
         flops = 0
         for c, n in zip(io["hist"].tolist(), io["new_len"].tolist()):
+            hist_kv += c * 2 * D * es
             kv += (c + n) * 2 * D * es            # K and V rows read once
             flops += 4 * D * (n * c + n * (n + 1) // 2)
         T = io["T"]
-        return kv + T * D * es + T * D * 4, flops, kv
+        return hist_kv, kv + T * D * es + T * D * 4, flops
 
 
 def host_info():
@@ -423,8 +438,8 @@ def kvhost_bench(args):
     vp = torch.zeros((P, H, d, ps), dtype=torch.bfloat16, device="cuda")
     page_bytes = 2 * H * ps * d * 2
     empty = (np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros((0, 4), np.int32), [])
-    def run(copies):
-        kv.copy_pages(Plan(*empty, copies), kp, vp)
+    def run(copies, stream=None):
+        kv.copy_pages(Plan(*empty, copies), kp, vp, stream=stream)
     off = np.array([[0, i, i, 0] for i in range(npg)], np.int32)
     on = np.array([[1, npg + i, i, 0] for i in range(npg)], np.int32)
     for _ in range(3):
@@ -468,6 +483,33 @@ def kvhost_bench(args):
     e[1].record()
     torch.cuda.synchronize()
     t_rec = e[0].elapsed_time(e[1]) / reps * 1e-3
+    # overlap: one user's onboard on a copy stream while another request's
+    # layers run on the compute stream (different pages: nothing to order
+    # between them), against the two back to back on one stream
+    copier = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    def pair(overlap):
+        if overlap:
+            copier.wait_stream(compute)
+            run(on_user, stream=copier)
+        else:
+            run(on_user)
+        st.forward(x, off_u, np.zeros(1, np.int32))
+        if overlap:
+            compute.wait_stream(copier)
+    for ov in (False, True):
+        for _ in range(3):
+            pair(ov)
+    torch.cuda.synchronize()
+    t_pair = {}
+    for ov in (False, True):
+        e[0].record()
+        for _ in range(reps):
+            pair(ov)
+        e[1].record()
+        torch.cuda.synchronize()
+        t_pair[ov] = e[0].elapsed_time(e[1]) / reps * 1e-3
+    hidden = (t_pair[False] - t_pair[True]) / min(t_user, t_rec)
     gb = npg * page_bytes / 1e9
     print(json.dumps({
         "metric": "host-tier page copies: offload / onboard bandwidth; onboard vs recompute of one user",
@@ -475,6 +517,10 @@ def kvhost_bench(args):
         "offload_GBs": gb / t_off, "onboard_GBs": gb / t_on, "pages": npg, "page_bytes": page_bytes,
         "user_onboard_us": t_user * 1e6, "user_recompute_us": t_rec * 1e6,
         "recompute_over_onboard": t_rec / t_user,
+        "onboard_then_layers_us": t_pair[False] * 1e6, "onboard_overlapped_with_layers_us": t_pair[True] * 1e6,
+        "overlap_hidden_fraction": hidden,
+        "overlap_note": "one user's onboard (copy stream) against another request's 3 layers (compute stream), "
+                        "hidden fraction = (serial - overlapped) / the shorter of the two",
         "config": {"workload": "kvhost-3layer-bf16-hist4096", "layers": L, "hidden": H * d, "heads": H,
                    "head_dim": d, "page_size": ps, "user_tokens": 4096, "user_pages": upages}}), flush=True)
 
@@ -801,84 +847,157 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
     import torch
+    from workloads import B8_KV_HIT_LONG
     b = Bench(args)
-    for s in range(args.warmup):
-        b.step(s)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        b.step(s)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    # Second pass over the same K steps with per-kernel start/stop events
-    # (stamped by the runtime at each kernel's start and end on the stream it
-    # runs on): exact kernel durations for the roofline and the stage split.
-    # Kept out of the timed pass because enqueueing the events slows the
-    # host's submission of the launches.
-    events = None
-    if not args.no_events:
-        events = b.make_events(args.steps)
-        torch.cuda.synchronize()
-        for s in range(args.steps):
-            b.step(s, events[s])
-        torch.cuda.synchronize()
-    tokens = sum(b.inst[s % b.R]["T"] for s in range(args.steps))
-    value = tokens / wall
+    m = time_stack(b, args.steps, args.warmup, events=not args.no_events)
+    value = m["tokens"] / m["wall"]
     from workloads import CONFIGS
     spec = CONFIGS[b.wl.name]
     out = dict(metric=METRIC if b.wl.name == WORKLOAD else f"HSTU stack new-tokens/sec ({b.wl.name})",
                value=value, unit="new tokens/s", n_gpus=1, steps=args.steps,
-               warmup=args.warmup, ms_per_step=1e3 * wall / args.steps, higher_is_better=True,
+               warmup=args.warmup, ms_per_step=1e3 * m["wall"] / args.steps, higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype=b.wl.dtype, data="synthetic",
                config=dict(workload=b.wl.name, layers=b.L, batch=b.B, hidden=b.D, heads=b.H,
                            head_dim=b.d, page_size=b.wl.page_size, pool_pages=b.wl.num_pool_pages,
                            hist=str(spec["hist"]), new=str(spec["new"]), instances=b.R,
                            timestamps=b.wl.ts_buckets > 0,
-                           new_tokens_per_step=tokens / args.steps,
+                           new_tokens_per_step=m["tokens"] / args.steps,
                            per_layer_new_tokens_per_s=value * b.L))
-    if events is not None:
-        stage_ms = np.zeros(b._lib.NUM_STAGES)
-        attn_bytes = attn_flops = 0
-        n_launch = 0
-        attn_each, step_each = [], []
-        for s in range(args.steps):
-            io = b.inst[s % b.R]
-            by, fl, _ = b.attn_work(io)
-            step_sum = 0.0
-            for l in range(b.L):
-                ev = events[s][l]
-                for k in range(b._lib.NUM_STAGES):
-                    ms = b.elapsed_ms(ev[2 * k], ev[2 * k + 1])
-                    stage_ms[k] += ms
-                    step_sum += ms
-                    if k == 2:
-                        attn_each.append(1e3 * ms)
-                attn_bytes += by
-                attn_flops += fl
-                n_launch += 1
-            step_each.append(1e3 * step_sum)
-        attn_s = stage_ms[2] / 1e3
-        achieved = attn_bytes / attn_s / 1e9
-        out["roofline"] = dict(kernel="paged_silu_attn", bound="hbm", achieved=achieved,
-                               peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                               traffic=load_traffic() if b.wl.name == WORKLOAD else None,
-                               mean_us=1e6 * attn_s / n_launch,
-                               timing="hipExtLaunchKernel start/stop events per launch, second pass of the same steps",
-                               bytes_per_launch=attn_bytes / n_launch,
-                               mfma_tflops=attn_flops / attn_s / 1e12,
-                               mfma_frac=attn_flops / attn_s / 1e12 / BF16_PEAK_TFLOPS)
-        out["stages_us"] = {name: 1e3 * stage_ms[k] / n_launch for k, name in enumerate(b._lib.STAGES)}
-        out["stages_note"] = ("per layer, from the layer-by-layer event pass, where prep runs in every layer; "
-                              "the timed stack call runs it once per step")
-        out["kernel_sum_ms_per_step"] = float(stage_ms.sum() / args.steps)
-        pct = lambda v: [float(np.percentile(v, q)) for q in (10, 50, 90)]
-        out["percentiles_us"] = {"attn_launch_p10_p50_p90": pct(attn_each),
-                                 "step_kernels_p10_p50_p90": pct(step_each),
-                                 "note": "event pass; steps rotate over the instances' different batches"}
+    if m.get("stage_ms") is not None:
+        out["roofline"] = roofline_of(m, load_traffic() if b.wl.name == WORKLOAD else None)
+        add_stages(out, m, b, args.steps)
+    headline = b.wl.name == WORKLOAD and not args.no_events and not args.no_extras
+    if headline:
+        # the same users recomputed from scratch (nothing cached), against
+        # the cached step of the same batch
+        out["cache_speedup"] = {b.wl.name: cache_speedup(args, b)}
     if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
+    if headline:
+        # the 8-layer long-history hit (where the pages' KV streaming lives)
+        del b
+        torch.cuda.empty_cache()
+        bl = Bench(argparse.Namespace(workload=B8_KV_HIT_LONG, instances=1, seed=args.seed))
+        ml = time_stack(bl, max(4, args.steps // 6), 2, events=True)
+        rec = dict(workload=bl.wl.name, value=ml["tokens"] / ml["wall"], unit="new tokens/s",
+                   ms_per_step=1e3 * ml["wall"] / ml["steps"], steps=ml["steps"], layers=bl.L, batch=bl.B,
+                   hist=str(CONFIGS[bl.wl.name]["hist"]), new=str(CONFIGS[bl.wl.name]["new"]),
+                   page_size=bl.wl.page_size, roofline=roofline_of(ml, None))
+        add_stages(rec, ml, bl, ml["steps"])
+        out["cache_speedup"][bl.wl.name] = cache_speedup(args, bl)
+        out["long_history"] = rec
     print(json.dumps(out), flush=True)
+
+
+def time_stack(b, steps, warmup, events=True):
+    """Wall time of `steps` stack calls after `warmup` (each one
+    hstu_stack_fwd call, synchronised on both sides), and, with events, a
+    second pass over the same steps with runtime-stamped start/stop events
+    around every stage kernel (kept out of the timed pass because enqueueing
+    the events slows the host's submission of the launches)."""
+    import torch
+    for s in range(warmup):
+        b.step(s)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        b.step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    m = dict(wall=wall, steps=steps, tokens=sum(b.inst[s % b.R]["T"] for s in range(steps)), stage_ms=None)
+    if not events:
+        return m
+    evs = b.make_events(steps)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        b.step(s, evs[s])
+    torch.cuda.synchronize()
+    stage_ms = np.zeros(b._lib.NUM_STAGES)
+    hist_bytes = broad_bytes = flops = 0
+    n_launch = 0
+    attn_each, step_each = [], []
+    for s in range(steps):
+        io = b.inst[s % b.R]
+        hb, bb, fl = b.attn_work(io)
+        step_sum = 0.0
+        for l in range(b.L):
+            ev = evs[s][l]
+            for k in range(b._lib.NUM_STAGES):
+                ms = b.elapsed_ms(ev[2 * k], ev[2 * k + 1])
+                stage_ms[k] += ms
+                step_sum += ms
+                if k == 2:
+                    attn_each.append(1e3 * ms)
+            hist_bytes += hb
+            broad_bytes += bb
+            flops += fl
+            n_launch += 1
+        step_each.append(1e3 * step_sum)
+    m.update(stage_ms=stage_ms, hist_bytes=hist_bytes, broad_bytes=broad_bytes, flops=flops, n_launch=n_launch,
+             attn_each=attn_each, step_each=step_each)
+    return m
+
+
+def roofline_of(m, traffic):
+    """The attention kernel against HBM: the algorithmic bytes are every
+    cached history key's K and V read once (4 * D bytes per key in bf16) per
+    launch, over its mean duration from the event pass; the broader count
+    (plus the new rows' K/V, the queries and one fp32 output) is kept beside
+    it, and the MFMA position of the same launches (4 * D FLOP per
+    query-key pair)."""
+    attn_s = m["stage_ms"][2] / 1e3
+    n = m["n_launch"]
+    achieved = m["hist_bytes"] / attn_s / 1e9
+    broad = m["broad_bytes"] / attn_s / 1e9
+    return dict(kernel="paged_silu_attn", bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=achieved / HBM_PEAK_GBS, traffic=traffic, mean_us=1e6 * attn_s / n,
+                timing="hipExtLaunchKernel start/stop events per launch, second pass of the same steps",
+                bytes_per_launch=m["hist_bytes"] / n,
+                bytes_note="algorithmic: every cached history key's K and V row read once (4 * D bytes)",
+                broad_bytes_per_launch=m["broad_bytes"] / n, broad_achieved=broad,
+                broad_frac=broad / HBM_PEAK_GBS,
+                mfma_tflops=m["flops"] / attn_s / 1e12, mfma_frac=m["flops"] / attn_s / 1e12 / BF16_PEAK_TFLOPS)
+
+
+def add_stages(out, m, b, steps):
+    n = m["n_launch"]
+    out["stages_us"] = {name: 1e3 * m["stage_ms"][k] / n for k, name in enumerate(b._lib.STAGES)}
+    out["stages_note"] = ("per layer, from the layer-by-layer event pass, where prep runs in every layer; "
+                          "the timed stack call runs it once per step")
+    out["kernel_sum_ms_per_step"] = float(m["stage_ms"].sum() / steps)
+    pct = lambda v: [float(np.percentile(v, q)) for q in (10, 50, 90)]
+    out["percentiles_us"] = {"attn_launch_p10_p50_p90": pct(m["attn_each"]),
+                             "step_kernels_p10_p50_p90": pct(m["step_each"]),
+                             "note": "event pass; steps rotate over the instances' different batches"}
+
+
+def cache_speedup(args, b, steps=6, warmup=2):
+    """The cached step of the bench's first batch against the same users
+    recomputed from scratch (each user's whole sequence, history and new
+    rows, as new rows with nothing cached) through the same stack: the
+    analogue, on one MI355X, of the pages' KV-hit versus no-cache latency
+    ratios (context only)."""
+    import torch
+    from workloads import make_workload
+    io = b.inst[0]
+    for _ in range(warmup):
+        b.step(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.step(0)
+    torch.cuda.synchronize()
+    cached = (time.perf_counter() - t0) / steps
+    full = (io["hist"] + io["new_len"]).astype(int).tolist()
+    wr = make_workload(b.wl.name, seed=args.seed + 1, B=len(full), hist=("const", 0), new=("fixed", full))
+    br = Bench(args, wl=wr)
+    mr = time_stack(br, steps, warmup, events=False)
+    rec = mr["wall"] / steps
+    del br
+    torch.cuda.empty_cache()
+    return dict(cached_ms_per_batch=1e3 * cached, recompute_ms_per_batch=1e3 * rec, speedup=rec / cached,
+                users=len(full), cached_tokens=int(io["hist"].sum()), new_tokens=int(io["T"]),
+                recompute_tokens=int(sum(full)))
 
 
 if __name__ == "__main__":

@@ -172,6 +172,21 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def stream_scope(stream):
+    """Context for a call on `stream` (a torch stream or a raw hipStream_t):
+    the binding's staging copies and output allocations then go on that
+    stream too, so they are ordered with the library's kernels there and the
+    caching allocator does not hand their memory to another stream early.
+    None: the current stream, nothing changes."""
+    import contextlib
+    import torch
+    if stream is None:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(stream)
+
+
 def _tdtype(desc: LayerDesc):
     import torch
     return torch.bfloat16 if desc.dtype == HSTU_BF16 else torch.float32

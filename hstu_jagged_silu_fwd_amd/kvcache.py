@@ -186,7 +186,12 @@ class KVCache:
 
     def copy_pages(self, plan: Plan, k_pool, v_pool, stream=None) -> None:
         """Runs the plan's offloads, then its onboards, between the device pools
-        and the pinned host tier (call before the batch's layers)."""
+        and the pinned host tier (call before the batch's layers), on `stream`
+        (default: the current stream)."""
+        with _lib.stream_scope(stream):
+            self._copy_pages(plan, k_pool, v_pool)
+
+    def _copy_pages(self, plan: Plan, k_pool, v_pool) -> None:
         import torch
         m = plan.copies.shape[0]
         if m == 0:
@@ -207,7 +212,7 @@ class KVCache:
         pbv = v_pool[0].numel() * v_pool.element_size()
         rc = self.lib.hstu_kv_copy_pages(P(k_pool.data_ptr()), P(v_pool.data_ptr()), P(hk.data_ptr()),
                                          P(hv.data_ptr()), pbk, pbv, int(k_pool.shape[0]), self.PH,
-                                         P(dev.data_ptr()), plan.n_offload, m, _lib._stream(stream))
+                                         P(dev.data_ptr()), plan.n_offload, m, _lib._stream(None))
         if rc != 0:
             raise KVCacheError("hstu_kv_copy_pages", rc)
 
@@ -222,7 +227,12 @@ class KVCache:
 
     def build_tables(self, plan: Plan, device="cuda", stream=None):
         """Applies the plan's updates to the device directory and returns the
-        batch's page tables [L, B, max_pages] int32 on the device."""
+        batch's page tables [L, B, max_pages] int32 on the device, all on
+        `stream` (default: the current stream)."""
+        with _lib.stream_scope(stream):
+            return self._build_tables(plan, device)
+
+    def _build_tables(self, plan: Plan, device="cuda"):
         import torch
         d = self.directory(device)
         B = plan.slots.shape[0]
@@ -243,7 +253,7 @@ class KVCache:
         upd = dev[:4 * nu]
         slots = dev[4 * nu:]
         tables = torch.empty((self.L, B, self.maxP), dtype=torch.int32, device=d.device)
-        st = _lib._stream(stream)
+        st = _lib._stream(None)
         rc = self.lib.hstu_kv_tables_build(P(d.data_ptr()), self.L, self.max_users, self.maxP,
                                            P(upd.data_ptr()) if nu else None, int(nu),
                                            P(slots.data_ptr()) if B else None, B,

@@ -43,6 +43,7 @@ class HSTUStack:
         self._ws = None
         self._sws = None          # workspace of the stack calls
         self._last_ws = None      # workspace of the last call (its status word)
+        self._last_stream = None  # stream of the last call
 
     def desc(self, total_new: int, num_users: Optional[int] = None) -> _lib.LayerDesc:
         kw = dict(self.common)
@@ -70,14 +71,18 @@ class HSTUStack:
         return self._ws
 
     def append(self, l: int, k_new, v_new, new_offsets, hist_len, stream=None) -> None:
-        """kv_pages_append of rows into layer l's pages (status in self.status)."""
+        """kv_pages_append of rows into layer l's pages (status in self.status),
+        on `stream` (default: the current stream; inputs are staged there)."""
+        with _lib.stream_scope(stream):
+            self._append(l, k_new, v_new, new_offsets, hist_len)
+
+    def _append(self, l, k_new, v_new, new_offsets, hist_len) -> None:
         k_new = self._dev(k_new, self.tdtype)
         v_new = self._dev(v_new, self.tdtype)
         off = self._dev(new_offsets, torch.int32)
         T = int(k_new.shape[0])
         _lib.kv_pages_append(self.desc(T), k_new, v_new, off, self._dev(hist_len, torch.int32),
-                             self.layers[l]["page_table"], self.k_pool, self.v_pool, self.status,
-                             stream=stream)
+                             self.layers[l]["page_table"], self.k_pool, self.v_pool, self.status)
 
     def layer(self, l: int, x: torch.Tensor, new_offsets: torch.Tensor, hist_len: torch.Tensor,
               y: torch.Tensor, workspace: Optional[torch.Tensor] = None, timestamps=None,
@@ -86,6 +91,13 @@ class HSTUStack:
         """Layer l over a batch; page_table [B, max_pages] overrides the layer's
         own table (the batch size is then taken from new_offsets);
         num_candidates [B] int32 marks each user's trailing candidate rows."""
+        with _lib.stream_scope(stream):
+            self._layer(l, x, new_offsets, hist_len, y, workspace, timestamps, ts_offsets, stage_events,
+                        page_table, num_candidates)
+        self._last_stream = stream
+
+    def _layer(self, l, x, new_offsets, hist_len, y, workspace, timestamps, ts_offsets, stage_events,
+               page_table, num_candidates) -> None:
         T = int(x.shape[0])
         L = self.layers[l]
         nu = None if page_table is None else int(new_offsets.shape[0]) - 1
@@ -99,7 +111,7 @@ class HSTUStack:
         _lib.layer_fwd(desc, x, new_offsets, hist_len, L["page_table"] if page_table is None else page_table, self.k_pool,
                        self.v_pool, L["w1t"], L["w2t"], L["pos_bias"], y, ws,
                        ts_bias=L["ts_bias"], timestamps=timestamps, ts_offsets=ts_offsets,
-                       stream=stream, stage_events=stage_events, num_candidates=num_candidates)
+                       stage_events=stage_events, num_candidates=num_candidates)
 
     def forward(self, x, new_offsets, hist_len, timestamps=None, ts_offsets=None,
                 stream=None, return_all: bool = False, page_tables=None, num_candidates=None):
@@ -107,7 +119,16 @@ class HSTUStack:
         prepared once for all layers); returns the last layer's output (or
         all outputs).  page_tables: optional per-layer [B, max_pages] tables
         (e.g. a KV cache plan's, from KVCache.build_tables) instead of the
-        layers' own."""
+        layers' own.  stream: where the call runs (default: the current
+        stream); inputs are staged and outputs allocated there too."""
+        with _lib.stream_scope(stream):
+            out = self._forward(x, new_offsets, hist_len, timestamps, ts_offsets, return_all, page_tables,
+                                num_candidates)
+        self._last_stream = stream
+        return out
+
+    def _forward(self, x, new_offsets, hist_len, timestamps, ts_offsets, return_all, page_tables,
+                 num_candidates):
         x = self._dev(x, self.tdtype)
         off = self._dev(new_offsets, torch.int32)
         hl = self._dev(hist_len, torch.int32)
@@ -129,11 +150,13 @@ class HSTUStack:
         _lib.stack_fwd(desc, x, off, hl, pts, [self.k_pool] * nl, [self.v_pool] * nl, [l["w1t"] for l in L],
                        [l["w2t"] for l in L], [l["pos_bias"] for l in L], outs, self._sws,
                        ts_bias=[l["ts_bias"] for l in L] if has_ts else None, timestamps=ts, ts_offsets=tso,
-                       num_candidates=nc, stream=stream)
+                       num_candidates=nc)
         self._last_ws = self._sws
         return outs if return_all else outs[-1]
 
     def read_status(self, workspace: Optional[torch.Tensor] = None) -> int:
         """Device status of the last call: the given workspace, else that of
-        the last forward (stack call) or layer call, whichever ran last."""
-        return _lib.read_device_status(self._last_ws if workspace is None else workspace)
+        the last forward (stack call) or layer call, whichever ran last
+        (synchronises the stream that call ran on)."""
+        return _lib.read_device_status(self._last_ws if workspace is None else workspace,
+                                       stream=self._last_stream)

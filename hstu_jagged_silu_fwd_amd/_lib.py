@@ -17,6 +17,8 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG), "include", "hstu.h")
 
 HSTU_F32 = 0
 HSTU_BF16 = 1
+FLAG_BATCH_INVARIANT = 1        # hstu_layer_desc.flags bit (HSTU_FLAG_BATCH_INVARIANT)
+INVARIANT_CHUNK_KEYS = 256      # HSTU_INVARIANT_CHUNK_KEYS
 NUM_STAGES = 5
 STAGES = ("prep", "proj", "attn", "norm", "out")
 
@@ -46,6 +48,7 @@ class LayerDesc(ctypes.Structure):
         ("attn_scale", ctypes.c_float),
         ("norm_eps", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -138,13 +141,18 @@ def status_string(code: int) -> str:
 def make_desc(*, num_users: int, num_heads: int, head_dim: int, page_size: int,
               max_pages_per_user: int, num_pool_pages: int, total_new: int,
               pos_buckets: int, pos_mbits: int, attn_scale: float, norm_eps: float,
-              dtype: str, ts_buckets: int = 0, ts_mbits: int = 0) -> LayerDesc:
+              dtype: str, ts_buckets: int = 0, ts_mbits: int = 0,
+              batch_invariant: bool = False) -> LayerDesc:
+    """batch_invariant sets FLAG_BATCH_INVARIANT: every row's result is then
+    bit-identical whatever the batch and however the user's sequence was split
+    into calls (cached history or recompute)."""
     return LayerDesc(num_users=num_users, num_heads=num_heads, head_dim=head_dim,
                      hidden=num_heads * head_dim, page_size=page_size,
                      max_pages_per_user=max_pages_per_user, num_pool_pages=num_pool_pages,
                      total_new=total_new, pos_buckets=pos_buckets, pos_mbits=pos_mbits,
                      ts_buckets=ts_buckets, ts_mbits=ts_mbits, attn_scale=attn_scale,
-                     norm_eps=norm_eps, dtype=HSTU_BF16 if dtype == "bf16" else HSTU_F32)
+                     norm_eps=norm_eps, dtype=HSTU_BF16 if dtype == "bf16" else HSTU_F32,
+                     flags=FLAG_BATCH_INVARIANT if batch_invariant else 0)
 
 
 def _ptr(t, what: str, dtype=None, allow_none: bool = False):

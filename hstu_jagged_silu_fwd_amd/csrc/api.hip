@@ -1,6 +1,7 @@
 // C ABI of libhstu: descriptor validation, workspace layout and the launch
 // sequence of one layer (prep -> X W1 + SiLU/split/append -> paged SiLU
 // attention -> norm * U -> G W2).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -48,7 +49,14 @@ Layout make_layout(const hstu_layer_desc& d, int target, int nl = 1) {
   // chunk hits its cap, where it is <= H * entries * ceil(max_len / cap).
   const int64_t max_len = static_cast<int64_t>(d.max_pages_per_user) * d.page_size;
   const int64_t per_entry = 1 + (max_len + kMaxChunkKeys - 1) / kMaxChunkKeys;
-  L.item_cap = static_cast<int>(d.num_heads * L.nqb_cap * per_entry + target);
+  int64_t cap = d.num_heads * L.nqb_cap * per_entry + target;
+  // batch-invariant calls cut an entry of k keys into ceil(k / chunk) pieces
+  if (d.flags & HSTU_FLAG_BATCH_INVARIANT)
+    cap = std::max<int64_t>(cap, d.num_heads * L.nqb_cap *
+                                     ((max_len + HSTU_INVARIANT_CHUNK_KEYS - 1) / HSTU_INVARIANT_CHUNK_KEYS));
+  // (an absurd bound only makes the workspace absurd; prep rejects a call
+  // whose items exceed the cap)
+  L.item_cap = static_cast<int>(std::min<int64_t>(cap, int64_t{1} << 30));
   size_t off = 256;  // WsHeader
   L.row_loc = off;  off = align256(off + 8 * T * static_cast<size_t>(nl));
   L.qb_first = off; off = align256(off + 4 * static_cast<size_t>(L.nqb_cap));
@@ -92,6 +100,7 @@ hstu_status check_common(const hstu_layer_desc* d) {
       d->num_pool_pages < 1)
     return HSTU_ERR_INVALID_ARG;
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if ((d->flags & ~HSTU_FLAG_BATCH_INVARIANT) != 0) return HSTU_ERR_INVALID_ARG;
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return HSTU_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(d->num_heads) * d->head_dim != d->hidden) return HSTU_ERR_INVALID_ARG;
   if (d->hidden % 64 != 0 || d->hidden > 2048) return HSTU_ERR_UNSUPPORTED;

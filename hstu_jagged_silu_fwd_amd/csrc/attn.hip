@@ -93,6 +93,7 @@ struct AttnArgs {
   const AttnItem* items;
   float* part;
   int H, D, ps_shift, maxP, nb, mbits, ntsb, tsmbits;
+  int pmax;                  // 1: one phase per item (batch-invariant calls), else 2
 };
 
 // First distance of bucket b (b >= 2^m) under the log-linear rule.
@@ -235,7 +236,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // columns below WP/2 take groups in pairs from 0, and the others take
     // the remaining groups, in pairs only as far as needed.
     const int NW = (ngroups + 1) >> 1;
-    const int P = (G::PMAX >= 2 && 2 * NW <= kWaves) ? 2 : 1;
+    // (Batch-invariant calls keep one phase: a row's steps are then added in
+    // key order whatever its q-block holds.)
+    const int P = (G::PMAX >= 2 && a.pmax >= 2 && 2 * NW <= kWaves) ? 2 : 1;
     // A round is RS = P * M steps, M of them per wave (two when every wave
     // multiplies every step, which halves the barriers), and the ring holds
     // R of them (at least three).
@@ -673,6 +676,7 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.mbits = d.pos_mbits;
   a.ntsb = d.ts_buckets;
   a.tsmbits = d.ts_mbits;
+  a.pmax = (d.flags & HSTU_FLAG_BATCH_INVARIANT) ? 1 : 2;
   const dim3 gr(grid), bl(64 * kWaves);
   if (d.ts_buckets > 0)
     return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, true>, gr, bl, stream, ev, a)

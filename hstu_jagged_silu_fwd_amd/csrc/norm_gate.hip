@@ -185,7 +185,8 @@ hipError_t norm_dt(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipS
                    const KernelEvents& ev) {
   // a wave per row (4 rows per workgroup) for small batches, whose 32-thread
   // grid would leave compute units idle; large batches keep 32 per row
-  if (d.hidden % 256 == 0 && d.hidden <= 512 && d.total_new < 4096)
+  // (batch-invariant calls too: the instance then depends on D alone)
+  if (d.hidden % 256 == 0 && d.hidden <= 512 && d.total_new < 4096 && !(d.flags & HSTU_FLAG_BATCH_INVARIANT))
     return norm_t<T, 64, 2>(d, ws, nqb_cap, stream, ev);
   if (d.hidden % 128 == 0) {                     // 32 threads per row, 8 rows per workgroup
     const int ng = d.hidden / 128;

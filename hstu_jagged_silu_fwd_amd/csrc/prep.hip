@@ -20,6 +20,9 @@
 // attention workgroups (plus the number of entries, when those alone exceed
 // it).  Each entry's keys are then cut into near-equal
 // chunks (multiples of 32 keys).
+// Batch-invariant calls (HSTU_FLAG_BATCH_INVARIANT) skip the search: every
+// entry's keys are cut at the multiples of HSTU_INVARIANT_CHUNK_KEYS, so a
+// row's pieces depend only on its own position, never on the batch.
 #include "common.h"
 
 namespace hstu {
@@ -58,6 +61,7 @@ struct PrepArgs {
   int nb, mbits, ntsb;
   int64_t P;
   int nqb_cap, item_cap, target_items;
+  int inv_steps;                        // fixed chunk length in steps (batch-invariant calls), else 0
 };
 
 struct PrepShared {
@@ -424,7 +428,7 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
       int nch = 0;
       if (e < nqb) {
         const int v = s.qbn[e];
-        const int L = chunk_steps(budget, v >> kWShift);
+        const int L = a.inv_steps > 0 ? a.inv_steps : chunk_steps(budget, v >> kWShift);
         nch = ((v & kStepMask) + L - 1) / L;
         s.qbn[e] = nch;
       }
@@ -475,7 +479,8 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
     // the entry's keys are cut into nch near-equal chunks (multiples of a
     // step); csz is at most the entry's chunk bound, so (nch - 1) * csz <
     // keys and no chunk is empty
-    const int csz = ((keys + nch - 1) / nch + kStepKeys - 1) / kStepKeys * kStepKeys;
+    const int csz = a.inv_steps > 0 ? a.inv_steps * kStepKeys
+                                    : ((keys + nch - 1) / nch + kStepKeys - 1) / kStepKeys * kStepKeys;
     const int k_lo = kc * csz;
     AttnItem it;
     it.a = make_int4(u, qb * kQB, h, k_lo);
@@ -523,6 +528,9 @@ hipError_t launch_prep(const hstu_layer_desc& d, const int32_t* new_off, const i
   a.nqb_cap = nqb_cap;
   a.item_cap = item_cap;
   a.target_items = target_items;
+  static_assert(HSTU_INVARIANT_CHUNK_KEYS % kStepKeys == 0 && HSTU_INVARIANT_CHUNK_KEYS <= kMaxChunkKeys,
+                "invariant chunks are whole steps");
+  a.inv_steps = (d.flags & HSTU_FLAG_BATCH_INVARIANT) ? HSTU_INVARIANT_CHUNK_KEYS / kStepKeys : 0;
   return launch_kernel(prep_kernel, dim3(2 + nl + (d.total_new + kRowsPerWg - 1) / kRowsPerWg),
                        dim3(kPrepThreads), stream, ev, a);
 }

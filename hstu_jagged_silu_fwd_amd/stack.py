@@ -18,7 +18,11 @@ class HSTUStack:
                  num_pool_pages: int, max_pages_per_user: int, pos_buckets: int,
                  pos_mbits: int, attn_scale: float, norm_eps: float = 1e-6,
                  dtype: str = "bf16", ts_buckets: int = 0, ts_mbits: int = 0,
-                 num_layers: int = 1, device: str = "cuda", pool_fill: Optional[float] = None):
+                 num_layers: int = 1, device: str = "cuda", pool_fill: Optional[float] = None,
+                 batch_invariant: bool = False):
+        """batch_invariant: every call runs with FLAG_BATCH_INVARIANT (rows
+        bit-identical whatever the batch and however a user's sequence is
+        split into calls)."""
         self.B, self.H, self.d = num_users, num_heads, head_dim
         self.D = num_heads * head_dim
         self.ps, self.P, self.maxP = page_size, num_pool_pages, max_pages_per_user
@@ -29,7 +33,8 @@ class HSTUStack:
                            page_size=page_size, max_pages_per_user=max_pages_per_user,
                            num_pool_pages=num_pool_pages, pos_buckets=pos_buckets,
                            pos_mbits=pos_mbits, attn_scale=attn_scale, norm_eps=norm_eps,
-                           dtype=dtype, ts_buckets=ts_buckets, ts_mbits=ts_mbits)
+                           dtype=dtype, ts_buckets=ts_buckets, ts_mbits=ts_mbits,
+                           batch_invariant=batch_invariant)
         shape_k = (num_pool_pages, num_heads, page_size, head_dim)
         shape_v = (num_pool_pages, num_heads, head_dim, page_size)
         if pool_fill is None:

@@ -113,10 +113,28 @@ typedef struct {
   float attn_scale;            /* 1/N */
   float norm_eps;              /* LayerNorm epsilon (> 0) */
   int32_t dtype;               /* hstu_dtype */
+  int32_t flags;               /* 0 or HSTU_FLAG_BATCH_INVARIANT */
 } hstu_layer_desc;
 
+/* desc->flags bit: batch-invariant results.  Every output row (and every K/V
+ * row the call appends) is then bit-identical whatever else is in the batch
+ * and however the user's sequence was split into calls: a user's rows come
+ * out the same from a call with other users as from a call of its own, and
+ * the same from a call that reads their history from the cache as from one
+ * that recomputes the whole sequence (the cache-reuse property the NVIDIA
+ * blog's "Benefits" section rests on; without the flag both hold to the
+ * dtype's rounding).  The attention then cuts every user's keys at fixed
+ * positions (multiples of HSTU_INVARIANT_CHUNK_KEYS) and adds a row's pieces
+ * in one fixed order, and the row norm reduces a row in one fixed way; the
+ * price is work balance (fewer, fixed-size pieces) and, for long causal
+ * recomputes, more partial-sum traffic.  The workspace is sized for the
+ * flag (hstu_layer_workspace_size takes it into account). */
+#define HSTU_FLAG_BATCH_INVARIANT 1
+#define HSTU_INVARIANT_CHUNK_KEYS 256
+
 /* Bytes of device workspace hstu_layer_fwd needs for `desc` (depends only on
- * B, H, d, D, total_new and dtype).  Host-only; enqueues nothing. */
+ * B, H, d, D, total_new, dtype, max_pages_per_user * page_size and flags).
+ * Host-only; enqueues nothing. */
 hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc, size_t* bytes);
 
 /* One HSTU layer over a jagged batch of new rows (see the top of this file).

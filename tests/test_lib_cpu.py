@@ -2,6 +2,7 @@
 every function the header declares, sizes workspaces, and rejects bad
 descriptors before touching the device."""
 import ctypes
+import os
 
 import pytest
 
@@ -47,9 +48,54 @@ def test_exports_every_kvcache_header_function():
 
 
 def test_desc_struct_layout():
-    # int32 x6, int64, int32 x5, float x2, int32 -> 64 bytes with the int64 aligned at 24.
-    assert ctypes.sizeof(_lib.LayerDesc) == 64
+    # int32 x6, int64, int32 x5, float x2, int32 x2 -> 72 bytes with the int64 aligned at 24.
+    assert ctypes.sizeof(_lib.LayerDesc) == 72
     assert _lib.LayerDesc.num_pool_pages.offset == 24
+    assert _lib.LayerDesc.flags.offset == 64
+
+
+def test_desc_struct_matches_the_header(tmp_path):
+    """The ctypes mirror against the C compiler's own layout of the header's
+    struct: size and every field's offset."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in _lib.LayerDesc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"hstu.h\"\nint main(void) {\n"
+                   '  printf("%zu\\n", sizeof(hstu_layer_desc));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(hstu_layer_desc, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.dirname(_lib.HEADER_PATH), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(_lib.LayerDesc)
+    assert got[1:] == [getattr(_lib.LayerDesc, f).offset for f in fields]
+    assert _lib.FLAG_BATCH_INVARIANT == 1 and _lib.INVARIANT_CHUNK_KEYS == 256
+    hdr = open(_lib.HEADER_PATH).read()
+    assert "#define HSTU_FLAG_BATCH_INVARIANT 1" in hdr and "#define HSTU_INVARIANT_CHUNK_KEYS 256" in hdr
+
+
+@pytest.mark.parametrize("flags", [2, 3, -1])
+def test_unknown_flag_bits_are_rejected(flags):
+    d = desc()
+    d.flags = flags
+    with pytest.raises(hs.HSTUError) as ei:
+        hs.workspace_size(d)
+    assert ei.value.code == -1
+
+
+def test_batch_invariant_workspace_holds_its_fixed_chunks():
+    """The invariant split has ceil(max_len / 256) pieces per (q-block, head):
+    its workspace is at least that many 256-row fp32 partial blocks."""
+    plain = hs.workspace_size(desc())
+    inv = hs.workspace_size(desc(batch_invariant=True))
+    assert inv >= plain
+    nqb_cap = (1000 + 255) // 256 + 8
+    per_entry = (136 * 32 + 255) // 256
+    assert inv >= 4 * nqb_cap * per_entry * 256 * 128 * 4
 
 
 def test_workspace_size_grows_with_rows():

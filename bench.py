@@ -220,7 +220,9 @@ class Bench:
                       ts=torch.from_numpy(wl.ts_flat()).to(dev) if has_ts else None,
                       tso=torch.from_numpy(wl.ts_offsets()).to(dev) if has_ts else None,
                       desc=hs.make_desc(num_users=B, total_new=T, **common))
-            ws_bytes = max(ws_bytes, hs.workspace_size(io["desc"]), _lib.stack_workspace_size(io["desc"], self.L))
+            inv = hs.make_desc(num_users=B, total_new=T, batch_invariant=True, **common)
+            ws_bytes = max(ws_bytes, hs.workspace_size(io["desc"]), _lib.stack_workspace_size(io["desc"], self.L),
+                           _lib.stack_workspace_size(inv, self.L))   # room for the batch-invariant mode too
             self.inst.append(io)
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream().cuda_stream
@@ -871,6 +873,7 @@ def main():
         # the same users recomputed from scratch (nothing cached), against
         # the cached step of the same batch
         out["cache_speedup"] = {b.wl.name: cache_speedup(args, b)}
+        out["batch_invariant"] = invariant_cost(b, args.steps, args.warmup, m)
     if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
     if headline:
@@ -887,6 +890,22 @@ def main():
         out["cache_speedup"][bl.wl.name] = cache_speedup(args, bl)
         out["long_history"] = rec
     print(json.dumps(out), flush=True)
+
+
+def invariant_cost(b, steps, warmup, m):
+    """The same timed steps with the batch-invariant flag set on every call
+    (fixed 256-key attention pieces, one phase per item): its cost against
+    the default split."""
+    for io in b.inst:
+        io["desc"].flags = b._lib.FLAG_BATCH_INVARIANT
+    try:
+        mi = time_stack(b, steps, warmup, events=False)
+    finally:
+        for io in b.inst:
+            io["desc"].flags = 0
+    ms = 1e3 * mi["wall"] / steps
+    return dict(value=mi["tokens"] / mi["wall"], unit="new tokens/s", ms_per_step=ms,
+                slowdown=ms / (1e3 * m["wall"] / m["steps"]))
 
 
 def time_stack(b, steps, warmup, events=True):

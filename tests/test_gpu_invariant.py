@@ -5,7 +5,7 @@ the batch and however the user's sequence was split into calls.  The cache
 reuse of the NVIDIA blog's "Benefits" section (cached K/V reused, only the
 new tokens computed) then gives exactly the rows of a full recompute:
 
-* a two-layer stack over five ragged users, recomputed in one call, against
+* a two-layer stack over seven ragged users (one of them empty), recomputed in one call, against
   the same users fed in three incremental calls (history read from the
   pool, users with no rows in a call, a different batch in every call), for
   bf16 with the timestamp term and for fp32: every row of every layer equal
@@ -30,9 +30,12 @@ CASES = {
     "bf16-d128-ts": dict(dtype="bf16", H=2, d=128, ps=32, nb=64, mbits=3, tsb=32, tsm=2),
     "f32-d32": dict(dtype="f32", H=2, d=32, ps=16, nb=32, mbits=2, tsb=0, tsm=0),
 }
-LENS = np.array([700, 40, 1300, 257, 5, 0], np.int64)       # total positions per user
-CUTS = [np.array([300, 40, 513, 0, 2, 0]),                    # rows [cut_{k-1}, cut_k) in call k
-        np.array([650, 40, 1290, 256, 5, 0]),
+# Total positions per user.  The whole batch (4,402 rows) takes the large-M
+# projection tiles, the incremental calls and single users the persistent
+# small-M kernel, so the comparisons also hold across the two GEMM forms.
+LENS = np.array([700, 40, 1300, 257, 5, 0, 2100], np.int64)
+CUTS = [np.array([300, 40, 513, 0, 2, 0, 1000]),              # rows [cut_{k-1}, cut_k) in call k
+        np.array([650, 40, 1290, 256, 5, 0, 2050]),
         LENS]
 NL = 2
 

@@ -66,9 +66,7 @@ Layout make_layout(const hstu_layer_desc& d, int target, int nl = 1) {
   L.items = off;    off = align256(off + sizeof(AttnItem) * static_cast<size_t>(L.item_cap));
   L.q = off;        off = align256(off + es * T * d.hidden);
   L.u = off;        off = align256(off + es * T * d.hidden);
-  // partial outputs: fp16 for bf16 layers, fp32 for fp32 layers
-  L.part = off;     off = align256(off + (d.dtype == HSTU_BF16 ? 2 : 4) * static_cast<size_t>(L.item_cap) * kQB *
-                                               d.head_dim);
+  L.part = off;     off = align256(off + 4 * static_cast<size_t>(L.item_cap) * kQB * d.head_dim);
   L.tables = off;   off = align256(off + 4 * static_cast<size_t>(kTabFloats) * nl);
   L.total = off;
   return L;
@@ -86,7 +84,7 @@ WsPtrs ws_ptrs(void* base, const Layout& L) {
   w.items = reinterpret_cast<AttnItem*>(b + L.items);
   w.q = b + L.q;
   w.u = b + L.u;
-  w.part = b + L.part;
+  w.part = reinterpret_cast<float*>(b + L.part);
   w.tables = reinterpret_cast<float*>(b + L.tables);
   return w;
 }

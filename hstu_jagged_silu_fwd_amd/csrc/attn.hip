@@ -41,7 +41,7 @@
 // tables here are scaled the same way, so S' = -log2(e) * s and
 //   SiLU(s) = s / (1 + e^-s) = -ln(2) * S' / (1 + 2^S'),
 // i.e. exp2, add, reciprocal, multiply per score.  The constant -ln(2) is
-// applied with the 1/N scale when the partial outputs are stored.
+// applied with the 1/N scale by the norm kernel.
 //
 // Bias: the layer's tables (built once per call by prep, see kTabFloats) are
 // copied into LDS by direct-to-LDS loads at the workgroup's start.  The
@@ -64,8 +64,7 @@
 // or past cs is kept only on the diagonal).  Rows before cs see nothing past
 // cs anyway, so one mask covers every row.
 //
-// Partial outputs go to the workspace, already scaled by attn_scale * -ln(2)
-// (fp16 for bf16 layers, fp32 for fp32 layers); the chunks of a row are added
+// Partial outputs (fp32) go to the workspace; the chunks of a row are added
 // by the norm kernel (no softmax, so partial sums over key ranges simply
 // add).  The grid is persistent, one workgroup per CU: workgroup i takes
 // item i first and, when there are more items than workgroups, fetches
@@ -92,8 +91,7 @@ struct AttnArgs {
   const int32_t* ncand;      // per-user candidate counts, or null
   WsHeader* hdr;
   const AttnItem* items;
-  Part<T>* part;             // [items][kQB][HD] this item's rows, scaled by `scale`
-  float scale;               // attn_scale * -ln(2) (the products are in the exponent domain)
+  float* part;
   int H, D, ps_shift, maxP, nb, mbits, ntsb, tsmbits;
   int pmax;                  // 1: one phase per item (batch-invariant calls), else 2
 };
@@ -641,20 +639,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
       for (int i = 0; i < kGpw; ++i) {
         const int row = 16 * (gi0 + i) + l16;          // row inside the q-block
         if (i < ng_w && q0 + row < n) {
-          Part<T>* dst = a.part + (static_cast<size_t>(it) * kQB + row) * HD + 4 * g;
+          float* dst = a.part + (static_cast<size_t>(it) * kQB + row) * HD + 4 * g;
 #pragma unroll
-          for (int ob = 0; ob < NO; ++ob) {
-            f32x4 v = o[i][ob] * a.scale;
-            if constexpr (std::is_same<Part<T>, float>::value) {
-              *reinterpret_cast<f32x4*>(dst + ob * 16) = v;
-            } else {
-              // (round to nearest; a scaled partial beyond fp16's range
-              // becomes inf, so the row's output turns non-finite rather
-              // than silently wrong)
-              typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-              *reinterpret_cast<f16x4*>(dst + ob * 16) = __builtin_convertvector(v, f16x4);
-            }
-          }
+          for (int ob = 0; ob < NO; ++ob) *reinterpret_cast<f32x4*>(dst + ob * 16) = o[i][ob];
         }
       }
     }
@@ -680,8 +667,7 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.ncand = ncand;
   a.hdr = ws.hdr;
   a.items = ws.items;
-  a.part = static_cast<Part<T>*>(ws.part);
-  a.scale = d.attn_scale * kNegLn2;
+  a.part = ws.part;
   a.H = d.num_heads;
   a.D = d.hidden;
   a.ps_shift = __builtin_ctz(static_cast<unsigned>(d.page_size));

@@ -54,13 +54,6 @@ constexpr float kMasked = 1e30f;
 // instruction e contracting over {8*g + e : g = 0..3} -- the same index set,
 // so both element types share every load and layout.
 // ---------------------------------------------------------------------------
-// Element type of the attention's per-chunk partial outputs: fp16 for bf16
-// layers (the partials carry the output scale, so they are O(1) and fp16's
-// 11-bit significand keeps them 8x finer than bf16), fp32 for fp32 layers.
-template <typename T> struct PartOf { typedef float type; };
-template <> struct PartOf<bf16> { typedef _Float16 type; };
-template <typename T> using Part = typename PartOf<T>::type;
-
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
 template <> struct Frag<float> { float v[8]; };
@@ -270,7 +263,7 @@ struct WsPtrs {
   AttnItem* items;           // [item_cap]
   void* q;                   // [T, D] dtype; reused for G after attention
   void* u;                   // [T, D] dtype
-  void* part;                // [item_cap, kQB, d] partial attention outputs (Part<T>, scaled)
+  float* part;               // [item_cap, kQB, d] fp32 partial attention outputs
   float* tables;             // [layers][kTabFloats] bias tables (see kTabFloats)
 };
 

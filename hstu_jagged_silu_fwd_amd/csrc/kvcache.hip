@@ -42,7 +42,9 @@ struct hstu_kvcache {
   std::vector<int64_t> slot_user;    // user id of each slot (-1: free)
   std::vector<int32_t> slot_len;     // cached tokens
   std::vector<int32_t> slot_npages;  // pages held per layer
-  std::vector<int32_t> pages;        // [max_users][L][maxP] page ids (host mirror of the directory)
+  // page ids, [max_users][maxP][L]: the host mirror of the directory, with
+  // a user's layers side by side so that a plan touches few memory pages
+  std::vector<int32_t> pages;
   std::vector<int32_t> prev, next;   // recency list over GPU-cached slots
   int32_t mru = -1, lru = -1;
   std::unordered_map<int64_t, int32_t> index;
@@ -54,8 +56,8 @@ struct hstu_kvcache {
   std::list<int64_t> host_order;     // front = most recent
   std::vector<int32_t> host_free;
 
-  int32_t* row(int32_t slot, int32_t layer) {
-    return pages.data() + (static_cast<size_t>(slot) * L + layer) * maxP;
+  int32_t& page(int32_t slot, int32_t layer, int32_t i) {
+    return pages[(static_cast<size_t>(slot) * maxP + i) * L + layer];
   }
   void unlink(int32_t s) {
     if (prev[s] >= 0) next[prev[s]] = next[s]; else if (mru == s) mru = next[s];
@@ -71,10 +73,8 @@ struct hstu_kvcache {
   }
   // frees a GPU-cached user's pages and slot (its data is gone or offloaded)
   void release_slot(int32_t s) {
-    for (int32_t l = 0; l < L; ++l) {
-      const int32_t* r = row(s, l);
-      for (int32_t i = 0; i < slot_npages[s]; ++i) free_pages.push_back(r[i]);
-    }
+    for (int32_t l = 0; l < L; ++l)                // layer by layer, in page-index order
+      for (int32_t i = 0; i < slot_npages[s]; ++i) free_pages.push_back(page(s, l, i));
     held -= static_cast<int64_t>(L) * slot_npages[s];
     index.erase(slot_user[s]);
     unlink(s);
@@ -307,12 +307,11 @@ hstu_kv_status hstu_kvcache_plan(hstu_kvcache* c, int32_t B, const int64_t* user
         e.npages = c->slot_npages[victim];
         e.pages.reserve(static_cast<size_t>(vp));
         for (int32_t l = 0; l < c->L; ++l) {
-          const int32_t* r = c->row(victim, l);
           for (int32_t i = 0; i < e.npages; ++i) {
             const int32_t hp = c->host_free.back();
             c->host_free.pop_back();
             e.pages.push_back(hp);
-            copies[nc++] = hstu_kv_copy{0, r[i], hp, 0};
+            copies[nc++] = hstu_kv_copy{0, c->page(victim, l, i), hp, 0};
           }
         }
         c->host_order.push_front(uid);
@@ -326,8 +325,12 @@ hstu_kv_status hstu_kvcache_plan(hstu_kvcache* c, int32_t B, const int64_t* user
   *n_evicted = std::min(ne, evicted_cap);
 
   // 4. slots and pages, in batch order; host hits come back by onboard copies
+  //    (pages come off the top of the free stack, the top first; the stack
+  //    is cut back once at the end)
   int32_t nu = 0;
   std::vector<int64_t> to_free;
+  const int32_t* fp = c->free_pages.data();
+  size_t top = c->free_pages.size();
   for (int32_t b = 0; b < B; ++b) {
     int32_t s = bslot[b];
     const HostUser* hu = nullptr;
@@ -341,16 +344,18 @@ hstu_kv_status hstu_kvcache_plan(hstu_kvcache* c, int32_t B, const int64_t* user
       if (from_host[b]) hu = &c->host.find(user_ids[b])->second;
     }
     const int32_t held = c->slot_npages[s];
+    const int32_t nb = need[b];
     for (int32_t l = 0; l < c->L; ++l) {
-      int32_t* r = c->row(s, l);
-      for (int32_t i = held; i < held + need[b]; ++i) {
-        const int32_t p = c->free_pages.back();
-        c->free_pages.pop_back();
-        r[i] = p;
-        updates[nu++] = hstu_kv_update{s, l, i, p};
-        if (hu != nullptr && i < hu->npages)
-          copies[nc++] = hstu_kv_copy{1, p, hu->pages[static_cast<size_t>(l) * hu->npages + i], 0};
+      hstu_kv_update* u = updates + nu;
+      for (int32_t k = 0; k < nb; ++k) {
+        const int32_t pg = fp[--top];
+        c->page(s, l, held + k) = pg;
+        u[k] = hstu_kv_update{s, l, held + k, pg};
       }
+      nu += nb;
+      if (hu != nullptr)
+        for (int32_t i = held; i < std::min(held + nb, hu->npages); ++i)
+          copies[nc++] = hstu_kv_copy{1, c->page(s, l, i), hu->pages[static_cast<size_t>(l) * hu->npages + i], 0};
     }
     if (hu != nullptr) to_free.push_back(user_ids[b]);
     c->slot_npages[s] = held + need[b];
@@ -360,6 +365,7 @@ hstu_kv_status hstu_kvcache_plan(hstu_kvcache* c, int32_t B, const int64_t* user
     slots[b] = s;
     bslot[b] = s;
   }
+  c->free_pages.resize(top);
   for (int64_t uid : to_free) c->drop_host(uid);
   *n_updates = nu;
   *n_copies = nc;
@@ -425,10 +431,8 @@ hstu_kv_status hstu_kvcache_trim(hstu_kvcache* c, int32_t B, const int64_t* user
     const int32_t s = c->index.find(user_ids[b])->second;
     c->slot_len[s] -= n_drop[b];
     const int32_t keep = pages_for(c->slot_len[s], c->ps);
-    for (int32_t l = 0; l < c->L; ++l) {
-      const int32_t* r = c->row(s, l);
-      for (int32_t i = keep; i < c->slot_npages[s]; ++i) c->free_pages.push_back(r[i]);
-    }
+    for (int32_t l = 0; l < c->L; ++l)
+      for (int32_t i = keep; i < c->slot_npages[s]; ++i) c->free_pages.push_back(c->page(s, l, i));
     c->held -= static_cast<int64_t>(c->L) * (c->slot_npages[s] - keep);
     c->slot_npages[s] = keep;
   }

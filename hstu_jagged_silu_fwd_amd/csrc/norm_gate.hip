@@ -1,5 +1,5 @@
-// Row norm and gating: O = sum of the row's chunk partials, in chunk order
-// (the attention stores them already scaled by attn_scale), then
+// Row norm and gating: O = attn_scale * (sum of the row's chunk partials, in
+// chunk order; the partials hold -log2(e) * sum SiLU(s) v, undone here), then
 // G = LayerNorm_row(O) * U, the elementwise gating that precedes the output
 // projection (aitrends.kr article 100093, "HSTU sequential modelling").
 // Population variance over the row's D entries, no affine.  G overwrites the
@@ -27,11 +27,11 @@ struct NormArgs {
   const int32_t* qb_nch;            // [entries] key chunks
   const int32_t* qb_row0;           // [entries] first jagged row
   const int32_t* qb_rows;           // [entries] rows
-  const Part<T>* part;              // [items][kQB][hd], scaled
+  const float* part;                // [items][kQB][hd]
   const T* u;                       // [T][D]
   T* g;                             // [T][D]
   int D, hd;
-  float eps;
+  float scale, eps;
 };
 
 template <typename T>
@@ -63,13 +63,6 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, const float* x) {
   *reinterpret_cast<bf16x4*>(p) = v;
 }
 
-// Four consecutive partial-output elements as fp32.
-__device__ __forceinline__ f32x4 load_part4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 load_part4(const _Float16* p) {
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-  return __builtin_convertvector(*reinterpret_cast<const f16x4*>(p), f32x4);
-}
-
 // TPR: threads per row; MAXNG: (4 * TPR)-column groups per row at most.
 template <typename T, int TPR, int MAXNG>
 __global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
@@ -96,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
   const int r = row0 + min(rib, rows - 1);
   const int NG = D / GW;
   float x[MAXNG][4], uu[MAXNG][4];
-  const Part<T>* psrc[MAXNG];
+  const float* psrc[MAXNG];
 #pragma unroll
   for (int gi = 0; gi < MAXNG; ++gi) {
     const int col = min(gi, NG - 1) * GW + 4 * sub;          // a valid column for every gi
@@ -117,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
     for (int c = 0; c < CU; ++c)
 #pragma unroll
       for (int gi = 0; gi < MAXNG; ++gi)
-        v[c][gi] = load_part4(psrc[gi] + min(kc0 + c, nch - 1) * stride);
+        v[c][gi] = *reinterpret_cast<const f32x4*>(psrc[gi] + min(kc0 + c, nch - 1) * stride);
     // keep the scheduler from interleaving the adds with the loads (it would
     // otherwise wait for each load before issuing the next)
     __builtin_amdgcn_sched_barrier(0);
@@ -136,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void norm_gate_kernel(NormArgs<T> a) {
   for (int gi = 0; gi < MAXNG; ++gi)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[gi][j] = gi < NG ? x[gi][j] : 0.f;
+      x[gi][j] = gi < NG ? x[gi][j] * a.scale : 0.f;
       s1 += x[gi][j];
     }
 #pragma unroll
@@ -175,11 +168,12 @@ hipError_t norm_t(const hstu_layer_desc& d, const WsPtrs& ws, int nqb_cap, hipSt
   a.qb_nch = ws.qb_nch;
   a.qb_row0 = ws.qb_row0;
   a.qb_rows = ws.qb_rows;
-  a.part = static_cast<const Part<T>*>(ws.part);
+  a.part = ws.part;
   a.u = static_cast<const T*>(ws.u);
   a.g = static_cast<T*>(ws.q);
   a.D = d.hidden;
   a.hd = d.head_dim;
+  a.scale = d.attn_scale * kNegLn2;   // the attention accumulates -log2(e) * SiLU
   a.eps = d.norm_eps;
   constexpr int kRows = kThreads / TPR;
   return launch_kernel(norm_gate_kernel<T, TPR, MAXNG>, dim3(static_cast<unsigned>(nqb_cap) * (kQB / kRows)),

@@ -98,8 +98,13 @@ class KVCache:
             raise KVCacheError("hstu_kvcache_create", -1)
         self.h = P(h)
         self._dir = None
+        self._bufs = {}           # reusable plan output buffers (see _scratch)
+        self._counts = (I32(0), I32(0), I32(0))
         self._pinned = None       # reused pinned host staging buffer for updates and slots
+        self._staged = None       # event after the last copy out of it
+        self._dstage = None       # device side of those copies
         self._cpinned = None      # the same for page copies
+        self._cstaged = None
         self.host_k = self.host_v = None
 
     def close(self) -> None:
@@ -124,25 +129,37 @@ class KVCache:
             raise KVCacheError("hstu_kvcache_lookup", rc)
         return (out, tier) if with_tier else out
 
+    def _scratch(self, name: str, rows: int, cols: int, dtype):
+        """A reusable host array of at least `rows` rows and its address
+        (numpy's .ctypes accessor costs tens of microseconds per call, so
+        the plan's output buffers are made once and their addresses kept)."""
+        a = self._bufs.get(name)
+        if a is None or a[0].shape[0] < rows:
+            arr = np.empty((max(rows, 1), cols) if cols else max(rows, 1), dtype=dtype)
+            a = self._bufs[name] = (arr, arr.__array_interface__["data"][0])
+        return a
+
     def plan(self, user_ids: Sequence[int], n_new: Sequence[int]) -> Plan:
         ids = np.ascontiguousarray(user_ids, dtype=np.int64)
         n = np.ascontiguousarray(n_new, dtype=np.int32)
         if ids.shape != n.shape or ids.ndim != 1:
             raise KVCacheError("plan", -1)
         B = ids.shape[0]
-        cached = np.maximum(self.lookup(ids), 0).astype(np.int64)
-        cap = int(self.L * np.sum((cached + np.maximum(n, 0) + self.ps - 1) // self.ps))
-        upd = np.empty((max(cap, 1), 4), dtype=np.int32)
-        ev = np.empty(max(self.max_users, 1), dtype=np.int64)
+        # every user holds at most max_pages pages per layer: a buffer of
+        # L * B * max_pages records always suffices (only the records written
+        # are ever touched), so no lookup is needed to size it
+        cap = self.L * B * self.maxP
+        upd, upd_p = self._scratch("upd", cap, 4, np.int32)
+        ev, ev_p = self._scratch("ev", self.max_users, 0, np.int64)
         ccap = 2 * self.P if self.PH > 0 else 0
-        cps = np.empty((max(ccap, 1), 4), dtype=np.int32)
+        cps, cps_p = self._scratch("cps", ccap, 4, np.int32)
         hist = np.empty(B, dtype=np.int32)
         slots = np.empty(B, dtype=np.int32)
-        nu, ne, nc = I32(0), I32(0), I32(0)
-        rc = self.lib.hstu_kvcache_plan(self.h, B, _np_ptr(ids), _np_ptr(n), _np_ptr(hist), _np_ptr(slots),
-                                        upd.ctypes.data_as(P), cap, ctypes.byref(nu), ev.ctypes.data_as(P),
-                                        ev.shape[0], ctypes.byref(ne), cps.ctypes.data_as(P), ccap,
-                                        ctypes.byref(nc))
+        addr = lambda a: a.__array_interface__["data"][0] if a.size else None
+        nu, ne, nc = self._counts
+        rc = self.lib.hstu_kvcache_plan(self.h, B, addr(ids), addr(n), addr(hist), addr(slots),
+                                        upd_p, cap, ctypes.byref(nu), ev_p, self.max_users, ctypes.byref(ne),
+                                        cps_p, ccap, ctypes.byref(nc))
         if rc != 0:
             raise KVCacheError("hstu_kvcache_plan", rc)
         return Plan(hist, slots, upd[:nu.value].copy(), ev[:ne.value].tolist(), cps[:nc.value].copy())
@@ -199,14 +216,14 @@ class KVCache:
         hk, hv = self.host_tier(tuple(k_pool.shape[1:]), tuple(v_pool.shape[1:]), k_pool.dtype)
         need = 4 * m
         if self._cpinned is None or self._cpinned.numel() < need:
-            self._cpinned = torch.empty(max(need, 1024) * 2, dtype=torch.int32, pin_memory=True)
-            self._cstaged = None
-        if getattr(self, "_cstaged", None) is not None:
-            self._cstaged.synchronize()
+            # a plan reports at most 2 * num_pages copies: sized once
+            self._cpinned = torch.empty(max(need, 8 * self.P, 1024), dtype=torch.int32, pin_memory=True)
+        if self._cstaged is None:
+            self._cstaged = torch.cuda.Event()
+        self._cstaged.synchronize()
         host = self._cpinned[:need]
         host.numpy()[:] = plan.copies.reshape(-1)
         dev = host.to(device=k_pool.device, non_blocking=True)
-        self._cstaged = torch.cuda.Event()
         self._cstaged.record()
         pbk = k_pool[0].numel() * k_pool.element_size()
         pbv = v_pool[0].numel() * v_pool.element_size()
@@ -237,19 +254,29 @@ class KVCache:
         d = self.directory(device)
         B = plan.slots.shape[0]
         nu = plan.updates.shape[0]
-        # updates and slots travel in one copy from a pinned staging buffer
+        # updates and slots travel in one copy from a pinned staging buffer,
+        # sized once for the most records a batch of B users can produce
+        # (pinned allocations are slow: growing it batch by batch cost more
+        # than the whole build)
         need = 4 * nu + B
         if self._pinned is None or self._pinned.numel() < need:
-            self._pinned = torch.empty(max(need, 1024) * 2, dtype=torch.int32, pin_memory=True)
-            self._staged = None
-        if getattr(self, "_staged", None) is not None:
-            self._staged.synchronize()              # the previous copy out of the buffer is done
+            worst = 4 * self.L * B * self.maxP + B
+            self._pinned = torch.empty(max(need, worst, 1024), dtype=torch.int32, pin_memory=True)
+        if self._staged is None:
+            self._staged = torch.cuda.Event()       # one event, re-recorded (creating one per call
+                                                    # now and then costs tens of microseconds)
+        self._staged.synchronize()                  # the previous build is done with both staging
+                                                    # buffers (on whichever stream it ran)
         host = self._pinned[:need]
         host[:4 * nu].numpy()[:] = plan.updates.reshape(-1)
         host[4 * nu:].numpy()[:] = plan.slots
-        dev = host.to(device=d.device, non_blocking=True)
-        self._staged = torch.cuda.Event()
-        self._staged.record()
+        # ... into a device buffer of the same size, kept (a fresh one of the
+        # batch's size each time sends the caching allocator to the driver
+        # now and then for a new segment)
+        if self._dstage is None or self._dstage.numel() < self._pinned.numel():
+            self._dstage = torch.empty(self._pinned.numel(), dtype=torch.int32, device=d.device)
+        dev = self._dstage[:need]
+        dev.copy_(host, non_blocking=True)
         upd = dev[:4 * nu]
         slots = dev[4 * nu:]
         tables = torch.empty((self.L, B, self.maxP), dtype=torch.int32, device=d.device)
@@ -260,4 +287,5 @@ class KVCache:
                                            P(tables.data_ptr()) if B else None, st)
         if rc != 0:
             raise KVCacheError("hstu_kv_tables_build", rc)
+        self._staged.record()
         return tables

@@ -79,11 +79,7 @@ typedef enum {
 
 typedef enum {
   HSTU_F32 = 0,   /* fp32 storage and fp32 arithmetic */
-  HSTU_BF16 = 1   /* bf16 storage, fp32 accumulation and score math; the
-                     attention's per-piece partial sums of a row (already
-                     multiplied by attn_scale) pass through the workspace as
-                     fp16, so each must stay below 65504 in magnitude (a
-                     larger one turns the row non-finite) */
+  HSTU_BF16 = 1   /* bf16 storage, fp32 accumulation and score math */
 } hstu_dtype;
 
 /* Codes written to the device status word. */

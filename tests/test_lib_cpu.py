@@ -89,14 +89,13 @@ def test_unknown_flag_bits_are_rejected(flags):
 
 def test_batch_invariant_workspace_holds_its_fixed_chunks():
     """The invariant split has ceil(max_len / 256) pieces per (q-block, head):
-    its workspace is at least that many 256-row partial blocks (fp16 for a
-    bf16 layer)."""
+    its workspace is at least that many 256-row fp32 partial blocks."""
     plain = hs.workspace_size(desc())
     inv = hs.workspace_size(desc(batch_invariant=True))
     assert inv >= plain
     nqb_cap = (1000 + 255) // 256 + 8
     per_entry = (136 * 32 + 255) // 256
-    assert inv >= 4 * nqb_cap * per_entry * 256 * 128 * 2
+    assert inv >= 4 * nqb_cap * per_entry * 256 * 128 * 4
     assert hs.workspace_size(desc(dtype="f32", batch_invariant=True)) >= 4 * nqb_cap * per_entry * 256 * 128 * 4
 
 

@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sv[b][r] += s_tb[bucket64(tq[i] - tk[4 * b + r], a.tsmbits, a.ntsb)];
+          for (int r = 0; r < 4; ++r) sv[b][r] += s_tb[bucket64_fast(tq[i] - tk[4 * b + r], a.tsmbits, a.ntsb)];
       }
       // The causal mask is in the bias already (negative distances read the
       // table's masked padding).  Keys at or past the candidates: element e

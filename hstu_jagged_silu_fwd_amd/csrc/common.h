@@ -149,6 +149,24 @@ __device__ __forceinline__ int bucket64(int64_t delta, int m, int nb) {
   return b < nb - 1 ? static_cast<int>(b) : nb - 1;
 }
 
+// bucket64 with the common case, 0 <= delta < 2^32, in 32-bit arithmetic:
+// with e = floor(log2 d) and t = d >> (e - m) (the top m + 1 bits, leading
+// one included), the rule's (e - m + 1) * 2^m + t - 2^m is (e - m) * 2^m + t.
+// Other deltas (negative, or 2^32 and beyond) take bucket64 itself.
+__device__ __forceinline__ int bucket64_fast(int64_t delta, int m, int nb) {
+  const uint32_t hi = static_cast<uint32_t>(static_cast<uint64_t>(delta) >> 32);
+  if (__builtin_expect(hi != 0u, 0)) return bucket64(delta, m, nb);
+  const uint32_t d = static_cast<uint32_t>(delta);
+  int b;
+  if (d < (1u << m)) {
+    b = static_cast<int>(d);
+  } else {
+    const int sh = 31 - __clz(d) - m;
+    b = (sh << m) + static_cast<int>(d >> sh);
+  }
+  return b < nb - 1 ? b : nb - 1;
+}
+
 // ---------------------------------------------------------------------------
 // Direct global -> LDS loads.  __builtin_amdgcn_global_load_lds(src, dst, 16,
 // 0, 0) copies 16 bytes per lane: lane l's bytes land at dst + 16 * l (dst is

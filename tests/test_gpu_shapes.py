@@ -146,3 +146,30 @@ def test_stack_other_shapes(dtype, d, ps, H):
                                 wl.pos_mbits)
     for l in range(wl.layers):
         tol_check(to_np(ys[l]), refs[l], dtype, f"stack {dtype} d={d} ps={ps} layer {l}")
+
+
+# Timestamp deltas across every branch of the bucket rule: epoch-millisecond
+# values, gaps from one to billions (pairs 2^32 and more apart) and steps
+# back in time (negative deltas, bucket 0); m = 0 and m = 3 keep buckets of
+# deltas past 2^32 below the last bucket, so those are checked exactly.
+@pytest.mark.parametrize("mbits,nb", [(0, 64), (3, 1024)])
+def test_timestamp_deltas_of_every_range(mbits, nb):
+    print(f"case timestamps wide m={mbits} nb={nb}", flush=True)
+    hist, new = [0, 40, 700, 3], [90, 60, 120, 200]
+    over = dict(dtype="bf16", D=256, H=2, d=128, page_size=32, B=len(hist), layers=1,
+                hist=("fixed", hist), new=("fixed", new), pool_pages=4096, ts_buckets=nb, ts_mbits=mbits)
+    wl = make_workload(B8_KV_HIT, seed=11, **over)
+    rng = np.random.default_rng(11)
+    ts = []
+    for u in range(wl.B):
+        n = int(wl.hist_len[u] + wl.new_len[u])
+        kind = rng.integers(0, 4, n)
+        gap = np.where(kind == 0, rng.integers(1, 10, n),
+              np.where(kind == 1, rng.integers(1_000, 1_000_000, n),
+              np.where(kind == 2, rng.integers(1_000_000_000, 6_000_000_000, n),
+                       -rng.integers(1, 100_000, n))))
+        ts.append((1_700_000_000_000 + np.cumsum(gap)).astype(np.int64))
+    wl.timestamps = ts
+    d = np.concatenate([t[:, None] - t[None, :] for t in ts if len(t)], axis=None)
+    assert (d < 0).any() and (d >= 2**32).any() and ((d > 0) & (d < 8)).any()
+    _check_layer(wl, {"ts": True}, f"timestamps m={mbits} nb={nb}")

@@ -104,14 +104,21 @@ __device__ __forceinline__ int bucket_start(int b, int m) {
   return (s + r) << (q - 1);
 }
 
-constexpr int kWaves = 8;          // waves per workgroup
-constexpr int kGpw = 2;            // 16-query groups per wave (an adjacent pair)
-static_assert(kQB == 16 * kWaves * kGpw, "a q-block is two groups per wave");
+// Wave layouts of a workgroup (a q-block is 256 rows either way):
+//   8 waves of an adjacent pair of 16-query groups each: two waves per SIMD,
+//     each K/V^T fragment read feeds two groups;
+//   16 waves of one group each (bf16 only, <= 128 registers): four waves per
+//     SIMD hide each other's LDS, matrix and transcendental latencies, at
+//     twice the fragment reads per group.
+// The host picks per call (launch_attn below).
 
 // Sizes of one ring stage (one 32-key step of K and V^T) for element type T
-// and head dim HD, and of the ring.
-template <typename T, int HD>
+// and head dim HD, and of the ring; WAVES is the layout.
+template <typename T, int HD, int WAVES>
 struct StepGeo {
+  static constexpr int kWaves = WAVES;
+  static constexpr int kGpw = kQB / (16 * WAVES);
+  static_assert(kQB == 16 * kWaves * kGpw && (kGpw == 1 || kGpw == 2), "a q-block is 256 rows");
   static constexpr int ES = static_cast<int>(sizeof(T));
   static constexpr int CE = 16 / ES;                   // elements per 16-byte chunk
   static constexpr int KCH = HD / CE;                  // chunks per K row
@@ -139,10 +146,14 @@ struct StepGeo {
   static_assert(NST * STAGE >= (PMAX - 1) * (kWaves / PMAX) * kGpw * 16 * HD * 4, "reduction fits the ring");
 };
 
-template <typename T, int HD, bool CAND, bool TS>
-__global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
-  using G = StepGeo<T, HD>;
+template <typename T, int HD, bool CAND, bool TS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attn_kernel(AttnArgs<T> a) {
+  using G = StepGeo<T, HD, WAVES>;
   constexpr int CE = G::CE, KCH = G::KCH, VCH = G::VCH, NST = G::NST, IPW = G::IPW;
+  constexpr int kWaves = G::kWaves, kGpw = G::kGpw;
+  // the two waves of a SIMD run half a step apart in the 8-wave layout (see
+  // the key loop); with four waves per SIMD every wave runs the plain order
+  constexpr bool kRot = kWaves == 8;
   constexpr int NT = 64 * kWaves;
   constexpr int NC = HD / 32;        // 32-wide slices of the head dim (contraction of S^T)
   constexpr int NO = HD / 16;        // 16-row blocks of O^T
@@ -235,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // that no SIMD holds two pairs while another holds a single group,
     // columns below WP/2 take groups in pairs from 0, and the others take
     // the remaining groups, in pairs only as far as needed.
-    const int NW = (ngroups + 1) >> 1;
+    const int NW = (ngroups + kGpw - 1) / kGpw;        // wave columns with groups
     // (Batch-invariant calls keep one phase: a row's steps are then added in
     // key order whatever its q-block holds.)
     const int P = (G::PMAX >= 2 && a.pmax >= 2 && 2 * NW <= kWaves) ? 2 : 1;
@@ -245,10 +256,15 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     const int M = P == 1 && NST >= 8 ? 2 : 1;
     const int RS = P * M;
     const int R = NST / RS;
-    const int half = kWaves / (2 * P);
+    [[maybe_unused]] const int half = kWaves / (2 * P);
     const int ph = w & (P - 1), col = w / P;
     int gi0, ng_w;                                     // this wave's first group and group count
-    if (col < half) {
+    if constexpr (kGpw == 1) {
+      // one group per column; column j's waves sit on SIMD j mod 4 (with two
+      // phases, the phases of a column on neighbouring SIMDs)
+      gi0 = col;
+      ng_w = col < ngroups ? 1 : 0;
+    } else if (col < half) {
       gi0 = 2 * col;
       ng_w = min(max(ngroups - gi0, 0), 2);
     } else {
@@ -526,7 +542,9 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
     // k-1 after barrier k, so the loads issued at barrier k (round k+R-2)
     // go into round k-2's stages: R-2 rounds are in flight ahead. ----
     auto key_loop = [&](auto ngc) __attribute__((always_inline)) {
-      const int D = R - 2;
+      // Without rotated waves every wave is done with round r-1 at barrier r,
+      // so the loads of round r+R-1 can go into its stages: R-1 rounds ahead.
+      const int D = kRot ? R - 2 : R - 1;
       for (int rr = 0; rr < min(D, nrounds); ++rr) issue_round(rr);
       for (int r = 0; r < nrounds; ++r) {
         // round r's loads have landed once only those issued after them remain
@@ -601,11 +619,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_kernel(AttnArgs<T> a) {
         }
       }
     };
-    if (w < 4) {
-      if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});
-      else if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
-      else key_loop(std::integral_constant<int, 0>{});
-    } else {
+    if (!kRot || w < 4) {
+      if constexpr (kGpw == 2) {
+        if (ng_w == 2) key_loop(std::integral_constant<int, 2>{});
+        else if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
+        else key_loop(std::integral_constant<int, 0>{});
+      } else {
+        if (ng_w == 1) key_loop(std::integral_constant<int, 1>{});
+        else key_loop(std::integral_constant<int, 0>{});
+      }
+    } else if constexpr (kRot) {
       if (ng_w == 2) key_loop_rot(std::integral_constant<int, 2>{});
       else if (ng_w == 1) key_loop_rot(std::integral_constant<int, 1>{});
       else key_loop_rot(std::integral_constant<int, 0>{});
@@ -677,12 +700,25 @@ hipError_t attn_t(const hstu_layer_desc& d, const int32_t* pt, const void* k_poo
   a.ntsb = d.ts_buckets;
   a.tsmbits = d.ts_mbits;
   a.pmax = (d.flags & HSTU_FLAG_BATCH_INVARIANT) ? 1 : 2;
-  const dim3 gr(grid), bl(64 * kWaves);
-  if (d.ts_buckets > 0)
-    return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, true>, gr, bl, stream, ev, a)
-                            : launch_kernel(attn_kernel<T, HD, false, true>, gr, bl, stream, ev, a);
-  return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, false>, gr, bl, stream, ev, a)
-                          : launch_kernel(attn_kernel<T, HD, false, false>, gr, bl, stream, ev, a);
+  const dim3 gr(grid);
+  auto go = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    const dim3 bl(64 * W);
+    if (d.ts_buckets > 0)
+      return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, true, W>, gr, bl, stream, ev, a)
+                              : launch_kernel(attn_kernel<T, HD, false, true, W>, gr, bl, stream, ev, a);
+    return ncand != nullptr ? launch_kernel(attn_kernel<T, HD, true, false, W>, gr, bl, stream, ev, a)
+                            : launch_kernel(attn_kernel<T, HD, false, false, W>, gr, bl, stream, ev, a);
+  };
+  // 16 waves of one group where each q-block has few groups to share a
+  // fragment read (short bursts of new rows: at most 96 per user on
+  // average) or the timestamp term adds vector work per score; 8 waves of
+  // pairs otherwise.  (fp32 fragments are twice as wide: 8 waves only.)
+  if constexpr (sizeof(T) == 2) {
+    const int64_t rows = d.total_new, users = d.num_users > 0 ? d.num_users : 1;
+    if (d.ts_buckets > 0 || rows <= 96 * users) return go(std::integral_constant<int, 16>{});
+  }
+  return go(std::integral_constant<int, 8>{});
 }
 
 template <typename T>

@@ -8,8 +8,8 @@ new tokens computed) then gives exactly the rows of a full recompute:
 * a two-layer stack over seven ragged users (one of them empty), recomputed in one call, against
   the same users fed in three incremental calls (history read from the
   pool, users with no rows in a call, a different batch in every call), for
-  bf16 with the timestamp term and for fp32: every row of every layer equal
-  bit for bit;
+  bf16 with and without the timestamp term and fp32: every row of every
+  layer equal bit for bit;
 * the same users one at a time against the batched call, bit for bit;
 * the invariant call against the oracle (layer 0), to the usual tolerance.
 
@@ -28,11 +28,14 @@ pytestmark = pytest.mark.gpu
 
 CASES = {
     "bf16-d128-ts": dict(dtype="bf16", H=2, d=128, ps=32, nb=64, mbits=3, tsb=32, tsm=2),
+    "bf16-d64": dict(dtype="bf16", H=4, d=64, ps=64, nb=64, mbits=3, tsb=0, tsm=0),
     "f32-d32": dict(dtype="f32", H=2, d=32, ps=16, nb=32, mbits=2, tsb=0, tsm=0),
 }
 # Total positions per user.  The whole batch (4,402 rows) takes the large-M
-# projection tiles, the incremental calls and single users the persistent
-# small-M kernel, so the comparisons also hold across the two GEMM forms.
+# projection tiles and, without timestamps, the 8-wave attention layout; the
+# incremental calls and single users take smaller tiles and, where a call
+# has at most 96 new rows per user, the 16-wave layout, so the comparisons
+# also hold across those forms.
 LENS = np.array([700, 40, 1300, 257, 5, 0, 2100], np.int64)
 CUTS = [np.array([300, 40, 513, 0, 2, 0, 1000]),              # rows [cut_{k-1}, cut_k) in call k
         np.array([650, 40, 1290, 256, 5, 0, 2050]),

@@ -173,3 +173,16 @@ def test_timestamp_deltas_of_every_range(mbits, nb):
     d = np.concatenate([t[:, None] - t[None, :] for t in ts if len(t)], axis=None)
     assert (d < 0).any() and (d >= 2**32).any() and ((d > 0) & (d < 8)).any()
     _check_layer(wl, {"ts": True}, f"timestamps m={mbits} nb={nb}")
+
+
+# Short bursts of new rows (at most 96 per user on average) take the 16-wave
+# attention layout (one query group per wave) in bf16; the grid above runs
+# the 8-wave layout. One user's 200 rows make a 13-group q-block (one
+# phase), the others two phases.
+@pytest.mark.parametrize("d,ps,H", [(32, 16, 6), (64, 64, 4), (128, 32, 4)])
+def test_sixteen_wave_layout(d, ps, H):
+    print(f"case 16-wave layout bf16 d={d} ps={ps} H={H}", flush=True)
+    hist, new = [0, 5, 333, 1000, 50, 1], [200, 17, 90, 64, 0, 3]
+    assert sum(new) <= 96 * len(new)
+    wl = _workload("bf16", d, ps, H, {}, seed=d + 1, hist=hist, new=new)
+    _check_layer(wl, {}, f"bf16 d={d} 16 waves")

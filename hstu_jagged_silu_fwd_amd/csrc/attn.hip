@@ -126,7 +126,10 @@ struct StepGeo {
   static constexpr int KBYTES = kStepKeys * HD * ES;   // the K rows of a step
   static constexpr int STAGE = 2 * KBYTES;             // K rows, then V^T rows
   static constexpr int NBLK = STAGE / 1024;            // 1 KiB loads per stage
-  static constexpr int IPW = (NBLK + kWaves - 1) / kWaves;   // loads per wave and stage (at most)
+  // waves that issue a stage's loads (the first kIssuers; the others only
+  // compute) and the loads each issues per stage (at most)
+  static constexpr int kIssuers = WAVES;
+  static constexpr int IPW = (NBLK + kIssuers - 1) / kIssuers;
   // ring: 8 stages, or as many as fit in 128 KiB (a power of two)
   static constexpr int NST_FIT = 131072 / STAGE;
   static constexpr int NST = NST_FIT >= 8 ? 8 : (NST_FIT >= 4 ? 4 : 2);
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_kernel(AttnArgs<T> a) {
     // own pages: in bounds; their K rows and V^T columns are zeroed in LDS
     // before the products and their scores masked.
     auto issue = [&](int s) __attribute__((always_inline)) {
+      if (my_cnt == 0) return;                         // uniform: a wave that only computes
       const int kb = k_lo + kStepKeys * s;
       unsigned char* stg = s_ring + (s % NST) * G::STAGE;
       const int pa = __builtin_amdgcn_readfirstlane(s_pages[(kb >> a.ps_shift) - pg0]);

@@ -16,13 +16,14 @@
 //   S^T [32 keys x 16 queries] = K * Q^T      (MFMA, 2 blocks over d, per half)
 //   online softmax in base 2 over the step's 64 keys (a lane holds 8
 //   consecutive keys of one query per half; the row maximum is reduced over
-//   the four lanes that share the query, once per step)
+//   the four lanes that share the query, once per step; O and the sum are
+//   rescaled only when a row's maximum grows by more than a set margin)
 //   O^T [d x 16] = alpha * O^T + V^T * P       (MFMA)
 // K rows feeding S^T block b are read in the order row m -> key 8*(m/4) +
 // 4*b + m%4, so a lane's score accumulators are exactly the keys of its
 // B-operand fragment for the value product (the scores stay in registers).
-// LDS rows are padded by 16 bytes, which spreads the 16 lanes of a fragment
-// read over distinct banks.  The chunk's unnormalised O, its running maximum
+// K rows keep their 16-byte chunks XOR-permuted by row (kmix) and V^T rows are
+// padded by 16 bytes, so the 16 lanes of a fragment read hit distinct banks.  The chunk's unnormalised O, its running maximum
 // and its sum go to the workspace (fp32).
 //
 // Kernel 2 gives one wave to each output row (request, beam, query head): it
@@ -43,6 +44,7 @@ constexpr int kBStep = 64;                   // keys per step (two 32-key halves
 constexpr int kCtxAlign = 32;                // max_ctx granularity: every 16-byte V^T load stays in the row
 constexpr int kCombineRows = 4;              // output rows (waves) per combine workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;                 // reference-maximum slack, log2 units (weights stay below 256)
 
 struct BeamArgs {
   const void* q;
@@ -65,11 +67,12 @@ template <typename T, int HD>
 struct BGeo {
   static constexpr int ES = static_cast<int>(sizeof(T));
   static constexpr int CE = 16 / ES;                  // elements per 16-byte chunk
-  static constexpr int KROW = HD * ES + 16;           // padded K row (bytes)
+  static constexpr int KCH = HD * ES / 16;            // chunks per K row
+  static constexpr int KROW = HD * ES;                // K row (bytes), chunks XOR-permuted (kswz)
+  static constexpr int KSH = KCH >= 16 ? 0 : 1;       // 1: 8-chunk rows
   static constexpr int VROW = kBStep * ES + 16;       // padded V^T row (bytes)
   static constexpr int KBYTES = kBStep * KROW;
   static constexpr int STAGE = KBYTES + HD * VROW;
-  static constexpr int KCH = HD * ES / 16;            // chunks per K row
   static constexpr int VCH = kBStep * ES / 16;        // chunks per V^T row
   static constexpr int NCHK = kBStep * KCH;
   static constexpr int NCH = NCHK + HD * VCH;
@@ -77,6 +80,16 @@ struct BGeo {
   static_assert(CPT >= 1 && CPT * kBThreads == NCH, "whole chunks per thread");
   static_assert(NCHK % kWave == 0, "a wave's chunk of a step is all K or all V^T");
 };
+
+// Chunk permutation of K rows in LDS: chunk p of row `row` is stored at
+// p ^ kswz(kmix(row)).  The 16 lanes of a fragment read take rows
+// 8*(l/4) + l%4 (+4, +32), whose kmix is exactly l.  Rows of 16 or more
+// chunks XOR with l itself; 8-chunk rows (two to a 256-byte line) with
+// (l & 7) ^ (l >> 3), which keeps the 16 lanes' reads on distinct banks both
+// when 8 lanes share a 128-byte pass and when 16 share a 256-byte one.
+__device__ __forceinline__ int kmix(int row) { return (row & 3) | (((row >> 3) & 3) << 2); }
+template <int KSH>
+__device__ __forceinline__ int kswz(int m) { return KSH == 0 ? m : ((m & 7) ^ (m >> 3)); }
 
 // Zeroes the elements at index >= nv of a 16-byte chunk.
 template <typename T>
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(kBThreads) void beam_ctx_kernel(BeamArgs a) {
       const int qi = tid + j * kBThreads;
       if (qi < G::NCHK) {
         const int row = qi / G::KCH, c = qi % G::KCH;
-        *reinterpret_cast<uint4*>(st + row * G::KROW + c * 16) = regs[j];
+        *reinterpret_cast<uint4*>(st + row * G::KROW + ((c ^ kswz<G::KSH>(kmix(row))) << 4)) = regs[j];
       } else {
         const int qv = qi - G::NCHK;
         const int e = qv / G::VCH, c = qv % G::VCH;
@@ -199,6 +212,7 @@ __global__ __launch_bounds__(kBThreads) void beam_ctx_kernel(BeamArgs a) {
     for (int ob = 0; ob < NO; ++ob) o[i][ob] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int krow0 = 8 * (l16 >> 2) + (l16 & 3);
+  const int ksw = kswz<G::KSH>(l16);                   // every K row this lane reads has kmix l16
 
   load_step(0);
   store_step(0);
@@ -216,8 +230,8 @@ __global__ __launch_bounds__(kBThreads) void beam_ctx_kernel(BeamArgs a) {
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
         const int chunk = (cc * 32 + 8 * gq) / G::CE;
-        read_frag(kf[cc][0], kp, chunk, 0);
-        read_frag(kf[cc][1], kp + 4 * G::KROW, chunk, 0);
+        read_frag(kf[cc][0], kp, chunk, ksw);
+        read_frag(kf[cc][1], kp + 4 * G::KROW, chunk, ksw);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -231,38 +245,61 @@ __global__ __launch_bounds__(kBThreads) void beam_ctx_kernel(BeamArgs a) {
       }
     }
     // online softmax over the step's 64 keys (half hf, element e: key
-    // kb + 32*hf + 8*gq + e); one maximum and one rescale per step
+    // kb + 32*hf + 8*gq + e), in base 2 with the scale folded into the
+    // exponent's multiply-add.  Each row keeps a reference maximum m that
+    // moves only when the step's maximum exceeds it by more than kLazy (so
+    // every weight stays below 2^kLazy): most steps then leave O and l
+    // unscaled, and the wave rescales only when one of its rows moved.  Only
+    // a chunk's last step can hold keys past its end, so only that step masks.
+    const bool full = kb + kBStep <= k_hi;             // uniform
     const int nvalid = k_hi - (kb + 8 * gq);
     Frag<T> pf[2][2];
+    float alpha[2];
+    bool grow = false;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       float p[2][8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[hf][e] = sc[i][hf][e >> 2][e & 3];
+      if (!full) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (32 * hf + e >= nvalid) p[hf][e] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[hf][e] = 32 * hf + e < nvalid ? sc[i][hf][e >> 2][e & 3] * a.scale2 : -INFINITY;
-          mx = fmaxf(mx, p[hf][e]);
-        }
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, p[hf][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(m[i], mx);              // finite: every step has a valid key
-      const float alpha = __builtin_amdgcn_exp2f(m[i] - mnew);
+      const float mc = mx * a.scale2;                  // finite: every step has a valid key
+      const bool gi = mc > m[i] + kLazy;               // always on the first step (m = -inf)
+      const float mref = gi ? mc : m[i];
+      alpha[i] = __builtin_amdgcn_exp2f(m[i] - mref);  // exactly 1 where the reference stays
+      grow |= gi;
       float ps = 0.f;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[hf][e] = __builtin_amdgcn_exp2f(p[hf][e] - mnew);
+          p[hf][e] = __builtin_amdgcn_exp2f(fmaf(p[hf][e], a.scale2, -mref));
           ps += p[hf][e];
         }
-      l[i] = l[i] * alpha + ps;
-      m[i] = mnew;
-#pragma unroll
-      for (int ob = 0; ob < NO; ++ob) o[i][ob] *= alpha;
+      l[i] = fmaf(l[i], alpha[i], ps);
+      m[i] = mref;
       set_frag(pf[i][0], p[0]);
       set_frag(pf[i][1], p[1]);
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ob = 0; ob < NO; ++ob) o[i][ob] *= alpha[i];
     }
     // O^T += V^T * P, half by half
 #pragma unroll

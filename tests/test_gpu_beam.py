@@ -126,3 +126,25 @@ def test_beam_decode_at_the_online_size_sampled_beams():
     sub = dict(c, q=c["q"][:, sel], bk=bk, bv=bv)
     ref = oracle(sub, path[:, sel], t, d ** -0.5)
     tol_check(got[:, sel], ref, "bf16", "beam full size sampled")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scores_that_grow_along_the_context(dtype):
+    """Context keys scaled by a ramp over their position, with a large
+    softmax scale: the rows' maxima climb by many units of log2 over the
+    chunk, by different amounts per row, so the kernel's running reference
+    maximum moves on some steps and rows and stays on others (weights up to
+    2^8 between moves); the result must not depend on when it moved."""
+    print(f"case beam growing scores {dtype}", flush=True)
+    R, W, Hq, Hkv, d, Cmax, t = 2, 24, 4, 2, 128, 1024, 1
+    c = make(15, R, W, Hq, Hkv, d, [1000, 333], Cmax, t + 1, dtype)
+    rnd = (lambda a: round_bf16(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32).astype(np.float64))
+    ramp = np.linspace(0.05, 3.0, Cmax)[None, None, :, None]
+    c["ck"] = rnd(c["ck"] * ramp)
+    path = c["rng"].integers(0, W, size=(R, W, t)).astype(np.int32)
+    scale = 0.35
+    out, code = run(c, path, t, dtype, scale)
+    assert code == 0
+    ref = oracle(c, path, t, scale)
+    assert np.all(np.isfinite(ref))
+    tol_check(out.float().cpu().numpy(), ref, dtype, f"beam growing scores {dtype}")

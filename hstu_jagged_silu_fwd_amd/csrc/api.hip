@@ -47,9 +47,12 @@ Layout make_layout(const hstu_layer_desc& d, int target, int nl = 1) {
   L.nqb_cap = static_cast<int>((T + kQB - 1) / kQB + B);
   // items <= total/chunk + H * entries, and total/chunk <= target unless the
   // chunk hits its cap, where it is <= H * entries * ceil(max_len / cap).
+  // When H * entries can reach the target, the work list rounds its target
+  // up to a multiple of it (at most one target more).
   const int64_t max_len = static_cast<int64_t>(d.max_pages_per_user) * d.page_size;
   const int64_t per_entry = 1 + (max_len + kMaxChunkKeys - 1) / kMaxChunkKeys;
-  int64_t cap = d.num_heads * L.nqb_cap * per_entry + target;
+  const int64_t heads_entries = static_cast<int64_t>(d.num_heads) * L.nqb_cap;
+  int64_t cap = heads_entries * per_entry + target + (heads_entries >= target ? target : 0);
   // batch-invariant calls cut an entry of k keys into ceil(k / chunk) pieces
   if (d.flags & HSTU_FLAG_BATCH_INVARIANT)
     cap = std::max<int64_t>(cap, d.num_heads * L.nqb_cap *

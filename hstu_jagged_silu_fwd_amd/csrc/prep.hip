@@ -71,6 +71,7 @@ struct PrepShared {
   int32_t qbn[kMaxQBlocks];        // chunks per q-block entry (steps | weight while searching)
   int32_t qbf[kMaxQBlocks];        // first work item of each q-block entry
   int32_t qbu[kMaxQBlocks];        // user of each q-block entry
+  int32_t ord[kMaxQBlocks];        // entries in work-list order (heavy entries first)
   int32_t pgp[kMaxUsers + 1];      // first flat page index of each user
   int32_t cnt[kPrepWaves][16];     // per-wave item counts of the candidate budgets
   float tpb[kMaxBuckets];          // a layer's scaled bucket tables (table workgroups)
@@ -433,19 +434,60 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
     const uint64_t fits = __ballot(j == lane && lane < kCand);
     const int jj = fits ? __builtin_ctzll(fits) : kCand - 1;
     const int budget = __shfl(bud, jj, kWave);       // lanes 0..15 hold the candidates in order
-    int64_t n_items = 0;
+    // Chunks per entry, and the order of the work list.  When the items
+    // outnumber the target (the workgroups; the rest are fetched by
+    // whichever workgroup finishes first) the entries go by the cost of one
+    // of their chunks, highest first, in 64 classes of budget / 64 (a
+    // counting sort; the order inside a class is whichever the LDS atomics
+    // give), so the cheapest chunks fill the end of the launch
+    // (longest-first scheduling); otherwise in entry order.  An entry's
+    // items stay together, heads then chunks, as the norm kernel reads
+    // them; which workgroup runs an item does not change its result.
+    // qbf ends up holding the first item of the k-th entry of the list.
+    static_assert(kPrepWaves * kCand == kWave, "one class counter per lane in cnt");
+    int* cls_n = &s.cnt[0][0];                       // 64 class counters (the search is done with cnt)
+    cls_n[lane] = 0;
+    int64_t all_items = 0;
     for (int e0 = 0; e0 < nqb; e0 += kWave) {
       const int e = e0 + lane;
-      int nch = 0;
+      int64_t ni = 0;
       if (e < nqb) {
         const int v = s.qbn[e];
-        const int L = a.inv_steps > 0 ? a.inv_steps : chunk_steps(budget, v >> kWShift);
-        nch = ((v & kStepMask) + L - 1) / L;
+        const int steps = v & kStepMask, wt = v >> kWShift;
+        const int L = a.inv_steps > 0 ? a.inv_steps : chunk_steps(budget, wt);
+        const int nch = (steps + L - 1) / L;
+        const int64_t cost = static_cast<int64_t>((steps + nch - 1) / nch) * wt;
+        const int cls = kWave - 1 - static_cast<int>(min<int64_t>(kWave - 1, cost * kWave / (budget + 1)));
         s.qbn[e] = nch;
+        s.qbf[e] = cls;                              // parked until the order is known
+        atomicAdd(&cls_n[cls], 1);
+        ni = static_cast<int64_t>(nch) * H;
       }
+      all_items += wave_sum(ni);
+    }
+    if (all_items > target) {
+      int tot;
+      const int start = wave_excl_scan(cls_n[lane], lane, &tot);   // class 0 (the costliest) first
+      cls_n[lane] = start;
+      for (int e0 = 0; e0 < nqb; e0 += kWave) {
+        const int e = e0 + lane;
+        if (e < nqb) s.ord[atomicAdd(&cls_n[s.qbf[e]], 1)] = e;
+      }
+    } else {
+      for (int e = lane; e < nqb; e += kWave) s.ord[e] = e;
+    }
+    int64_t n_items = 0;
+    for (int k0 = 0; k0 < nqb; k0 += kWave) {
+      const int k = k0 + lane;
+      const int e = k < nqb ? s.ord[k] : 0;
+      const int64_t ni = k < nqb ? static_cast<int64_t>(s.qbn[e]) * H : 0;
       int64_t tot;
-      const int64_t ex = n_items + wave_excl_scan(static_cast<int64_t>(nch) * H, lane, &tot);
-      if (e < nqb) s.qbf[e] = static_cast<int32_t>(min<int64_t>(ex, a.item_cap));
+      const int64_t ex = n_items + wave_excl_scan(ni, lane, &tot);
+      if (k < nqb) {
+        const int32_t first = static_cast<int32_t>(min<int64_t>(ex, a.item_cap));
+        s.qbf[k] = first;
+        a.ws.qb_first[e] = first;
+      }
       n_items += tot;
     }
     if (lane == 0) {
@@ -468,22 +510,23 @@ __device__ void work_list(const PrepArgs& a, PrepShared& s) {
 
   // 5. the work list (one thread per item) and the per-entry tables used by
   //    the norm kernel
-  for (int e = tid; e < nqb; e += kPrepThreads) {
+  for (int e = tid; e < nqb; e += kPrepThreads) {    // (qb_first is written with the order above)
     const int u = s.qbu[e], qb = e - s.qbb[u];
-    a.ws.qb_first[e] = s.qbf[e];
     a.ws.qb_nch[e] = s.qbn[e];
     a.ws.qb_row0[e] = s.off[u] + qb * kQB;
     a.ws.qb_rows[e] = min(kQB, s.off[u + 1] - s.off[u] - qb * kQB);
   }
   // thread t writes the contiguous items [t*m, (t+1)*m): one binary search
-  // for the entry of its first item, then a walk over the entries
+  // (over the list order, in which the entries' first items increase) for
+  // the entry of its first item, then a walk over the entries
   const int m = (n_items + kPrepThreads - 1) / kPrepThreads;
   const int i_beg = min(n_items, tid * m), i_end = min(n_items, i_beg + m);
-  int e = i_beg < i_end ? entry_user(s.qbf, nqb, i_beg) : 0;   // last entry whose first item <= i
+  int pos = i_beg < i_end ? entry_user(s.qbf, nqb, i_beg) : 0;   // last list position whose first item <= i
   for (int i = i_beg; i < i_end; ++i) {
-    while (e + 1 < nqb && s.qbf[e + 1] <= i) ++e;
+    while (pos + 1 < nqb && s.qbf[pos + 1] <= i) ++pos;
+    const int e = s.ord[pos];
     const int u = s.qbu[e], qb = e - s.qbb[u], nch = s.qbn[e];
-    const int r = i - s.qbf[e], h = r / nch, kc = r - h * nch;
+    const int r = i - s.qbf[pos], h = r / nch, kc = r - h * nch;
     const int n = s.off[u + 1] - s.off[u];
     const int c = s.hist[u];
     const int keys = c + min(n, (qb + 1) * kQB);

@@ -17,7 +17,11 @@ layers' kernels, synchronised on both sides), the attention kernel's roofline
 position (HBM-bound: algorithmic bytes / its mean duration, from start/stop
 events that the runtime stamps on each attention kernel's execution in a
 second pass over the same steps) and a CPU baseline (the fp64 oracle on a
-bounded sample of the same workload).
+bounded sample of the same workload).  The same line carries records of the
+other configurations through the same path: the 8-layer long-history hit
+(`long_history`, HBM roofline), the batch-8 full recompute and the 64-user
+serving mix (`full_recompute`, `serving_mix`, MFMA roofline), with the
+cached-against-recomputed ratios and the batch-invariant mode's cost.
 """
 from __future__ import annotations
 
@@ -938,7 +942,7 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
     import torch
-    from workloads import B8_KV_HIT_LONG
+    from workloads import B8_KV_HIT_LONG, B8_RECOMPUTE, B64_SERVING
     b = Bench(args)
     m = time_stack(b, args.steps, args.warmup, events=not args.no_events)
     value = m["tokens"] / m["wall"]
@@ -969,15 +973,18 @@ def main():
         # the 8-layer long-history hit (where the pages' KV streaming lives)
         del b
         torch.cuda.empty_cache()
-        bl = Bench(argparse.Namespace(workload=B8_KV_HIT_LONG, instances=1, seed=args.seed))
-        ml = time_stack(bl, max(4, args.steps // 6), 2, events=True)
-        rec = dict(workload=bl.wl.name, value=ml["tokens"] / ml["wall"], unit="new tokens/s",
-                   ms_per_step=1e3 * ml["wall"] / ml["steps"], steps=ml["steps"], layers=bl.L, batch=bl.B,
-                   hist=str(CONFIGS[bl.wl.name]["hist"]), new=str(CONFIGS[bl.wl.name]["new"]),
-                   page_size=bl.wl.page_size, roofline=roofline_of(ml, None))
-        add_stages(rec, ml, bl, ml["steps"])
+        bl, rec = workload_record(args, B8_KV_HIT_LONG, max(4, args.steps // 6), 2)
         out["cache_speedup"][bl.wl.name] = cache_speedup(args, bl)
         out["long_history"] = rec
+        del bl
+        torch.cuda.empty_cache()
+        # the compute-bound configurations: the batch-8 full recompute and the
+        # 64-user serving mix (its long miss users' causal recomputes)
+        for name, key, st in ((B8_RECOMPUTE, "full_recompute", max(4, args.steps // 6)),
+                              (B64_SERVING, "serving_mix", 3)):
+            bx, out[key] = workload_record(args, name, st, 1, bound="mfma")
+            del bx
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 
@@ -1065,6 +1072,35 @@ def roofline_of(m, traffic):
                 broad_bytes_per_launch=m["broad_bytes"] / n, broad_achieved=broad,
                 broad_frac=broad / HBM_PEAK_GBS,
                 mfma_tflops=m["flops"] / attn_s / 1e12, mfma_frac=m["flops"] / attn_s / 1e12 / BF16_PEAK_TFLOPS)
+
+
+def roofline_mfma(m):
+    """The attention kernel against the bf16 MFMA peak (4 * D FLOP per
+    (query, key) pair over the causal and cached keys), for workloads whose
+    attention is compute-bound (full recompute, long miss users)."""
+    attn_s = m["stage_ms"][2] / 1e3
+    n = m["n_launch"]
+    achieved = m["flops"] / attn_s / 1e12
+    return dict(kernel="paged_silu_attn", bound="mfma", achieved=achieved, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=achieved / BF16_PEAK_TFLOPS, traffic=None, mean_us=1e6 * attn_s / n,
+                timing="hipExtLaunchKernel start/stop events per launch, second pass of the same steps",
+                flops_per_launch=m["flops"] / n,
+                flops_note="4 * D FLOP per (query, key) pair over the causal and cached keys")
+
+
+def workload_record(args, name, steps, warmup, bound="hbm"):
+    """One more configuration through the same stack path, as a record of
+    the main line (its own batch, one instance)."""
+    import torch
+    from workloads import CONFIGS
+    b = Bench(argparse.Namespace(workload=name, instances=1, seed=args.seed))
+    m = time_stack(b, steps, warmup, events=True)
+    rec = dict(workload=b.wl.name, value=m["tokens"] / m["wall"], unit="new tokens/s",
+               ms_per_step=1e3 * m["wall"] / m["steps"], steps=m["steps"], layers=b.L, batch=b.B,
+               hist=str(CONFIGS[name]["hist"]), new=str(CONFIGS[name]["new"]), page_size=b.wl.page_size,
+               roofline=roofline_of(m, None) if bound == "hbm" else roofline_mfma(m))
+    add_stages(rec, m, b, m["steps"])
+    return b, rec
 
 
 def add_stages(out, m, b, steps):

@@ -17,9 +17,12 @@
 // `budget` units per item an entry's chunks are at most
 // clamp(budget / w, kMinSteps, kCapSteps) steps long, and the budget is the
 // smallest one found that keeps the item count within the number of resident
-// attention workgroups (plus the number of entries, when those alone exceed
-// it).  Each entry's keys are then cut into near-equal
-// chunks (multiples of 32 keys).
+// attention workgroups (when the entries alone reach that number: within
+// the workgroups plus the entries, rounded up to a whole multiple of the
+// workgroups).  Each entry's keys are then cut into near-equal chunks
+// (multiples of 32 keys).  When the items outnumber the workgroups the list
+// is ordered by chunk cost, highest first: the first items go to the
+// workgroups in list order and the rest to whichever finishes first.
 // Batch-invariant calls (HSTU_FLAG_BATCH_INVARIANT) skip the search: every
 // entry's keys are cut at the multiples of HSTU_INVARIANT_CHUNK_KEYS, so a
 // row's pieces depend only on its own position, never on the batch.

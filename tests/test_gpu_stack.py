@@ -86,6 +86,31 @@ def test_bad_page_in_last_layer_stops_the_stack():
         assert torch.all(y == 3.0)
 
 
+@pytest.mark.parametrize("layer,user,which,value", [(1, 77, 2, "pool"), (3, 199, -1, -1), (0, 0, 0, "pool")])
+def test_bad_page_anywhere_in_a_long_validation_stops_the_stack(layer, user, which, value):
+    """200 users over 4 layers: the page check gives each thread several
+    pages per layer, so its loads run across layer boundaries and rounds; a
+    bad id in any layer, at any user and page, must be found."""
+    print(f"case stack bad page layer {layer} user {user}", flush=True)
+    wl = make_workload(TINY_FP32, seed=11, B=200, layers=4, hist=("uniform", 5, 400), new=("uniform", 1, 20),
+                       pool_pages=8192)
+    st = stack_from_workload(wl)
+    x, off, hl = inputs(wl, st)
+    npages = int((wl.hist_len[user] + wl.new_len[user] + wl.page_size - 1) // wl.page_size)
+    pg = which if which >= 0 else npages - 1                 # a page in use by the user
+    st.layers[layer]["page_table"][user, pg] = wl.num_pool_pages if value == "pool" else value
+    ys = [torch.full_like(x, 3.0) for _ in range(4)]
+    from hstu_jagged_silu_fwd_amd import _lib
+    desc = st.desc(int(x.shape[0]))
+    ws = torch.empty(_lib.stack_workspace_size(desc, 4), dtype=torch.uint8, device=st.device)
+    L = st.layers
+    _lib.stack_fwd(desc, x, off, hl, [l["page_table"] for l in L], [st.k_pool] * 4, [st.v_pool] * 4,
+                   [l["w1t"] for l in L], [l["w2t"] for l in L], [l["pos_bias"] for l in L], ys, ws)
+    assert _lib.read_device_status(ws) == 4
+    for y in ys:
+        assert torch.all(y == 3.0)
+
+
 def test_stack_equals_layers_with_timestamps():
     """The serving workload's timestamp bias term through the stack call."""
     print("case stack bf16 timestamps", flush=True)

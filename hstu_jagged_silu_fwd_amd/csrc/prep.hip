@@ -36,15 +36,16 @@ constexpr int kPrepWaves = kPrepThreads / kWave;
 constexpr int kStepKeys = 32;   // attention key step
 constexpr int kMinSteps = 4;    // shortest chunk: a step for each of up to four phases
 constexpr int kCapSteps = kMaxChunkKeys / kStepKeys;
-// Cost of one 32-key step by the entry's query groups G, in units of about a
-// tenth of a microsecond (measured per step on MI355X: about 0.6 us up to
-// two groups, 0.7 up to four, 0.87 up to eight -- the attention workgroup
-// splits those steps over four or two phases -- and 1.5 to 1.8 us beyond,
-// where every wave multiplies every step).
+// Cost of one 32-key step by the entry's query groups G, in units
+// proportional to the attention's measured time per step (per-workgroup
+// s_memtime stamps of an instrumented build on MI355X, about 2 GHz: some
+// 1.46k ticks up to two groups, 1.67k up to eight -- the workgroup splits
+// those steps over two phases -- 2.45k up to twelve and 2.9k beyond, where
+// every wave multiplies every step; the 16-wave layout's ratios are alike).
 __device__ __forceinline__ int step_weight(int groups) {
-  return groups <= 2 ? 6 : (groups <= 4 ? 7 : (groups <= 8 ? 9 : (groups <= 12 ? 15 : 18)));
+  return groups <= 2 ? 9 : (groups <= 4 ? 10 : (groups <= 8 ? 11 : (groups <= 12 ? 15 : 18)));
 }
-constexpr int kMinWeight = 6;
+constexpr int kMinWeight = 9;
 constexpr int kMaxWeight = 18;
 constexpr int kWShift = 25;     // entry word: steps (bits 0..24) | weight << 25
 constexpr int kStepMask = (1 << kWShift) - 1;

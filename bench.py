@@ -967,6 +967,8 @@ def main():
         # the cached step of the same batch
         out["cache_speedup"] = {b.wl.name: cache_speedup(args, b)}
         out["batch_invariant"] = invariant_cost(b, args.steps, args.warmup, m)
+        # the same steps with two and three batches in flight (serving)
+        out["in_flight"] = [in_flight(b, args.steps, args.warmup, k, value) for k in (2, 3)]
     if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
     if headline:
@@ -986,6 +988,47 @@ def main():
             del bx
             torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
+
+
+def in_flight(b, steps, warmup, nstreams, serial_value):
+    """The headline steps with `nstreams` batches in flight, as a server
+    running several instances of the model on one GPU would: step s runs
+    batch s mod R in one hstu_stack_fwd call on stream s mod nstreams, each
+    stream with a workspace of its own (R is a multiple of nstreams, so a
+    batch always runs on the same stream and no two streams write the same
+    output rows or pool pages).  Every step still runs the whole stack over
+    its 8 users; only consecutive steps overlap in time."""
+    import torch
+    if b.R % nstreams:
+        raise ValueError("instances must be a multiple of the streams")
+    P = ctypes.c_void_p
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]     # default priority
+    wss = [b.ws] + [torch.empty_like(b.ws) for _ in range(nstreams - 1)]
+    calls = []
+    for i, io in enumerate(b.inst):
+        a = list(io["stack_args"])
+        a[-3] = P(wss[i % nstreams].data_ptr())
+        a[-1] = P(streams[i % nstreams].cuda_stream)
+        calls.append(tuple(a))
+
+    def run(n):
+        for s in range(n):
+            rc = b.lib.hstu_stack_fwd(*calls[s % b.R])
+            if rc != 0:
+                raise RuntimeError(f"hstu_stack_fwd failed: {rc}")
+
+    torch.cuda.synchronize()
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tokens = sum(b.inst[s % b.R]["T"] for s in range(steps))
+    value = tokens / wall
+    return dict(streams=nstreams, value=value, unit="new tokens/s", ms_per_step=1e3 * wall / steps,
+                steps=steps, speedup_vs_serial=value / serial_value,
+                note="wall time of the steps; each stream's calls are ordered, the streams' calls overlap")
 
 
 def invariant_cost(b, steps, warmup, m):

@@ -49,6 +49,7 @@ class HSTUStack:
         self._sws = None          # workspace of the stack calls
         self._last_ws = None      # workspace of the last call (its status word)
         self._last_stream = None  # stream of the last call
+        self._ws_stream = {}      # workspace address -> stream of its last call
 
     def desc(self, total_new: int, num_users: Optional[int] = None) -> _lib.LayerDesc:
         kw = dict(self.common)
@@ -100,6 +101,7 @@ class HSTUStack:
             self._layer(l, x, new_offsets, hist_len, y, workspace, timestamps, ts_offsets, stage_events,
                         page_table, num_candidates)
         self._last_stream = stream
+        self._ws_stream[self._last_ws.data_ptr()] = stream
 
     def _layer(self, l, x, new_offsets, hist_len, y, workspace, timestamps, ts_offsets, stage_events,
                page_table, num_candidates) -> None:
@@ -119,21 +121,27 @@ class HSTUStack:
                        stage_events=stage_events, num_candidates=num_candidates)
 
     def forward(self, x, new_offsets, hist_len, timestamps=None, ts_offsets=None,
-                stream=None, return_all: bool = False, page_tables=None, num_candidates=None):
+                stream=None, return_all: bool = False, page_tables=None, num_candidates=None,
+                workspace: Optional[torch.Tensor] = None):
         """Run every layer in one hstu_stack_fwd call (the batch metadata is
         prepared once for all layers); returns the last layer's output (or
         all outputs).  page_tables: optional per-layer [B, max_pages] tables
         (e.g. a KV cache plan's, from KVCache.build_tables) instead of the
         layers' own.  stream: where the call runs (default: the current
-        stream); inputs are staged and outputs allocated there too."""
+        stream); inputs are staged and outputs allocated there too.
+        workspace: a uint8 device tensor of at least stack_workspace_size
+        bytes for this call (default: one the stack keeps).  Calls that
+        overlap in time (batches in flight on different streams) each need
+        a workspace of their own, and their users' pages must not overlap."""
         with _lib.stream_scope(stream):
             out = self._forward(x, new_offsets, hist_len, timestamps, ts_offsets, return_all, page_tables,
-                                num_candidates)
+                                num_candidates, workspace)
         self._last_stream = stream
+        self._ws_stream[self._last_ws.data_ptr()] = stream
         return out
 
     def _forward(self, x, new_offsets, hist_len, timestamps, ts_offsets, return_all, page_tables,
-                 num_candidates):
+                 num_candidates, workspace=None):
         x = self._dev(x, self.tdtype)
         off = self._dev(new_offsets, torch.int32)
         hl = self._dev(hist_len, torch.int32)
@@ -145,23 +153,29 @@ class HSTUStack:
         nu = None if page_tables is None else int(off.shape[0]) - 1
         desc = self.desc(T, nu)
         need = _lib.stack_workspace_size(desc, nl)
-        if self._sws is None or self._sws.numel() < need:
-            self._sws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        if workspace is not None:
+            if workspace.dtype != torch.uint8 or workspace.device.type != "cuda" or workspace.numel() < need:
+                raise ValueError(f"workspace: a uint8 device tensor of at least {need} bytes is needed")
+            ws = workspace
+        else:
+            if self._sws is None or self._sws.numel() < need:
+                self._sws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            ws = self._sws
         outs = [torch.empty_like(x) for _ in range(nl)]
         L = self.layers
         pts = [L[l]["page_table"] for l in range(nl)] if page_tables is None else \
             [self._dev(page_tables[l], torch.int32) for l in range(nl)]
         has_ts = L[0]["ts_bias"] is not None
         _lib.stack_fwd(desc, x, off, hl, pts, [self.k_pool] * nl, [self.v_pool] * nl, [l["w1t"] for l in L],
-                       [l["w2t"] for l in L], [l["pos_bias"] for l in L], outs, self._sws,
+                       [l["w2t"] for l in L], [l["pos_bias"] for l in L], outs, ws,
                        ts_bias=[l["ts_bias"] for l in L] if has_ts else None, timestamps=ts, ts_offsets=tso,
                        num_candidates=nc)
-        self._last_ws = self._sws
+        self._last_ws = ws
         return outs if return_all else outs[-1]
 
     def read_status(self, workspace: Optional[torch.Tensor] = None) -> int:
-        """Device status of the last call: the given workspace, else that of
-        the last forward (stack call) or layer call, whichever ran last
+        """Device status of the last call on the given workspace, else of the
+        last forward (stack call) or layer call, whichever ran last
         (synchronises the stream that call ran on)."""
-        return _lib.read_device_status(self._last_ws if workspace is None else workspace,
-                                       stream=self._last_stream)
+        ws = self._last_ws if workspace is None else workspace
+        return _lib.read_device_status(ws, stream=self._ws_stream.get(ws.data_ptr(), self._last_stream))

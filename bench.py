@@ -169,7 +169,7 @@ class Bench:
         self.hip = _lib.hip_runtime()
         if wl is None:
             name = args.workload
-            self.R = args.instances if name == WORKLOAD else 1
+            self.R = args.instances if name == WORKLOAD or getattr(args, "any_instances", False) else 1
             B = CONFIGS[name]["B"]
             wl = make_workload(name, seed=args.seed, B=B * self.R)
         else:
@@ -980,6 +980,9 @@ def main():
         out["long_history"] = rec
         del bl
         torch.cuda.empty_cache()
+        bl, out["long_history"]["in_flight"] = workload_in_flight(args, B8_KV_HIT_LONG, max(4, args.steps // 6), 2, 2)
+        del bl
+        torch.cuda.empty_cache()
         # the compute-bound configurations: the batch-8 full recompute and the
         # 64-user serving mix (its long miss users' causal recomputes)
         for name, key, st in ((B8_RECOMPUTE, "full_recompute", max(4, args.steps // 6)),
@@ -1143,6 +1146,25 @@ def workload_record(args, name, steps, warmup, bound="hbm"):
                hist=str(CONFIGS[name]["hist"]), new=str(CONFIGS[name]["new"]), page_size=b.wl.page_size,
                roofline=roofline_of(m, None) if bound == "hbm" else roofline_mfma(m))
     add_stages(rec, m, b, m["steps"])
+    return b, rec
+
+
+def workload_in_flight(args, name, steps, warmup, nstreams):
+    """Configuration `name` with `nstreams` independent batches (its users
+    drawn nstreams times over), timed with the steps serialised on one
+    stream and then with the batches in flight on streams of their own;
+    the history K/V streamed per second of wall time (every layer's cached
+    keys, 4 * D bytes each) is reported beside the token rates."""
+    b = Bench(argparse.Namespace(workload=name, instances=nstreams, seed=args.seed, any_instances=True))
+    m = time_stack(b, steps, warmup, events=False)
+    serial = m["tokens"] / m["wall"]
+    rec = in_flight(b, steps, warmup, nstreams, serial)
+    hist_bytes = b.L * sum(b.attn_work(b.inst[s % b.R])[0] for s in range(steps))
+    wall = rec["ms_per_step"] * steps / 1e3
+    rec.update(serial_value=serial, serial_ms_per_step=1e3 * m["wall"] / steps,
+               kv_stream_gbs=hist_bytes / wall / 1e9, kv_stream_frac=hist_bytes / wall / 1e9 / HBM_PEAK_GBS,
+               serial_kv_stream_gbs=hist_bytes / m["wall"] / 1e9,
+               kv_note="history K/V bytes of every layer over the wall time of the whole steps (all kernels)")
     return b, rec
 
 

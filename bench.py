@@ -968,7 +968,8 @@ def main():
         out["cache_speedup"] = {b.wl.name: cache_speedup(args, b)}
         out["batch_invariant"] = invariant_cost(b, args.steps, args.warmup, m)
         # the same steps with two and three batches in flight (serving)
-        out["in_flight"] = [in_flight(b, args.steps, args.warmup, k, value) for k in (2, 3)]
+        out["in_flight"] = [in_flight(b, args.steps, args.warmup, 2, value)] + \
+            [in_flight(b, args.steps, args.warmup, k, value, graphs=True) for k in (1, 2, 3)]
     if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
     if headline:
@@ -980,7 +981,7 @@ def main():
         out["long_history"] = rec
         del bl
         torch.cuda.empty_cache()
-        bl, out["long_history"]["in_flight"] = workload_in_flight(args, B8_KV_HIT_LONG, max(4, args.steps // 6), 2, 2)
+        bl, out["long_history"]["in_flight"] = workload_in_flight(args, B8_KV_HIT_LONG, max(6, args.steps // 6), 2, 3)
         del bl
         torch.cuda.empty_cache()
         # the compute-bound configurations: the batch-8 full recompute and the
@@ -993,34 +994,57 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def in_flight(b, steps, warmup, nstreams, serial_value):
+def in_flight(b, steps, warmup, nstreams, serial_value, graphs=False):
     """The headline steps with `nstreams` batches in flight, as a server
     running several instances of the model on one GPU would: step s runs
     batch s mod R in one hstu_stack_fwd call on stream s mod nstreams, each
     stream with a workspace of its own (R is a multiple of nstreams, so a
     batch always runs on the same stream and no two streams write the same
     output rows or pool pages).  Every step still runs the whole stack over
-    its 8 users; only consecutive steps overlap in time."""
+    its users; only consecutive steps overlap in time.  graphs: each batch's
+    call is captured once into a HIP graph on its stream and the steps
+    replay the graphs (one host call per step instead of one per kernel:
+    the eager calls' host-side enqueueing, ~100 us per 3-layer step, would
+    otherwise bound the overlapped steps)."""
     import torch
     if b.R % nstreams:
         raise ValueError("instances must be a multiple of the streams")
     P = ctypes.c_void_p
     streams = [torch.cuda.Stream() for _ in range(nstreams)]     # default priority
-    wss = [b.ws] + [torch.empty_like(b.ws) for _ in range(nstreams - 1)]
+    wss = [torch.empty_like(b.ws) for _ in range(nstreams)]
     calls = []
     for i, io in enumerate(b.inst):
         a = list(io["stack_args"])
         a[-3] = P(wss[i % nstreams].data_ptr())
         a[-1] = P(streams[i % nstreams].cuda_stream)
-        calls.append(tuple(a))
+        calls.append((tuple(a), streams[i % nstreams]))
 
-    def run(n):
-        for s in range(n):
-            rc = b.lib.hstu_stack_fwd(*calls[s % b.R])
-            if rc != 0:
-                raise RuntimeError(f"hstu_stack_fwd failed: {rc}")
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"hstu_stack_fwd failed: {rc}")
 
     torch.cuda.synchronize()
+    if graphs:
+        replays = []
+        for a, st in calls:
+            check(b.lib.hstu_stack_fwd(*a))          # once eagerly on the capture stream
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                check(b.lib.hstu_stack_fwd(*a))
+            replays.append((g, st))
+        torch.cuda.synchronize()
+
+        def run(n):
+            for s in range(n):
+                g, st = replays[s % b.R]
+                with torch.cuda.stream(st):
+                    g.replay()
+    else:
+        def run(n):
+            for s in range(n):
+                check(b.lib.hstu_stack_fwd(*calls[s % b.R][0]))
+
     run(warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -1029,8 +1053,8 @@ def in_flight(b, steps, warmup, nstreams, serial_value):
     wall = time.perf_counter() - t0
     tokens = sum(b.inst[s % b.R]["T"] for s in range(steps))
     value = tokens / wall
-    return dict(streams=nstreams, value=value, unit="new tokens/s", ms_per_step=1e3 * wall / steps,
-                steps=steps, speedup_vs_serial=value / serial_value,
+    return dict(streams=nstreams, graphs=graphs, value=value, unit="new tokens/s",
+                ms_per_step=1e3 * wall / steps, steps=steps, speedup_vs_serial=value / serial_value,
                 note="wall time of the steps; each stream's calls are ordered, the streams' calls overlap")
 
 
@@ -1152,13 +1176,14 @@ def workload_record(args, name, steps, warmup, bound="hbm"):
 def workload_in_flight(args, name, steps, warmup, nstreams):
     """Configuration `name` with `nstreams` independent batches (its users
     drawn nstreams times over), timed with the steps serialised on one
-    stream and then with the batches in flight on streams of their own;
+    stream (eager calls) and then with the batches in flight on streams of
+    their own (graph replays, see in_flight);
     the history K/V streamed per second of wall time (every layer's cached
     keys, 4 * D bytes each) is reported beside the token rates."""
     b = Bench(argparse.Namespace(workload=name, instances=nstreams, seed=args.seed, any_instances=True))
     m = time_stack(b, steps, warmup, events=False)
     serial = m["tokens"] / m["wall"]
-    rec = in_flight(b, steps, warmup, nstreams, serial)
+    rec = in_flight(b, steps, warmup, nstreams, serial, graphs=True)
     hist_bytes = b.L * sum(b.attn_work(b.inst[s % b.R])[0] for s in range(steps))
     wall = rec["ms_per_step"] * steps / 1e3
     rec.update(serial_value=serial, serial_ms_per_step=1e3 * m["wall"] / steps,

@@ -64,6 +64,50 @@ def test_two_batches_in_flight_equal_serial_calls():
         tol_check(to_np(got[-1][i][2]), x[rows], "bf16", f"in-flight batch {i} layer 2")
 
 
+def test_graphs_replayed_in_flight_equal_serial_calls():
+    """Each batch's stack call captured once into a HIP graph on a stream of
+    its own, then the two graphs replayed in flight (eager work and
+    synchronisations between the rounds): every replay equals the serial
+    eager calls bit for bit."""
+    print("case in-flight graph replays two streams", flush=True)
+    wl = make_workload(B8_KV_HIT, seed=23, B=8, hist=("uniform", 256, 1500), new=("uniform", 16, 256), layers=3,
+                       pool_pages=4096)
+    st = stack_from_workload(wl)
+    users = (np.arange(0, 4), np.arange(4, 8))
+    bs = [_batch(wl, st, u) for u in users]
+    ref = [_call(st, b)[-1].clone() for b in bs]
+    assert st.read_status() == 0
+    from hstu_jagged_silu_fwd_amd import _lib
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    graphs, outs, wss = [], [], []
+    for b, s in zip(bs, streams):
+        desc = st.desc(int(b["x"].shape[0]), num_users=len(users[0]))
+        w = torch.empty(_lib.stack_workspace_size(desc, 3), dtype=torch.uint8, device=st.device)
+        s.wait_stream(torch.cuda.current_stream())
+        _call(st, b, stream=s, workspace=w)          # warm the allocator on the capture stream
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            outs.append(_call(st, b, stream=s, workspace=w)[-1])
+        graphs.append(g)
+        wss.append(w)
+    for rep in range(3):
+        junk = torch.randn(1 << 20, device=st.device).sum()   # eager work between the rounds
+        torch.cuda.synchronize()
+        for o in outs:
+            o.fill_(7.0)
+        torch.cuda.synchronize()
+        for g, s in zip(graphs, streams):
+            with torch.cuda.stream(s):
+                g.replay()
+        torch.cuda.synchronize()
+        for w in wss:
+            assert _lib.read_device_status(w) == 0
+        for i in range(2):
+            assert torch.equal(outs[i], ref[i]), f"replay {rep} batch {i} differs"
+        del junk
+
+
 def test_workspace_too_small_is_refused():
     wl = make_workload(B8_KV_HIT, seed=22, B=2, hist=("uniform", 40, 90), new=("uniform", 16, 40), layers=1,
                        pool_pages=256)

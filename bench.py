@@ -75,6 +75,9 @@ def parse():
                     help="the projection products of the batch-8 workloads (cached hit, full recompute) through "
                          "the vendor GEMM library (torch.matmul -> hipBLASLt, plain products without the fused "
                          "epilogues) beside this library's projection stages on the same batches")
+    ap.add_argument("--in-flight", type=int, default=0, metavar="S",
+                    help="only the headline steps with S batches in flight (graph replays; S divides --instances), "
+                         "after the same steps serialised on one stream, as one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -943,6 +946,14 @@ def main():
         sys.exit(2)
     import torch
     from workloads import B8_KV_HIT_LONG, B8_RECOMPUTE, B64_SERVING
+    if args.in_flight > 0:
+        b = Bench(args)
+        m = time_stack(b, args.steps, args.warmup, events=False)
+        serial = m["tokens"] / m["wall"]
+        rec = in_flight(b, args.steps, args.warmup, args.in_flight, serial, graphs=True)
+        rec.update(workload=b.wl.name, serial_value=serial, serial_ms_per_step=1e3 * m["wall"] / args.steps)
+        print(json.dumps(rec), flush=True)
+        return
     b = Bench(args)
     m = time_stack(b, args.steps, args.warmup, events=not args.no_events)
     value = m["tokens"] / m["wall"]

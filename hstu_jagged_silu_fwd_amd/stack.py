@@ -6,6 +6,7 @@ pool; layer l's output rows are layer l+1's input rows.
 """
 from __future__ import annotations
 
+import collections
 from typing import List, Optional
 
 import torch
@@ -49,7 +50,19 @@ class HSTUStack:
         self._sws = None          # workspace of the stack calls
         self._last_ws = None      # workspace of the last call (its status word)
         self._last_stream = None  # stream of the last call
-        self._ws_stream = {}      # workspace address -> stream of its last call
+        # workspace address -> stream of its last call (the most recent
+        # kWsStreams workspaces; callers that make a new workspace per call
+        # do not grow it without bound)
+        self._ws_stream: "collections.OrderedDict[int, object]" = collections.OrderedDict()
+
+    kWsStreams = 64
+
+    def _note_stream(self, stream) -> None:
+        key = self._last_ws.data_ptr()
+        self._ws_stream.pop(key, None)
+        self._ws_stream[key] = stream
+        while len(self._ws_stream) > self.kWsStreams:
+            self._ws_stream.popitem(last=False)
 
     def desc(self, total_new: int, num_users: Optional[int] = None) -> _lib.LayerDesc:
         kw = dict(self.common)
@@ -101,7 +114,7 @@ class HSTUStack:
             self._layer(l, x, new_offsets, hist_len, y, workspace, timestamps, ts_offsets, stage_events,
                         page_table, num_candidates)
         self._last_stream = stream
-        self._ws_stream[self._last_ws.data_ptr()] = stream
+        self._note_stream(stream)
 
     def _layer(self, l, x, new_offsets, hist_len, y, workspace, timestamps, ts_offsets, stage_events,
                page_table, num_candidates) -> None:
@@ -137,7 +150,7 @@ class HSTUStack:
             out = self._forward(x, new_offsets, hist_len, timestamps, ts_offsets, return_all, page_tables,
                                 num_candidates, workspace)
         self._last_stream = stream
-        self._ws_stream[self._last_ws.data_ptr()] = stream
+        self._note_stream(stream)
         return out
 
     def _forward(self, x, new_offsets, hist_len, timestamps, ts_offsets, return_all, page_tables,

@@ -227,3 +227,25 @@ def test_noalloc_host_checks():
     rc = lib.hstu_layer_fwd_noalloc(ctypes.byref(big), *([None] * 13), ctypes.byref(status), None)
     assert rc == -6
     assert "scratch" in hs.status_string(-6)
+
+
+def test_stack_workspace_stream_map_is_bounded():
+    """HSTUStack remembers the stream of each workspace's last call (for
+    read_status) only for its most recent workspaces, so callers that make a
+    new workspace per call do not grow it; a workspace used again moves to
+    the most recent end."""
+    import torch
+    from hstu_jagged_silu_fwd_amd.stack import HSTUStack
+    st = HSTUStack(num_users=1, num_heads=1, head_dim=32, page_size=16, num_pool_pages=1,
+                   max_pages_per_user=1, pos_buckets=32, pos_mbits=3, attn_scale=1.0, device="cpu")
+    keep = [torch.empty(256, dtype=torch.uint8) for _ in range(3 * st.kWsStreams)]
+    first = keep[0]
+    for i, w in enumerate(keep):
+        st._last_ws = w
+        st._note_stream(i)
+        st._last_ws = first                  # the first workspace stays in use
+        st._note_stream("first")
+    assert len(st._ws_stream) == st.kWsStreams
+    assert st._ws_stream[first.data_ptr()] == "first"
+    assert st._ws_stream[keep[-1].data_ptr()] == len(keep) - 1
+    assert keep[1].data_ptr() not in st._ws_stream

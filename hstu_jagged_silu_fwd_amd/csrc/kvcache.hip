@@ -51,6 +51,8 @@ struct hstu_kvcache {
   std::vector<int32_t> free_slots;   // stacks: back() is taken first
   std::vector<int32_t> free_pages;
   int64_t held = 0;                  // GPU pages held by cached users (all layers)
+  std::vector<int32_t> pins;         // pin count of each slot (pinned users are never evicted)
+  std::unordered_set<int32_t> pinned;   // slots with pins > 0
   // host tier
   std::unordered_map<int64_t, HostUser> host;
   std::list<int64_t> host_order;     // front = most recent
@@ -81,6 +83,8 @@ struct hstu_kvcache {
     slot_user[s] = -1;
     slot_len[s] = 0;
     slot_npages[s] = 0;
+    pins[s] = 0;                                   // (callers never release a pinned slot)
+    pinned.erase(s);
     free_slots.push_back(s);
   }
   void drop_host(int64_t uid) {
@@ -196,6 +200,7 @@ hstu_kvcache* hstu_kvcache_create(int32_t num_layers, int64_t num_pages, int32_t
     c->pages.assign(static_cast<size_t>(dir), -1);
     c->prev.assign(max_users, -1);
     c->next.assign(max_users, -1);
+    c->pins.assign(max_users, 0);
     c->free_slots.reserve(max_users);
     for (int32_t s = max_users - 1; s >= 0; --s) c->free_slots.push_back(s);
     c->free_pages.reserve(static_cast<size_t>(num_pages));
@@ -243,6 +248,7 @@ hstu_kv_status hstu_kvcache_plan(hstu_kvcache* c, int32_t B, const int64_t* user
     if (n_new[b] < 0 || !seen.insert(user_ids[b]).second) return HSTU_KV_INVALID_ARG;
     const auto it = c->index.find(user_ids[b]);
     const int32_t s = it == c->index.end() ? -1 : it->second;
+    if (s >= 0 && c->pins[s] > 0) return HSTU_KV_PINNED;   // its earlier batch is still in flight
     bslot[b] = s;
     hist[b] = 0;
     if (s >= 0) {
@@ -266,23 +272,32 @@ hstu_kv_status hstu_kvcache_plan(hstu_kvcache* c, int32_t B, const int64_t* user
   }
   if (need_pages > update_cap) return HSTU_KV_CAPACITY;
   if (c->PH > 0 && onboard + (c->held - batch_held) > copy_cap) return HSTU_KV_CAPACITY;
-  const int64_t free_after = static_cast<int64_t>(c->free_pages.size()) + (c->held - batch_held);
-  const int64_t slots_after = static_cast<int64_t>(c->free_slots.size()) +
-                              (static_cast<int64_t>(c->index.size()) - gpu_hits);
-  if (free_after < need_pages || slots_after < slot_need) return HSTU_KV_FULL;
-
-  // 3. evict least recently used GPU-cached users outside the batch until the
-  //    batch fits, offloading them to the host tier where they fit
   std::vector<char> in_batch(c->max_users, 0);
   for (int32_t b = 0; b < B; ++b)
     if (bslot[b] >= 0) in_batch[bslot[b]] = 1;
+  // pinned users outside the batch keep their pages and slots
+  int64_t pinned_pages = 0, pinned_users = 0;
+  for (const int32_t s : c->pinned)
+    if (!in_batch[s]) {
+      pinned_pages += static_cast<int64_t>(c->L) * c->slot_npages[s];
+      ++pinned_users;
+    }
+  const int64_t free_after =
+      static_cast<int64_t>(c->free_pages.size()) + (c->held - batch_held - pinned_pages);
+  const int64_t slots_after = static_cast<int64_t>(c->free_slots.size()) +
+                              (static_cast<int64_t>(c->index.size()) - gpu_hits - pinned_users);
+  if (free_after < need_pages || slots_after < slot_need) return HSTU_KV_FULL;
+
+  // 3. evict least recently used GPU-cached users outside the batch (and not
+  //    pinned) until the batch fits, offloading them to the host tier where
+  //    they fit
   int32_t ne = 0, nc = 0;
   int32_t cur = c->lru;
   std::unordered_set<int64_t> offloaded;   // entered the host tier in this plan: their
                                            // copies are pending, so they are not dropped
   while (static_cast<int64_t>(c->free_pages.size()) < need_pages ||
          static_cast<int64_t>(c->free_slots.size()) < slot_need) {
-    while (cur >= 0 && in_batch[cur]) cur = c->prev[cur];
+    while (cur >= 0 && (in_batch[cur] || c->pins[cur] > 0)) cur = c->prev[cur];
     if (cur < 0) return HSTU_KV_FULL;              // unreachable after the check above
     const int32_t victim = cur;
     cur = c->prev[cur];
@@ -407,11 +422,32 @@ hstu_kv_status hstu_kvcache_evict(hstu_kvcache* c, int64_t user_id, int32_t* fou
   *found = 0;
   const auto it = c->index.find(user_id);
   if (it != c->index.end()) {
+    if (c->pins[it->second] > 0) return HSTU_KV_PINNED;
     c->release_slot(it->second);
     *found = 1;
   } else if (c->host.count(user_id)) {
     c->drop_host(user_id);
     *found = 1;
+  }
+  return HSTU_KV_OK;
+}
+
+hstu_kv_status hstu_kvcache_pin(hstu_kvcache* c, int32_t B, const int64_t* user_ids, int32_t pin) {
+  if (c == nullptr || B < 0 || (B > 0 && user_ids == nullptr)) return HSTU_KV_INVALID_ARG;
+  // every check first, so that a rejected call changes nothing
+  std::unordered_set<int64_t> seen;
+  for (int32_t b = 0; b < B; ++b) {
+    const auto it = c->index.find(user_ids[b]);
+    if (it == c->index.end() || !seen.insert(user_ids[b]).second) return HSTU_KV_INVALID_ARG;
+    if (pin == 0 && c->pins[it->second] == 0) return HSTU_KV_INVALID_ARG;
+  }
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t s = c->index.find(user_ids[b])->second;
+    if (pin != 0) {
+      if (c->pins[s]++ == 0) c->pinned.insert(s);
+    } else if (--c->pins[s] == 0) {
+      c->pinned.erase(s);
+    }
   }
   return HSTU_KV_OK;
 }
@@ -427,6 +463,8 @@ hstu_kv_status hstu_kvcache_trim(hstu_kvcache* c, int32_t B, const int64_t* user
     if (it == c->index.end() || !seen.insert(user_ids[b]).second) return HSTU_KV_INVALID_ARG;
     if (n_drop[b] < 0 || n_drop[b] > c->slot_len[it->second]) return HSTU_KV_INVALID_ARG;
   }
+  for (int32_t b = 0; b < B; ++b)
+    if (c->pins[c->index.find(user_ids[b])->second] > 0) return HSTU_KV_PINNED;
   for (int32_t b = 0; b < B; ++b) {
     const int32_t s = c->index.find(user_ids[b])->second;
     c->slot_len[s] -= n_drop[b];

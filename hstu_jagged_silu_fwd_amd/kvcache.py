@@ -54,6 +54,8 @@ def _lib_kv() -> ctypes.CDLL:
     lib.hstu_kvcache_evict.argtypes = [P, I64, ctypes.POINTER(I32)]
     lib.hstu_kvcache_trim.restype = I32
     lib.hstu_kvcache_trim.argtypes = [P, I32, P, P]
+    lib.hstu_kvcache_pin.restype = I32
+    lib.hstu_kvcache_pin.argtypes = [P, I32, P, I32]
     lib.hstu_kvcache_stats.restype = I32
     lib.hstu_kvcache_stats.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(I32), ctypes.POINTER(I64),
                                        ctypes.POINTER(I32)]
@@ -181,6 +183,25 @@ class KVCache:
         rc = self.lib.hstu_kvcache_trim(self.h, ids.shape[0], _np_ptr(ids), _np_ptr(k))
         if rc != 0:
             raise KVCacheError("hstu_kvcache_trim", rc)
+
+    def pin(self, user_ids: Sequence[int]) -> None:
+        """Pins GPU-cached users while a planned batch of theirs is in flight
+        (its layer calls still running on some stream): no plan evicts them
+        or hands out their pages, and a plan, evict or trim that names one
+        fails (HSTU_KV_PINNED).  All or nothing; pins count."""
+        self._pin(user_ids, 1)
+
+    def unpin(self, user_ids: Sequence[int]) -> None:
+        """Undoes one pin of each user (once its batch's calls have finished)."""
+        self._pin(user_ids, 0)
+
+    def _pin(self, user_ids, pin: int) -> None:
+        ids = np.ascontiguousarray(user_ids, dtype=np.int64)
+        if ids.ndim != 1:
+            raise KVCacheError("pin", -1)
+        rc = self.lib.hstu_kvcache_pin(self.h, ids.shape[0], _np_ptr(ids), pin)
+        if rc != 0:
+            raise KVCacheError("hstu_kvcache_pin", rc)
 
     def stats(self, host: bool = False):
         """(free GPU pages, GPU-cached users), plus (free host pages, host users)

@@ -32,10 +32,10 @@
  *   2. every user needs ceil((hist_len + n_new) / page_size) GPU pages per
  *      layer (a host hit all of them, as it comes back); a miss or a host hit
  *      also needs a slot.  If the free pages and slots, plus those of every
- *      GPU-cached user outside the batch, cannot cover the batch, the plan
- *      fails with HSTU_KV_FULL and changes nothing;
+ *      GPU-cached user outside the batch that is not pinned, cannot cover
+ *      the batch, the plan fails with HSTU_KV_FULL and changes nothing;
  *   3. while pages or slots are short, the least recently used GPU-cached
- *      user outside the batch is evicted.  With a host tier it is offloaded
+ *      user outside the batch that is not pinned is evicted.  With a host tier it is offloaded
  *      when its pages fit there: host-cached users outside the batch are
  *      dropped least recently used first until they do (a user with more
  *      pages than the whole tier is dropped instead), it takes host pages off
@@ -55,7 +55,8 @@
  *      last one most recent), and each user's cached length becomes
  *      hist_len + n_new (the layer forward appends those tokens).
  * A user whose tokens would exceed max_pages_per_user * page_size makes the
- * plan fail with HSTU_KV_TOO_LONG, changing nothing.  The host tier keeps
+ * plan fail with HSTU_KV_TOO_LONG, and a pinned user (hstu_kvcache_pin) with
+ * HSTU_KV_PINNED, changing nothing.  The host tier keeps
  * its own recency order: a user enters it as its most recent entry.
  *
  * A plan's copies list every offload before every onboard; they must run
@@ -93,7 +94,8 @@ typedef enum {
   HSTU_KV_FULL = -10,         /* the batch needs more pages or slots than can be freed */
   HSTU_KV_TOO_LONG = -11,     /* a user's tokens exceed max_pages_per_user * page_size */
   HSTU_KV_CAPACITY = -12,     /* an output array is too small */
-  HSTU_KV_HIP = -13           /* a HIP launch failed (hstu_kv_tables_build) */
+  HSTU_KV_HIP = -13,          /* a HIP launch failed (hstu_kv_tables_build) */
+  HSTU_KV_PINNED = -14        /* plan, evict or trim of a pinned user (hstu_kvcache_pin) */
 } hstu_kv_status;
 
 typedef struct hstu_kvcache hstu_kvcache;
@@ -151,7 +153,7 @@ hstu_kv_status hstu_kvcache_lookup(const hstu_kvcache* cache, int32_t B, const i
 
 /* Drops one user from whichever tier holds it (its pages and slot are
  * freed, pushed as in step 3, nothing is offloaded).  *found = 1 when the
- * user was cached, else 0. */
+ * user was cached, else 0.  A pinned user is not dropped: HSTU_KV_PINNED. */
 hstu_kv_status hstu_kvcache_evict(hstu_kvcache* cache, int64_t user_id, int32_t* found);
 
 /* Shortens the cached length of each of B distinct GPU-cached users by
@@ -165,9 +167,24 @@ hstu_kv_status hstu_kvcache_evict(hstu_kvcache* cache, int64_t user_id, int32_t*
  * directory keeps its stale entries past the new length: a later plan that
  * grows the user rewrites them.  Any invalid entry (unknown or host-cached
  * user, duplicate, count out of range) fails the whole call with
- * HSTU_KV_INVALID_ARG and no change.  Host pointers. */
+ * HSTU_KV_INVALID_ARG and no change; a pinned user fails it with
+ * HSTU_KV_PINNED and no change.  Host pointers. */
 hstu_kv_status hstu_kvcache_trim(hstu_kvcache* cache, int32_t B, const int64_t* user_ids,
                                  const int32_t* n_drop);
+
+/* Pins (pin != 0) or unpins (pin == 0) B distinct GPU-cached users, for
+ * callers that keep several planned batches in flight, i.e. layer calls of
+ * earlier plans still running on other streams while the next batch is
+ * planned.  No plan evicts a pinned user or hands out its pages: a pinned
+ * user counts as neither free nor evictable in step 2.  A batch that holds
+ * a pinned user fails with HSTU_KV_PINNED and no change (its earlier batch
+ * has not appended its K/V yet), and hstu_kvcache_evict and
+ * hstu_kvcache_trim refuse a pinned user the same way.  Pin a batch's users
+ * after its plan and unpin them once its layer calls have finished.  Pins count: a user pinned twice stays
+ * pinned until it is unpinned twice.  Any invalid entry (a user not cached
+ * on the GPU, a duplicate, an unpin of an unpinned user) fails the whole
+ * call with HSTU_KV_INVALID_ARG and no change.  Host pointers. */
+hstu_kv_status hstu_kvcache_pin(hstu_kvcache* cache, int32_t B, const int64_t* user_ids, int32_t pin);
 
 /* Free GPU pages and GPU-cached users, free host pages and host-cached
  * users (the host pointers may be NULL). */

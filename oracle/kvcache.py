@@ -44,6 +44,13 @@ cached length shrinks by a given count; the pages past ceil(new length /
 page_size) go onto the free-page stack layer by layer and index by index
 (as in an eviction); recency is unchanged.
 
+Pins (a reading for batches in flight, i.e. layer calls of earlier plans still
+running while the next batch is planned; the pages give no rule for it): a
+pinned GPU-cached user is never evicted and counts as neither free nor
+evictable when a plan checks whether its batch fits; a plan, an explicit
+evict or a trim that names a pinned user fails and changes nothing; pins
+count, and unpinning an unpinned user is an error.
+
 This model keeps last-use / entry times and picks victims by minimum time;
 the library keeps linked recency lists.  The two agree exactly on every
 output, which the tests check on random traces.
@@ -59,6 +66,10 @@ class CacheFull(Exception):
 
 
 class TooLong(Exception):
+    pass
+
+
+class Pinned(Exception):
     pass
 
 
@@ -92,6 +103,7 @@ class RefKVCache:
     host: Dict[int, _HostUser] = field(default_factory=dict)
     host_free: List[int] = field(default_factory=list)
     host_clock: int = 0
+    pins: Dict[int, int] = field(default_factory=dict)     # user id -> pin count (> 0)
 
     def __post_init__(self):
         self.free_pages = list(range(self.num_pages - 1, -1, -1))
@@ -120,7 +132,26 @@ class RefKVCache:
             for p in layer_pages:
                 self.host_free.append(p)
 
+    def pin(self, ids: Sequence[int], pin: bool = True) -> None:
+        """Pins (or unpins) distinct GPU-cached users; all or nothing
+        (ValueError)."""
+        ids = list(ids)
+        if len(set(ids)) != len(ids) or any(i not in self.users for i in ids) or \
+                (not pin and any(self.pins.get(i, 0) == 0 for i in ids)):
+            raise ValueError("bad pin")
+        for i in ids:
+            n = self.pins.get(i, 0) + (1 if pin else -1)
+            if n:
+                self.pins[i] = n
+            else:
+                del self.pins[i]
+
+    def unpin(self, ids: Sequence[int]) -> None:
+        self.pin(ids, pin=False)
+
     def evict(self, uid: int) -> bool:
+        if uid in self.pins:
+            raise Pinned(uid)
         if uid in self.users:
             self._evict(uid)
             return True
@@ -139,13 +170,15 @@ class RefKVCache:
                 (self.host[i].length if i in self.host else 0) for i in ids]
         need = []
         for i, h, n in zip(ids, hist, n_new):
+            if i in self.pins:
+                raise Pinned(i)
             if h + n > self.max_pages_per_user * self.page_size:
                 raise TooLong(i)
             held = len(self.users[i].pages[0]) if i in self.users else 0
             need.append(self._pages_for(h + n) - held)
         need_pages = self.num_layers * sum(need)
         misses = sum(1 for i in ids if i not in self.users)
-        outside = [i for i in self.users if i not in set(ids)]
+        outside = [i for i in self.users if i not in set(ids) and i not in self.pins]
         can_free = sum(self.num_layers * len(self.users[i].pages[0]) for i in outside)
         if len(self.free_pages) + can_free < need_pages or len(self.free_slots) + len(outside) < misses:
             raise CacheFull()
@@ -205,6 +238,8 @@ class RefKVCache:
         if len(set(ids)) != len(ids) or any(i not in self.users for i in ids) or \
                 any(k < 0 or k > self.users[i].length for i, k in zip(ids, drop)):
             raise ValueError("bad trim")
+        if any(i in self.pins for i in ids):
+            raise Pinned(ids)
         for i, k in zip(ids, drop):
             u = self.users[i]
             u.length -= k

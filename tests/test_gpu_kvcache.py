@@ -140,6 +140,130 @@ def serving_loop(dtype, seed, n_steps, host_pages=0, stream=None):
     return kinds, outs
 
 
+@pytest.mark.parametrize("dtype,seed", [("bf16", 9), ("f32", 10)])
+def test_serving_loop_with_batches_in_flight_equals_recompute(dtype, seed):
+    """Two batches in flight: batch i runs on stream i mod 2 with a
+    workspace of its own, and the next batch is planned while earlier ones
+    still run.  A batch's users are pinned (hstu_kvcache_pin) from its plan
+    until its stream has finished it, so no plan evicts them or hands out
+    their pages meanwhile; a batch takes only users not in flight, and a
+    plan that cannot fit beside the pinned users waits for the oldest batch
+    in flight, unpins it and plans again.  The pool (56 pages, 4 slots, 6
+    recurring users) forces evictions.  Every batch must equal the oracle's
+    recompute of each user's whole sequence."""
+    from hstu_jagged_silu_fwd_amd import _lib
+    from hstu_jagged_silu_fwd_amd.kvcache import KVCacheError
+    print(f"case kv serving loop with batches in flight {dtype} seed {seed}", flush=True)
+    L, ps, maxP, cap, n_steps = 2, 16, 12, 8 * 16, 16
+    if dtype == "f32":
+        wl = make_workload(TINY_FP32, seed=seed, B=2, layers=L, attn_scale=1.0 / cap)
+    else:
+        wl = make_workload(B8_KV_HIT, seed=seed, B=2, layers=L, hist=("const", 0), new=("const", 16),
+                           attn_scale=1.0 / cap)
+    D, H = wl.D, wl.H
+    kv = KVCache(num_layers=L, num_pages=56, page_size=ps, max_pages_per_user=maxP, max_users=4)
+    st = HSTUStack(num_users=1, num_heads=H, head_dim=wl.d, page_size=ps, num_pool_pages=56,
+                   max_pages_per_user=maxP, pos_buckets=wl.pos_buckets, pos_mbits=wl.pos_mbits,
+                   attn_scale=wl.attn_scale, norm_eps=EPS, dtype=dtype, num_layers=L)
+    layers = []
+    for l in range(L):
+        li = wl.layer(l)
+        st.set_layer(l, w1t=li.w1t, w2t=li.w2t, pos_bias=li.pos_bias, page_table=np.zeros((1, maxP), np.int32))
+        layers.append(dict(w1=li.w1, w2=li.w2, pos_bias=li.pos_bias, hist_k=None, hist_v=None))
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    ws = [torch.empty(_lib.stack_workspace_size(st.desc(3 * cap, num_users=3), L), dtype=torch.uint8,
+                      device="cuda") for _ in range(2)]
+    rng = np.random.default_rng(seed + 200)
+    seqs, flight, results = {}, [], []
+    kinds = {"hit": 0, "miss_again": 0, "new": 0, "waits": 0, "evicted": 0}
+
+    def retire_oldest():
+        ids_, ev_ = flight.pop(0)
+        ev_.synchronize()
+        kv.unpin(ids_)
+
+    for step in range(n_steps):
+        busy = {u for ids_, _ in flight for u in ids_}
+        free = [u for u in range(1, 7) if u not in busy]
+        if not free:
+            retire_oldest()
+            free = [u for u in range(1, 7) if u not in {u for ids_, _ in flight for u in ids_}]
+        B = int(rng.integers(1, min(3, len(free)) + 1))
+        ids = [int(u) for u in rng.choice(free, size=B, replace=False)]
+        fresh = [int(k) for k in rng.integers(1, 40, size=B)]
+        cached = kv.lookup(ids).tolist()
+        rows, n_new, new_seqs = [], [], {}
+        for uid, c, k in zip(ids, cached, fresh):
+            xnew = rng.standard_normal((k, D))
+            if dtype == "bf16":
+                xnew = torch.from_numpy(xnew).to(torch.bfloat16).double().numpy()
+            prev = seqs.get(uid, np.zeros((0, D)))
+            if c < 0 and prev.shape[0] > 0:
+                kinds["miss_again"] += 1
+                send = np.vstack([prev, xnew])
+            elif c < 0:
+                kinds["new"] += 1
+                send = xnew
+            else:
+                kinds["hit"] += 1
+                assert c == prev.shape[0]
+                send = xnew
+            if prev.shape[0] + k > cap:                  # restart the user's sequence
+                send, xnew = send[:0], xnew[:0]
+                kv.evict(uid)
+                seqs.pop(uid, None)
+                prev = np.zeros((0, D))
+            new_seqs[uid] = np.vstack([prev, xnew])
+            rows.append(send)
+            n_new.append(send.shape[0])
+        while True:
+            try:
+                plan = kv.plan(ids, n_new)
+                break
+            except KVCacheError as e:                    # full beside the pinned users: wait for one
+                assert e.code == -10 and flight, e
+                kinds["waits"] += 1
+                retire_oldest()
+        kinds["evicted"] += len(plan.evicted)
+        seqs.update(new_seqs)
+        if sum(n_new) == 0:
+            continue
+        kv.pin(ids)
+        s_ = streams[step % 2]
+        tables = kv.build_tables(plan, stream=s_)
+        x = torch.from_numpy(np.vstack(rows)).to(tdt)
+        off = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+        y = st.forward(x, off, plan.hist_len, page_tables=[tables[l] for l in range(L)], stream=s_,
+                       workspace=ws[step % 2])
+        ev = torch.cuda.Event()
+        ev.record(s_)
+        flight.append((ids, ev))
+        want = []
+        for b, uid in enumerate(ids):
+            if n_new[b] == 0:
+                continue
+            full = seqs[uid]
+            ys = olayer.stack_forward(full, [full.shape[0]], [0],
+                                      [dict(l0, hist_k=[np.zeros((0, D))], hist_v=[np.zeros((0, D))])
+                                       for l0 in layers], wl.attn_scale, EPS, H, wl.pos_mbits)
+            want.append((b, uid, ys[-1][-n_new[b]:]))
+        results.append((step, y, off, want, ws[step % 2], s_))
+    while flight:
+        retire_oldest()
+    torch.cuda.synchronize()
+    print(f"[kvcache] in flight {kinds}", flush=True)
+    for step, y, off, want, w, s_ in results:
+        assert st.read_status(w) == 0
+        yn = y.float().cpu().numpy().astype(np.float64)
+        # the batch's rows together (a one-row user's output can be tiny)
+        got_rows = np.vstack([yn[off[b]:off[b + 1]] for b, _, _ in want])
+        tol_check(got_rows, np.vstack([ref for _, _, ref in want]), dtype, f"in flight step {step}")
+    assert kinds["hit"] > 0 and kinds["evicted"] > 0
+
+
 @pytest.mark.parametrize("dtype,seed", [("f32", 3), ("bf16", 4)])
 def test_serving_loop_with_eviction_equals_recompute(dtype, seed):
     print(f"case kv serving loop {dtype} seed {seed}", flush=True)

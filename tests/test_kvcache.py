@@ -12,13 +12,13 @@ import os
 import numpy as np
 import pytest
 
-from oracle.kvcache import CacheFull, RefKVCache, TooLong
+from oracle.kvcache import CacheFull, Pinned, RefKVCache, TooLong
 from hstu_jagged_silu_fwd_amd.kvcache import KVCache, KVCacheError
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRACE = json.load(open(os.path.join(HERE, "golden", "kvcache_trace.json")))
 HOST_TRACE = json.load(open(os.path.join(HERE, "golden", "kvcache_host_trace.json")))
-ERR = {"full": -10, "too_long": -11, "invalid": -1}
+ERR = {"full": -10, "too_long": -11, "invalid": -1, "pinned": -14}
 
 
 def test_reference_model_follows_the_hand_worked_trace():
@@ -332,3 +332,109 @@ def test_library_matches_reference_model_with_trims(seed, host):
         for u in ref.users.values():
             assert all(len(lp) == -(-u.length // cfg["page_size"]) for lp in u.pages)
     assert ok > 50
+
+
+# ---- pins: users of batches still in flight are kept ----
+
+PIN_CFG = dict(num_layers=1, num_pages=4, page_size=4, max_pages_per_user=4, max_users=4)
+
+
+def test_pins_hand_worked_model_and_library():
+    """Pool of 4 pages.  User 1 takes 2 pages and is pinned (its batch in
+    flight): a batch of user 2 needing 3 pages cannot evict it and fails;
+    plan, evict and trim naming user 1 fail; after one of two pins is undone
+    it still holds; after the second, user 2's batch evicts it."""
+    ref, kv = RefKVCache(**PIN_CFG), KVCache(**PIN_CFG)
+    for c in (ref, kv):
+        c.plan([1], [8])
+        c.pin([1])
+        c.pin([1])
+    with pytest.raises(CacheFull):
+        ref.plan([2], [12])
+    with pytest.raises(KVCacheError) as ei:
+        kv.plan([2], [12])
+    assert ei.value.code == ERR["full"]
+    assert kv.stats() == (2, 1) and len(ref.free_pages) == 2
+    with pytest.raises(Pinned):
+        ref.plan([1, 3], [1, 1])
+    with pytest.raises(Pinned):
+        ref.evict(1)
+    with pytest.raises(Pinned):
+        ref.trim([1], [1])
+    for call in (lambda: kv.plan([3, 1], [1, 1]), lambda: kv.evict(1), lambda: kv.trim([1], [1])):
+        with pytest.raises(KVCacheError) as ei:
+            call()
+        assert ei.value.code == ERR["pinned"]
+    assert kv.stats() == (2, 1) and kv.lookup([1, 3]).tolist() == [8, -1]
+    # a batch that fits beside the pinned user goes through
+    assert kv.plan([3], [8]).evicted == [] and ref.plan([3], [8])[3] == []
+    for c in (ref, kv):
+        c.unpin([1])                              # one pin left
+    with pytest.raises(CacheFull):
+        ref.plan([2], [12])
+    with pytest.raises(KVCacheError):
+        kv.plan([2], [12])
+    for c in (ref, kv):
+        c.unpin([1])
+    want = ref.plan([2], [12])
+    got = kv.plan([2], [12])
+    assert want[3] == got.evicted == [1, 3]       # least recently planned first
+    assert [tuple(u) for u in got.updates.tolist()] == [tuple(u) for u in want[2]]
+
+
+def test_pin_rejects_bad_arguments_and_changes_nothing():
+    kv = KVCache(**PIN_CFG)
+    kv.plan([1, 2], [4, 4])
+    for ids, pin in (([5], True), ([1, 1], True), ([1], False), ([1, 5], True)):
+        with pytest.raises(KVCacheError) as ei:
+            (kv.pin if pin else kv.unpin)(ids)
+        assert ei.value.code == ERR["invalid"]
+    assert kv.evict(1) is True                    # nothing was pinned
+
+
+@pytest.mark.parametrize("seed,host", [(20, False), (21, False), (22, True), (23, True)])
+def test_library_matches_reference_model_with_batches_in_flight(seed, host):
+    """Random plans with up to two earlier batches kept in flight (pinned,
+    then unpinned oldest first); batches avoid the users in flight, as a
+    server must.  Plans, evictions and failures agree exactly."""
+    rng = np.random.default_rng(seed)
+    cfg = dict(num_layers=int(rng.integers(1, 3)), num_pages=int(rng.integers(24, 60)),
+               page_size=int(2 ** rng.integers(2, 4)), max_pages_per_user=int(rng.integers(4, 12)),
+               max_users=int(rng.integers(8, 14)))
+    if host:
+        cfg["host_pages"] = int(rng.integers(4, 100))
+    ref, kv = RefKVCache(**cfg), KVCache(**cfg)
+    flight = []
+    evicted_beside_pins = 0
+    outcomes = {"ok": 0, "full": 0, "too_long": 0}
+    for ids, n in random_trace(rng, 300, 5, 24, 3 * cfg["page_size"]):
+        busy = {u for b in flight for u in b}
+        keep = [k for k, u in enumerate(ids) if u not in busy]
+        ids, n = [ids[k] for k in keep], [n[k] for k in keep]
+        if len(flight) == 2:
+            done = flight.pop(0)
+            ref.pin(done, pin=False)
+            kv.unpin(done)
+        try:
+            want = ref.plan(ids, n)
+        except (CacheFull, TooLong) as e:
+            kind = "full" if isinstance(e, CacheFull) else "too_long"
+            outcomes[kind] += 1
+            with pytest.raises(KVCacheError) as ei:
+                kv.plan(ids, n)
+            assert ei.value.code == ERR[kind]
+            continue
+        outcomes["ok"] += 1
+        got = kv.plan(ids, n)
+        assert got.hist_len.tolist() == want[0] and got.slots.tolist() == want[1]
+        assert [tuple(u) for u in got.updates.tolist()] == [tuple(u) for u in want[2]]
+        assert got.evicted == want[3]
+        assert not set(got.evicted) & {u for b in flight for u in b}
+        evicted_beside_pins += bool(got.evicted and flight)
+        assert [tuple(c) for c in got.copies[:, :3].tolist()] == [tuple(c) for c in ref.last_copies]
+        assert kv.stats(host=True) == (len(ref.free_pages), len(ref.users), len(ref.host_free), len(ref.host))
+        if ids and rng.random() < 0.7:
+            ref.pin(ids)
+            kv.pin(ids)
+            flight.append(ids)
+    assert outcomes["ok"] > 50 and evicted_beside_pins > 10

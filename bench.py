@@ -979,8 +979,8 @@ def main():
         out["cache_speedup"] = {b.wl.name: cache_speedup(args, b)}
         out["batch_invariant"] = invariant_cost(b, args.steps, args.warmup, m)
         # the same steps with two and three batches in flight (serving)
-        out["in_flight"] = [in_flight(b, args.steps, args.warmup, 2, value)] + \
-            [in_flight(b, args.steps, args.warmup, k, value, graphs=True) for k in (1, 2, 3)]
+        out["in_flight"] = [guarded(in_flight, b, args.steps, args.warmup, 2, value)] + \
+            [guarded(in_flight, b, args.steps, args.warmup, k, value, graphs=True) for k in (1, 2, 3)]
     if not args.no_cpu_baseline and b.wl.name == WORKLOAD:
         out["cpu_baseline"] = cpu_baseline(b.wl, b.B, b.R)
     if headline:
@@ -992,8 +992,8 @@ def main():
         out["long_history"] = rec
         del bl
         torch.cuda.empty_cache()
-        bl, out["long_history"]["in_flight"] = workload_in_flight(args, B8_KV_HIT_LONG, max(6, args.steps // 6), 2, 3)
-        del bl
+        out["long_history"]["in_flight"] = guarded(
+            lambda: workload_in_flight(args, B8_KV_HIT_LONG, max(6, args.steps // 6), 2, 3)[1])
         torch.cuda.empty_cache()
         # the compute-bound configurations: the batch-8 full recompute and the
         # 64-user serving mix (its long miss users' causal recomputes)
@@ -1003,6 +1003,17 @@ def main():
             del bx
             torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
+
+
+def guarded(fn, *a, **kw):
+    """An extra record of the JSON line: its failure is reported in the
+    record instead of ending the run before the headline line is printed."""
+    import torch
+    try:
+        return fn(*a, **kw)
+    except Exception as e:                      # noqa: BLE001 -- reported, not hidden
+        torch.cuda.synchronize()
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def in_flight(b, steps, warmup, nstreams, serial_value, graphs=False):
